@@ -1,0 +1,150 @@
+"""CPU oracle for route-sparse GQA attention (fp64, plain C + a thin numpy wrapper).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this package; the product path never does.  It
+shares no code with the HIP library; the two meet only at the seeded inputs
+from ``workloads``.
+
+Functions (all inputs contiguous numpy arrays; bfloat16 tensors are passed as
+their ``uint16`` bit patterns):
+
+* ``route_lists(routes, kv_length)``      -> (int32 [B,S_q,K], int32 [B,S_q])
+* ``membership(routes, kv_length)``       -> uint8 [B,S_q,round_up(kv_length,128)]
+* ``tile_class(routes, kv_length)``       -> int32 [B,ceil(S_q/128),ceil(kv_length/128)]
+* ``forward(q, k, v, routes, scale, rows=None)`` -> float64 [B,rows,Hq,D]
+
+See ``qsa_oracle.c`` for the definitions and the passages they follow.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+TILE = 128
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` with gcc (OpenMP over rows)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+             _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class Oracle:
+    """ctypes handle on one build of ``qsa_oracle.c`` (tests may load a variant)."""
+
+    def __init__(self, lib_path: str):
+        lib = ctypes.CDLL(lib_path)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_route_lists.argtypes = [p, i64, i64, i64, p, p]
+        lib.oracle_membership.argtypes = [p, i64, i64, i64, i64, p]
+        lib.oracle_tile_class.argtypes = [p, i64, i64, i64, i64, p]
+        lib.oracle_forward.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i64,
+                                       ctypes.c_double, i64, i64, p]
+        for f in (lib.oracle_route_lists, lib.oracle_membership, lib.oracle_tile_class, lib.oracle_forward):
+            f.restype = None
+        self.lib = lib
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    def route_lists(self, routes, kv_length):
+        r = _routes64(routes)
+        B, S_q, K = r.shape
+        lst = np.empty((B, S_q, K), dtype=np.int32)
+        cnt = np.empty((B, S_q), dtype=np.int32)
+        self.lib.oracle_route_lists(_ptr(r), B * S_q, K, int(kv_length), _ptr(lst), _ptr(cnt))
+        return lst, cnt
+
+    def membership(self, routes, kv_length):
+        r = _routes64(routes)
+        B, S_q, K = r.shape
+        ldm = ldm_of(kv_length)
+        out = np.empty((B, S_q, ldm), dtype=np.uint8)
+        self.lib.oracle_membership(_ptr(r), B * S_q, K, int(kv_length), ldm, _ptr(out))
+        return out
+
+    def tile_class(self, routes, kv_length):
+        r = _routes64(routes)
+        B, S_q, K = r.shape
+        n_ti, n_tj = (S_q + TILE - 1) // TILE, (int(kv_length) + TILE - 1) // TILE
+        out = np.empty((B, n_ti, n_tj), dtype=np.int32)
+        self.lib.oracle_tile_class(_ptr(r), B, S_q, K, int(kv_length), _ptr(out))
+        return out
+
+    def forward(self, q, k, v, routes, scale, rows=None):
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if t.dtype != np.uint16:
+                raise TypeError(f"{name} must hold bfloat16 bits as uint16")
+        q, k, v = (np.ascontiguousarray(t) for t in (q, k, v))
+        r = _routes64(routes)
+        B, S_q, Hq, D = q.shape
+        _, S_kv, Hkv, _ = k.shape
+        K = r.shape[2]
+        if Hkv < 1 or Hq % Hkv != 0:
+            raise ValueError("Hq must be a positive multiple of Hkv")
+        r0, r1 = (0, S_q) if rows is None else (int(rows[0]), int(rows[1]))
+        out = np.empty((B, r1 - r0, Hq, D), dtype=np.float64)
+        self.lib.oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(r), B, S_q, S_kv, Hq, Hkv, D, K,
+                                float(scale), r0, r1, _ptr(out))
+        return out
+
+
+def _load() -> Oracle:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = Oracle(_LIB_PATH)
+    return _lib
+
+
+def num_threads() -> int:
+    return _load().num_threads()
+
+
+def _routes64(routes: np.ndarray) -> np.ndarray:
+    r = np.asarray(routes)
+    if r.dtype not in (np.int32, np.int64):
+        raise TypeError("routes must be int32 or int64")
+    return np.ascontiguousarray(r.astype(np.int64))  # int32 -> int64 sign-extends
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def ldm_of(kv_length: int) -> int:
+    return (int(kv_length) + TILE - 1) // TILE * TILE
+
+
+def route_lists(routes: np.ndarray, kv_length: int):
+    return _load().route_lists(routes, kv_length)
+
+
+def membership(routes: np.ndarray, kv_length: int) -> np.ndarray:
+    return _load().membership(routes, kv_length)
+
+
+def tile_class(routes: np.ndarray, kv_length: int) -> np.ndarray:
+    return _load().tile_class(routes, kv_length)
+
+
+def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, routes: np.ndarray, scale: float,
+            rows: tuple[int, int] | None = None) -> np.ndarray:
+    """fp64 attention output [B, rows, Hq, D] for query rows ``rows`` (default: all)."""
+    return _load().forward(q, k, v, routes, scale, rows)

@@ -1,0 +1,189 @@
+/*
+ * qsa_oracle.c -- plain fp64 CPU oracle for route-sparse GQA attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header, table or helper with the
+ * HIP library.
+ *
+ * It is the plain definition, written for a reader to check by eye, with no
+ * blocking, fusion or reordering:
+ *
+ *  - Route set of a query row (flex_qsa page, `_routes_to_membership`
+ *    parameters and module description; fa4_qsa page, `_preprocess`
+ *    parameters; qsa page, `qsa_gqa_attention` parameters): every slot value
+ *    x is widened to int64; x is a valid key iff 0 <= x < kv_length (negative
+ *    IDs, -1 padding and out-of-range values, including huge int64 values,
+ *    are ignored); duplicates collapse to one.  R(b,i) is that set in
+ *    ascending order.
+ *  - Membership table (fa4_qsa page, `_preprocess` return value): uint8
+ *    [B, S_q, ldm], 1 iff column c is in R(b,i); columns past kv_length are
+ *    the row padding and hold 0.
+ *  - Tile classes (fa4_qsa page, `_block_kinds` and `_compact_blocks`):
+ *    int32 [B, ceil(S_q/128), ceil(kv_length/128)]; 0 when no member pair
+ *    lies in the tile, 2 when every in-range pair of the tile is a member,
+ *    1 otherwise.
+ *  - Attention (flex_qsa page, module description and
+ *    `flex_sparse_gqa_attention`; fa4_qsa page, `fa4_sparse_gqa_attention`;
+ *    qsa page, `_gathered_qsa_gqa_attention_chunk` grouped layout): query
+ *    head h reads KV head h / (Hq/Hkv); over j in R(b,i),
+ *    s_j = scale * <q[b,i,h,:], k[b,j,hk,:]>, o = sum_j softmax(s)_j v[b,j,hk,:];
+ *    an empty R gives exactly zero; no causal or other mask is added.
+ *    All arithmetic is fp64 on the exact bfloat16 input values.
+ *
+ * Rows are independent, so each entry point runs its outer row loop under
+ * OpenMP; that changes no per-row arithmetic.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int cmp_int64(const void *a, const void *b) {
+    int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* R(row): ascending distinct valid IDs of one row of K slots; returns |R|. */
+static int64_t route_set(const int64_t *slots, int64_t K, int64_t kv_length, int64_t *out) {
+    int64_t n = 0;
+    for (int64_t s = 0; s < K; ++s) {
+        int64_t x = slots[s];
+        if (x >= 0 && x < kv_length) out[n++] = x;
+    }
+    qsort(out, (size_t)n, sizeof(int64_t), cmp_int64);
+    int64_t m = 0;
+    for (int64_t j = 0; j < n; ++j)
+        if (m == 0 || out[j] != out[m - 1]) out[m++] = out[j];
+    return m;
+}
+
+static double bf16_to_double(uint16_t h) {
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* route_list [rows, K] int32 (R ascending, then -1) and route_count [rows]. */
+void oracle_route_lists(const int64_t *routes, int64_t rows, int64_t K, int64_t kv_length,
+                        int32_t *route_list, int32_t *route_count) {
+#pragma omp parallel
+    {
+        int64_t *set = (int64_t *)malloc((size_t)K * sizeof(int64_t));
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t r = 0; r < rows; ++r) {
+            int64_t n = route_set(routes + r * K, K, kv_length, set);
+            for (int64_t j = 0; j < K; ++j) route_list[r * K + j] = j < n ? (int32_t)set[j] : -1;
+            route_count[r] = (int32_t)n;
+        }
+        free(set);
+    }
+}
+
+/* membership [rows, ldm] uint8: 1 iff the column is in the row's route set. */
+void oracle_membership(const int64_t *routes, int64_t rows, int64_t K, int64_t kv_length, int64_t ldm,
+                       uint8_t *membership) {
+#pragma omp parallel
+    {
+        int64_t *set = (int64_t *)malloc((size_t)K * sizeof(int64_t));
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t r = 0; r < rows; ++r) {
+            uint8_t *row = membership + r * ldm; /* int64 offset throughout */
+            for (int64_t c = 0; c < ldm; ++c) row[c] = 0;
+            int64_t n = route_set(routes + r * K, K, kv_length, set);
+            for (int64_t j = 0; j < n; ++j) row[set[j]] = 1;
+        }
+        free(set);
+    }
+}
+
+/* tile_class [B, ceil(S_q/128), ceil(kv_length/128)] int32 in {0, 1, 2}. */
+void oracle_tile_class(const int64_t *routes, int64_t B, int64_t S_q, int64_t K, int64_t kv_length,
+                       int32_t *tile_class) {
+    const int64_t T = 128;
+    const int64_t n_ti = (S_q + T - 1) / T, n_tj = (kv_length + T - 1) / T;
+#pragma omp parallel
+    {
+        int64_t *set = (int64_t *)malloc((size_t)K * sizeof(int64_t));
+        int64_t *members = (int64_t *)malloc((size_t)n_tj * sizeof(int64_t));
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t ti = 0; ti < n_ti; ++ti) {
+                int64_t r0 = ti * T, r1 = r0 + T < S_q ? r0 + T : S_q;
+                for (int64_t tj = 0; tj < n_tj; ++tj) members[tj] = 0;
+                for (int64_t i = r0; i < r1; ++i) {
+                    int64_t n = route_set(routes + (b * S_q + i) * K, K, kv_length, set);
+                    for (int64_t j = 0; j < n; ++j) members[set[j] / T] += 1;
+                }
+                for (int64_t tj = 0; tj < n_tj; ++tj) {
+                    int64_t c0 = tj * T, c1 = c0 + T < kv_length ? c0 + T : kv_length;
+                    int64_t pairs = (r1 - r0) * (c1 - c0);
+                    int32_t cls = members[tj] == 0 ? 0 : (members[tj] == pairs ? 2 : 1);
+                    tile_class[(b * n_ti + ti) * n_tj + tj] = cls;
+                }
+            }
+        }
+        free(set);
+        free(members);
+    }
+}
+
+/*
+ * out [B, row_end - row_begin, Hq, D] fp64: attention of query rows
+ * [row_begin, row_end) of every batch row.  q is [B,S_q,Hq,D], k and v are
+ * [B,S_kv,Hkv,D], all contiguous bfloat16 bit patterns; routes [B,S_q,K].
+ */
+void oracle_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int64_t *routes,
+                    int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,
+                    double scale, int64_t row_begin, int64_t row_end, double *out) {
+    const int64_t G = Hq / Hkv;
+    const int64_t n_rows = row_end - row_begin;
+#pragma omp parallel
+    {
+        int64_t *set = (int64_t *)malloc((size_t)K * sizeof(int64_t));
+        double *score = (double *)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(dynamic, 4) collapse(2)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t i = row_begin; i < row_end; ++i) {
+                int64_t n = route_set(routes + (b * S_q + i) * K, K, S_kv, set);
+                for (int64_t h = 0; h < Hq; ++h) {
+                    int64_t hk = h / G;
+                    const uint16_t *qv = q + ((b * S_q + i) * Hq + h) * D;
+                    double *o = out + ((b * n_rows + (i - row_begin)) * Hq + h) * D;
+                    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                    if (n == 0) continue; /* empty route set: exactly zero */
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < n; ++j) {
+                        const uint16_t *kv = k + ((b * S_kv + set[j]) * Hkv + hk) * D;
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d) dot += bf16_to_double(qv[d]) * bf16_to_double(kv[d]);
+                        score[j] = scale * dot;
+                        if (score[j] > m) m = score[j];
+                    }
+                    double denom = 0.0;
+                    for (int64_t j = 0; j < n; ++j) {
+                        double w = exp(score[j] - m);
+                        denom += w;
+                        const uint16_t *vv = v + ((b * S_kv + set[j]) * Hkv + hk) * D;
+                        for (int64_t d = 0; d < D; ++d) o[d] += w * bf16_to_double(vv[d]);
+                    }
+                    for (int64_t d = 0; d < D; ++d) o[d] /= denom;
+                }
+            }
+        }
+        free(set);
+        free(score);
+    }
+}

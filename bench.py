@@ -1,0 +1,243 @@
+"""Benchmark of the route-sparse GQA forward path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input
+already resident in HBM:
+  1. qsa_preprocess: route normalisation (lists + counts), membership table
+     and 128x128 tile classes;
+  2. qsa_forward_preprocessed: the fused gather-attention kernel.
+
+Prints ONE JSON line (rank 0):
+  value        routed-attention TFLOP/s of the whole step, F = 4*D*Hq*N flops
+               with N = total distinct valid routes;
+  roofline     the gather-attention kernel against the 8 TB/s HBM roofline:
+               algorithmic bytes per launch (routed K and V rows once per
+               (query row, KV head), Q, O, lists and counts) over its average
+               launch time, measured with HIP events on the launch stream;
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same rows.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "routed-attention TFLOP/s + achieved HBM GB/s (fwd, BF16, D=256) on 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "right_padded"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="JSON with rocprofv3-derived HBM bytes per launch of the attention kernel")
+    return ap.parse_args()
+
+
+class Plan:
+    """Pre-marshalled C-ABI calls for one workload (no per-step Python allocation)."""
+
+    def __init__(self, w, q, k, v, routes, dev):
+        import torch
+
+        import route_sparse_gqa_amd as qsa
+
+        self.w = w
+        self.L = qsa.lib()
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        i8 = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.q = torch.from_numpy(q.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.k = torch.from_numpy(k.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.v = torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.routes = torch.from_numpy(routes).to(dev)
+        B, S_q, K = routes.shape
+        n_ti, n_tj = -(-S_q // 128), -(-w.S_kv // 128)
+        self.lst = torch.empty((B, S_q, K), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((B, S_q), dtype=torch.int32, device=dev)
+        self.mem = torch.empty((B, S_q, n_tj * 128), dtype=torch.uint8, device=dev)
+        self.tc = torch.empty((B, n_ti, n_tj), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, S_q, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+        st = lambda t: (ctypes.c_int64 * t.dim())(*t.stride())
+        self.pre_args = (i8(self.routes), 1 if routes.dtype == np.int64 else 0, B, S_q, K, st(self.routes),
+                         w.S_kv, i8(self.lst), i8(self.cnt), i8(self.mem), i8(self.tc), self.stream)
+        self.fwd_args = (i8(self.q), st(self.q), i8(self.k), st(self.k), i8(self.v), st(self.v), i8(self.lst),
+                         i8(self.cnt), B, S_q, w.S_kv, w.Hq, w.Hkv, w.D, K, ctypes.c_float(w.scale),
+                         i8(self.out), self.stream)
+
+    def preprocess(self):
+        rc = self.L.qsa_preprocess(*self.pre_args)
+        if rc != 0:
+            raise RuntimeError(f"qsa_preprocess failed with status {rc}")
+
+    def attention(self):
+        rc = self.L.qsa_forward_preprocessed(*self.fwd_args)
+        if rc != 0:
+            raise RuntimeError(f"qsa_forward_preprocessed failed with status {rc}")
+
+
+def algorithmic_counts(w, N: int):
+    rows = w.B * w.S_q
+    flops = 4 * w.D * w.Hq * N
+    kv_bytes = 4 * w.D * w.Hkv * N               # routed K and V rows, once per (query row, KV head)
+    qo_bytes = 2 * 2 * rows * w.Hq * w.D         # Q read + O written, bf16
+    list_bytes = 4 * N + 4 * rows                # compacted IDs read + counts
+    return flops, kv_bytes + qo_bytes + list_bytes
+
+
+def cpu_baseline(w, q, k, v, routes, counts, target_s: float):
+    """Time the fp64 oracle on contiguous query rows taken from the middle of the workload."""
+    import oracle
+
+    S_q = w.S_q
+    per_row_routes = counts.sum(axis=0)  # summed over the batch
+    start = S_q // 2
+
+    def run(nrows):
+        r0, r1 = start, min(S_q, start + nrows)
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, routes, w.scale, rows=(r0, r1))
+        dt = time.perf_counter() - t0
+        return dt, int(per_row_routes[r0:r1].sum()), r1 - r0
+
+    dt, n_routes, nrows = run(4)
+    while dt < 0.5 and nrows < S_q - start:
+        dt, n_routes, nrows = run(min(S_q - start, nrows * 4))
+    if dt < target_s and nrows < S_q - start:
+        want = int(nrows * target_s / max(dt, 1e-3))
+        dt, n_routes, nrows = run(min(S_q - start, max(nrows, want)))
+    tflops = 4 * w.D * w.Hq * n_routes / dt / 1e12
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 oracle forward on query rows [{start}, {start + nrows}) of every batch row "
+                  f"({n_routes} routed pairs, {dt:.2f} s)",
+    }
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    print(f"[bench] generating workload {w.name}: {w.description}", file=sys.stderr, flush=True)
+    _, q, k, v, routes = make_inputs(w.name)
+    dev = torch.device("cuda", 0)
+    plan = Plan(w, q, k, v, routes, dev)
+
+    plan.preprocess()
+    torch.cuda.synchronize()
+    counts = plan.cnt.cpu().numpy()
+    N = int(counts.sum())
+    flops, alg_bytes = algorithmic_counts(w, N)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        plan.preprocess()
+        plan.attention()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    pre_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    att_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    total0, total1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    total0.record(stream)
+    for s in range(args.steps):
+        pre_ev[s][0].record(stream)
+        plan.preprocess()
+        pre_ev[s][1].record(stream)
+        att_ev[s][0].record(stream)
+        plan.attention()
+        att_ev[s][1].record(stream)
+    total1.record(stream)
+    torch.cuda.synchronize()
+
+    ms_step = total0.elapsed_time(total1) / args.steps
+    ms_att = sum(a.elapsed_time(b) for a, b in att_ev) / args.steps
+    ms_pre = sum(a.elapsed_time(b) for a, b in pre_ev) / args.steps
+    achieved = alg_bytes / (ms_att * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            t = json.load(f)
+        if t.get("workload") == w.name and t.get("kernel_source_sha") == _kernel_sha():
+            traffic = t.get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, q, k, v, routes, counts, args.cpu_seconds)
+
+    result = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "S_q": w.S_q, "S_kv": w.S_kv, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+            "K": w.K, "q_offset": w.q_offset, "routes_N": N, "route_dtype": str(routes.dtype),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "gather_attention",
+            "ms_per_launch": ms_att,
+            "alg_bytes_per_launch": alg_bytes,
+        },
+        "kernels_ms": {"preprocess(route_normalize+membership_tiles)": ms_pre, "gather_attention": ms_att},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def _kernel_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "route_sparse_gqa_amd", "csrc", "gather_attention.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

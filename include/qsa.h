@@ -1,0 +1,161 @@
+/*
+ * qsa.h -- C ABI of libqsa: route-sparse grouped-query attention (forward)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Every query row attends exactly to its own set of key/value token IDs
+ * ("routes").  The operation is the one defined on the route-sparse GQA
+ * pages:
+ *   - flex_qsa page, module description: padded batches, packed THD rows and
+ *     context parallelism all reduce to "each query row attends to its route
+ *     IDs"; rows without a valid route give exactly zero output.
+ *   - fa4_qsa page, `_preprocess` and `fa4_sparse_gqa_attention`: duplicate
+ *     IDs select a token once; invalid IDs, including huge int64 values, are
+ *     discarded; no causal or other mask is added beyond the routes.
+ *   - qsa page, `_gathered_qsa_gqa_attention_chunk`: grouped query layout
+ *     [B, Q, Hkv, G, D], i.e. query head h reads KV head h / G, G = Hq / Hkv.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates nothing, frees nothing and keeps no pointer or other
+ *     state after a call returns; it is safe to call from several threads.
+ *   - Sizes and strides are int64_t; strides are in ELEMENTS.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued on it; no call synchronises the host or reads device memory
+ *     on the host.
+ *   - Every output byte is written by the library (list padding, membership
+ *     row padding, zero rows): callers need not clear anything.
+ *   - Return value: QSA_OK (0) or a negative QSA_ERR_* status.  Argument
+ *     checks are host-only; when one fails nothing is enqueued.  Route
+ *     VALUES are data, never errors: invalid IDs are ignored.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define QSA_OK 0
+#define QSA_ERR_NULL_POINTER -1 /* a required pointer is NULL                          */
+#define QSA_ERR_EMPTY_DIM -2    /* B, S_q, S_kv, Hq, Hkv, D or K < 1 (pages: nonempty)  */
+#define QSA_ERR_KV_LENGTH -3    /* kv_length < 1 or > 2^31 (IDs are stored as int32)   */
+#define QSA_ERR_HEADS -4        /* Hq is not a positive multiple of Hkv                */
+#define QSA_ERR_HEAD_DIM -5     /* D not in {64, 128, 256}                             */
+#define QSA_ERR_ROUTE_DTYPE -6  /* routes_dtype is neither QSA_INT32 nor QSA_INT64     */
+#define QSA_ERR_SCALE -7        /* scale is not finite and > 0                         */
+#define QSA_ERR_LAYOUT -8       /* last stride != 1, or a row/pointer not 16-B aligned */
+#define QSA_ERR_ALIAS -9        /* an output overlaps an input or another output       */
+#define QSA_ERR_WORKSPACE -10   /* workspace NULL or smaller than required             */
+#define QSA_ERR_LIMIT -11       /* K > QSA_MAX_ROUTES or G > QSA_MAX_GROUP             */
+#define QSA_ERR_HIP -12         /* a HIP launch reported an error                      */
+
+/* ---- constants --------------------------------------------------------- */
+#define QSA_INT32 0          /* routes are int32_t (sign-extended before the checks) */
+#define QSA_INT64 1          /* routes are int64_t                                    */
+#define QSA_TILE 128         /* rows and columns of one membership tile              */
+#define QSA_MAX_ROUTES 16384 /* largest K (route slots per query row)               */
+#define QSA_MAX_GROUP 16     /* largest G = Hq / Hkv                                */
+
+/*
+ * qsa_preprocess -- validate, deduplicate and compact the routes; optionally
+ * build the uint8 membership table and the 128x128 tile classes.
+ *
+ * Definition (fa4_qsa page, `_preprocess`, `_block_kinds`; flex_qsa page,
+ * `_routes_to_membership` and `_membership_flat_offset`): a slot value x
+ * (int32 values sign-extended to int64) is a valid key iff
+ * 0 <= x < kv_length; R(b,i) = the ascending set of distinct valid values of
+ * row (b,i).
+ *
+ *   routes        [B, S_q, K] int32 or int64 (`routes_dtype`), any strides
+ *                 (`route_strides`, elements, may be 0 or negative).
+ *   kv_length     number of physical K/V rows, 1 <= kv_length <= 2^31.
+ *   route_list    OUT [B, S_q, K] int32, contiguous: R(b,i) ascending, then
+ *                 -1 in the remaining K - |R| slots.
+ *   route_count   OUT [B, S_q] int32, contiguous: |R(b,i)|.
+ *   membership    OUT, nullable: [B, S_q, ldm] uint8, contiguous,
+ *                 ldm = round_up(kv_length, 128); 1 iff the column is in
+ *                 R(b,i), 0 elsewhere (padding columns included).  Offsets
+ *                 are 64-bit: the table may exceed 2^31 bytes.
+ *   tile_class    OUT, nullable: [B, ceil(S_q/128), ceil(kv_length/128)]
+ *                 int32, contiguous: 0 = no member pair in the tile,
+ *                 2 = every in-range pair of the tile is a member,
+ *                 1 = otherwise.  Independent of `membership`.
+ *
+ * Errors: NULL_POINTER, EMPTY_DIM, KV_LENGTH, ROUTE_DTYPE, LIMIT (K),
+ * LAYOUT (route_count/list not 4-B aligned, membership not 16-B aligned),
+ * ALIAS (outputs overlap each other or `routes`), HIP.
+ */
+int qsa_preprocess(const void *routes, int routes_dtype, int64_t B, int64_t S_q, int64_t K,
+                   const int64_t route_strides[3], int64_t kv_length, int32_t *route_list,
+                   int32_t *route_count, uint8_t *membership, int32_t *tile_class, void *stream);
+
+/*
+ * qsa_forward_workspace_size -- bytes of device workspace qsa_forward needs:
+ * the compacted lists and counts (4*B*S_q*K + 4*B*S_q) plus alignment.
+ * Returns 0 when a size is < 1 or the product overflows.
+ */
+size_t qsa_forward_workspace_size(int64_t B, int64_t S_q, int64_t K);
+
+/*
+ * qsa_forward -- route-sparse GQA attention, BF16 in and out, fp32 softmax.
+ *
+ * Definition (flex_qsa page, `flex_sparse_gqa_attention`; fa4_qsa page,
+ * `fa4_sparse_gqa_attention`; qsa page, `gathered_qsa_gqa_attention`): for
+ * each (b, i, h) with hk = h / G and R = R(b,i) computed with
+ * kv_length = S_kv:
+ *   s_j = scale * <q[b,i,h,:], k[b,j,hk,:]>  for j in R,
+ *   out[b,i,h,:] = sum_j softmax(s)_j * v[b,j,hk,:],  or +0.0 when R is empty.
+ *
+ *   q        [B, S_q, Hq, D] bf16; k, v [B, S_kv, Hkv, D] bf16.  Strides in
+ *            elements; the last stride must be 1, base pointers 16-B
+ *            aligned and the other strides multiples of 8 elements.
+ *   routes   as in qsa_preprocess, in K/V coordinates of the same batch row.
+ *   D        64, 128 or 256.  G = Hq / Hkv <= 16.
+ *   scale    finite and > 0 (the pages default to 1/sqrt(D); callers pass it).
+ *   out      OUT [B, S_q, Hq, D] bf16, contiguous, must not overlap any input
+ *            or the workspace.
+ *   workspace, workspace_bytes   device scratch of at least
+ *            qsa_forward_workspace_size(B, S_q, K) bytes, 256-B aligned; it
+ *            receives the compacted lists (overwritten each call).
+ *
+ * Runs the route-normalisation kernel into the workspace, then the
+ * gather-attention kernel.  Errors: NULL_POINTER, EMPTY_DIM, KV_LENGTH
+ * (S_kv > 2^31), HEADS, HEAD_DIM, ROUTE_DTYPE, SCALE, LAYOUT, ALIAS,
+ * WORKSPACE, LIMIT, HIP.
+ */
+int qsa_forward(const void *q, const int64_t q_strides[4], const void *k, const int64_t k_strides[4],
+                const void *v, const int64_t v_strides[4], const void *routes, int routes_dtype,
+                const int64_t route_strides[3], int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq,
+                int64_t Hkv, int64_t D, int64_t K, float scale, void *out, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/*
+ * qsa_forward_preprocessed -- the gather-attention kernel alone, on lists
+ * already produced by qsa_preprocess (routes reused across calls, as the
+ * pages build the route mask once per layer call and reuse it: qsa page,
+ * `QSARouteSelection.flex_mask` and `qsa_gqa_attention` flex_mask).
+ *
+ *   route_list [B, S_q, K] int32 contiguous and route_count [B, S_q] int32
+ *   exactly as qsa_preprocess writes them (with kv_length = S_kv).  Counts
+ *   are clamped to [0, K] and IDs to [0, S_kv) before any address is formed,
+ *   so malformed lists cannot fault, but their result is unspecified.
+ *   Other arguments as in qsa_forward.
+ */
+int qsa_forward_preprocessed(const void *q, const int64_t q_strides[4], const void *k,
+                             const int64_t k_strides[4], const void *v, const int64_t v_strides[4],
+                             const int32_t *route_list, const int32_t *route_count, int64_t B,
+                             int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,
+                             float scale, void *out, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *qsa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

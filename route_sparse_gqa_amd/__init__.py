@@ -1,0 +1,235 @@
+"""Route-sparse GQA attention (forward) on AMD Instinct MI355X.
+
+Thin Python binding over the C ABI of ``libqsa.so`` (declared in
+``include/qsa.h``).  The functions below only marshal arguments: they check
+that tensors live on a ROCm GPU, copy inputs whose last stride is not 1
+(the pages accept arbitrary strides and copy such inputs), allocate outputs
+and workspace with ``torch.empty`` and pass raw device pointers, sizes and
+torch's current HIP stream to the library.  Every step of the computation
+runs in the library's HIP kernels; there is no other code path.
+
+* ``qsa_preprocess(routes, kv_length, membership=False, tile_class=False)``
+* ``qsa_forward(q, k, v, routes, scale=None)``
+* ``qsa_forward_preprocessed(q, k, v, route_list, route_count, scale=None)``
+* ``qsa_forward_workspace_size(B, S_q, K)``
+* ``qsa_status_string(status)``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqsa.so")
+
+QSA_INT32, QSA_INT64 = 0, 1
+TILE = 128
+MAX_ROUTES = 16384
+MAX_GROUP = 16
+
+# argument-error statuses raise ValueError; HIP errors raise RuntimeError
+_HIP_ERROR = -12
+
+_lib = None
+
+
+class QSAError(ValueError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {qsa_status_string(status)} (status {status})")
+
+
+class QSAHipError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {qsa_status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libqsa.so``; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m route_sparse_gqa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        P64 = ctypes.POINTER(ctypes.c_int64)
+        L.qsa_status_string.argtypes = [i32]
+        L.qsa_status_string.restype = ctypes.c_char_p
+        L.qsa_forward_workspace_size.argtypes = [i64, i64, i64]
+        L.qsa_forward_workspace_size.restype = ctypes.c_size_t
+        L.qsa_preprocess.argtypes = [p, i32, i64, i64, i64, P64, i64, p, p, p, p, p]
+        L.qsa_preprocess.restype = i32
+        L.qsa_forward.argtypes = [p, P64, p, P64, p, P64, p, i32, P64, i64, i64, i64, i64, i64, i64, i64,
+                                  ctypes.c_float, p, p, ctypes.c_size_t, p]
+        L.qsa_forward.restype = i32
+        L.qsa_forward_preprocessed.argtypes = [p, P64, p, P64, p, P64, p, p, i64, i64, i64, i64, i64, i64, i64,
+                                               ctypes.c_float, p, p]
+        L.qsa_forward_preprocessed.restype = i32
+        _lib = L
+    return _lib
+
+
+def qsa_status_string(status: int) -> str:
+    return lib().qsa_status_string(int(status)).decode()
+
+
+def qsa_forward_workspace_size(B: int, S_q: int, K: int) -> int:
+    return int(lib().qsa_forward_workspace_size(int(B), int(S_q), int(K)))
+
+
+def _check(status: int, where: str) -> None:
+    if status == 0:
+        return
+    if status == _HIP_ERROR:
+        raise QSAHipError(status, where)
+    raise QSAError(status, where)
+
+
+def _strides(t: torch.Tensor):
+    return (ctypes.c_int64 * t.dim())(*t.stride())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_gpu(*tensors: torch.Tensor) -> torch.device:
+    dev = tensors[0].device
+    for t in tensors:
+        if t.device.type != "cuda":
+            raise ValueError("route-sparse GQA runs on a ROCm GPU only; got a tensor on " + str(t.device))
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _route_dtype(routes: torch.Tensor) -> int:
+    if routes.dtype == torch.int64:
+        return QSA_INT64
+    if routes.dtype == torch.int32:
+        return QSA_INT32
+    raise ValueError(f"routes must be int32 or int64, got {routes.dtype}")
+
+
+def _bf16_operand(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D, got shape {tuple(t.shape)}")
+    if t.stride(-1) != 1 or any(s % 8 for s in t.stride()[:3]) or t.data_ptr() % 16:
+        t = t.contiguous()  # arbitrary strides are accepted by copying
+    return t
+
+
+def qsa_preprocess(routes: torch.Tensor, kv_length: int, membership: bool = False, tile_class: bool = False):
+    """Validate, deduplicate and compact routes on the GPU.
+
+    Returns ``(route_list, route_count, membership_or_None, tile_class_or_None)``:
+    int32 [B,S_q,K] (ascending distinct valid IDs, then -1), int32 [B,S_q],
+    uint8 [B,S_q,round_up(kv_length,128)], int32 [B,ceil(S_q/128),ceil(kv_length/128)].
+    """
+    dev = _require_gpu(routes)
+    if routes.dim() != 3:
+        raise ValueError(f"routes must be [B, S_q, K], got shape {tuple(routes.shape)}")
+    B, S_q, K = routes.shape
+    dt = _route_dtype(routes)
+    kv_length = int(kv_length)
+    n_ti, n_tj = -(-S_q // TILE), -(-kv_length // TILE)
+    ldm = n_tj * TILE
+    lst = torch.empty((B, S_q, K), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, S_q), dtype=torch.int32, device=dev)
+    mem = torch.empty((B, S_q, ldm), dtype=torch.uint8, device=dev) if membership else None
+    tc = torch.empty((B, n_ti, n_tj), dtype=torch.int32, device=dev) if tile_class else None
+    st = lib().qsa_preprocess(_ptr(routes), dt, B, S_q, K, _strides(routes), kv_length, _ptr(lst), _ptr(cnt),
+                              _ptr(mem), _ptr(tc), _stream(dev))
+    _check(st, "qsa_preprocess")
+    return lst, cnt, mem, tc
+
+
+def _attention_shapes(q, k, v):
+    if k.shape != v.shape:
+        raise ValueError(f"value must have key's shape: {tuple(k.shape)} vs {tuple(v.shape)}")
+    B, S_q, Hq, D = q.shape
+    Bk, S_kv, Hkv, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"query {tuple(q.shape)} and key {tuple(k.shape)} disagree on batch or head dim")
+    return B, S_q, Hq, D, S_kv, Hkv
+
+
+def _output(out: Optional[torch.Tensor], shape, dev) -> torch.Tensor:
+    if out is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(shape) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {tuple(shape)}")
+    if out.device != dev:
+        raise ValueError("out must be on the inputs' device")
+    return out
+
+
+def _scale(scale: Optional[float], D: int) -> float:
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def qsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, routes: torch.Tensor,
+                scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Route-sparse GQA forward: BF16 [B,S_q,Hq,D] x [B,S_kv,Hkv,D] with routes [B,S_q,K]."""
+    dev = _require_gpu(q, k, v, routes)
+    q, k, v = _bf16_operand(q, "query"), _bf16_operand(k, "key"), _bf16_operand(v, "value")
+    B, S_q, Hq, D, S_kv, Hkv = _attention_shapes(q, k, v)
+    if routes.dim() != 3 or routes.shape[0] != B or routes.shape[1] != S_q:
+        raise ValueError(f"routes must be [B, S_q, K] = [{B}, {S_q}, K], got {tuple(routes.shape)}")
+    K = routes.shape[2]
+    dt = _route_dtype(routes)
+    out = _output(out, (B, S_q, Hq, D), dev)
+    ws_bytes = qsa_forward_workspace_size(B, S_q, K)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().qsa_forward(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(routes), dt,
+                           _strides(routes), B, S_q, S_kv, Hq, Hkv, D, K, _scale(scale, D), _ptr(out),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "qsa_forward")
+    return out
+
+
+def qsa_forward_preprocessed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, route_list: torch.Tensor,
+                             route_count: torch.Tensor, scale: Optional[float] = None,
+                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gather-attention alone, on lists produced by ``qsa_preprocess(routes, S_kv)``."""
+    dev = _require_gpu(q, k, v, route_list, route_count)
+    q, k, v = _bf16_operand(q, "query"), _bf16_operand(k, "key"), _bf16_operand(v, "value")
+    B, S_q, Hq, D, S_kv, Hkv = _attention_shapes(q, k, v)
+    if route_list.dtype != torch.int32 or route_count.dtype != torch.int32:
+        raise ValueError("route_list and route_count must be int32")
+    if route_list.dim() != 3 or tuple(route_list.shape[:2]) != (B, S_q) or tuple(route_count.shape) != (B, S_q):
+        raise ValueError("route_list must be [B, S_q, K] and route_count [B, S_q]")
+    route_list, route_count = route_list.contiguous(), route_count.contiguous()
+    K = route_list.shape[2]
+    out = _output(out, (B, S_q, Hq, D), dev)
+    st = lib().qsa_forward_preprocessed(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+                                        _ptr(route_list), _ptr(route_count), B, S_q, S_kv, Hq, Hkv, D, K,
+                                        _scale(scale, D), _ptr(out), _stream(dev))
+    _check(st, "qsa_forward_preprocessed")
+    return out
+
+
+__all__ = [
+    "qsa_preprocess",
+    "qsa_forward",
+    "qsa_forward_preprocessed",
+    "qsa_forward_workspace_size",
+    "qsa_status_string",
+    "lib",
+    "QSAError",
+    "QSAHipError",
+]

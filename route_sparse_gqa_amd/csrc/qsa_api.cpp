@@ -1,0 +1,271 @@
+// C-ABI entry points of libqsa: host-side argument checks, workspace layout
+// and kernel launches.  No entry point allocates, synchronises the host or
+// reads device memory; every failure is reported before anything is
+// enqueued.  Argument rules follow the route-sparse GQA pages: nonempty
+// dimensions, a positive kv_length, Hq a positive multiple of Hkv, a finite
+// positive scale (fa4_qsa page, `fa4_sparse_gqa_attention` and `_preprocess`
+// parameters), int32/int64 routes (flex_qsa page, `flex_sparse_gqa_attention`),
+// an output independent of the inputs (fa4_qsa page, return value), and no
+// silent fallback to another path (qsa page, `qsa_gqa_attention`).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/qsa.h"
+#include "qsa_internal.h"
+
+#define QSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kMaxKv = int64_t{1} << 31;  // IDs are stored as int32
+constexpr int64_t kMaxGrid = (int64_t{1} << 31) - 1;
+
+struct Range {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi) bytes; empty when lo == hi
+};
+
+// Byte range touched by a strided tensor (shape/strides in elements).
+Range extent(const void* p, const int64_t* shape, const int64_t* strides, int rank, int64_t elem) {
+  int64_t lo = 0, hi = 0;
+  for (int d = 0; d < rank; ++d) {
+    const int64_t span = (shape[d] - 1) * strides[d];
+    if (span < 0) lo += span; else hi += span;
+  }
+  const uintptr_t base = reinterpret_cast<uintptr_t>(p);
+  return Range{base + static_cast<uintptr_t>(lo * elem), base + static_cast<uintptr_t>((hi + 1) * elem)};
+}
+
+Range dense(const void* p, int64_t bytes) {
+  const uintptr_t base = reinterpret_cast<uintptr_t>(p);
+  return Range{base, base + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// a * b with overflow detection (both >= 0).
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+int check_bf16_tensor(const void* p, const int64_t* strides) {
+  if (strides[3] != 1) return QSA_ERR_LAYOUT;
+  if (!aligned(p, 16)) return QSA_ERR_LAYOUT;
+  for (int d = 0; d < 3; ++d)
+    if (strides[d] % 8 != 0) return QSA_ERR_LAYOUT;
+  return QSA_OK;
+}
+
+struct Sizes {
+  int64_t rows = 0;      // B * S_q
+  int64_t list = 0;      // B * S_q * K
+  int64_t list_bytes = 0;
+  int64_t count_bytes = 0;
+};
+
+int check_route_dims(int64_t B, int64_t S_q, int64_t K, Sizes* s) {
+  if (B < 1 || S_q < 1 || K < 1) return QSA_ERR_EMPTY_DIM;
+  if (K > QSA_MAX_ROUTES) return QSA_ERR_LIMIT;
+  if (!mul_ok(B, S_q, &s->rows) || s->rows > kMaxGrid) return QSA_ERR_LIMIT;
+  if (!mul_ok(s->rows, K, &s->list) || s->list > (INT64_MAX >> 3)) return QSA_ERR_LIMIT;
+  s->list_bytes = 4 * s->list;
+  s->count_bytes = 4 * s->rows;
+  return QSA_OK;
+}
+
+constexpr size_t kWorkspaceAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_HIP; }
+
+}  // namespace
+
+QSA_EXPORT const char* qsa_status_string(int status) {
+  switch (status) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case QSA_ERR_EMPTY_DIM: return "dimensions must be nonempty (B, S_q, S_kv, Hq, Hkv, D, K >= 1)";
+    case QSA_ERR_KV_LENGTH: return "kv_length must be in [1, 2^31]";
+    case QSA_ERR_HEADS: return "query_heads must be a positive multiple of kv_heads";
+    case QSA_ERR_HEAD_DIM: return "head dimension must be 64, 128 or 256";
+    case QSA_ERR_ROUTE_DTYPE: return "routes must be int32 or int64";
+    case QSA_ERR_SCALE: return "softmax scale must be finite and positive";
+    case QSA_ERR_LAYOUT: return "tensor layout unsupported (last stride 1, 16-byte aligned rows required)";
+    case QSA_ERR_ALIAS: return "an output overlaps an input or another output";
+    case QSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QSA_ERR_LIMIT: return "size beyond a library limit (K <= 16384, G <= 16, grid size)";
+    case QSA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+QSA_EXPORT size_t qsa_forward_workspace_size(int64_t B, int64_t S_q, int64_t K) {
+  Sizes s;
+  if (B < 1 || S_q < 1 || K < 1) return 0;
+  if (!mul_ok(B, S_q, &s.rows) || !mul_ok(s.rows, K, &s.list) || s.list > (INT64_MAX >> 3)) return 0;
+  return round_up(static_cast<size_t>(4 * s.list), kWorkspaceAlign) +
+         round_up(static_cast<size_t>(4 * s.rows), kWorkspaceAlign);
+}
+
+QSA_EXPORT int qsa_preprocess(const void* routes, int routes_dtype, int64_t B, int64_t S_q, int64_t K,
+                              const int64_t route_strides[3], int64_t kv_length, int32_t* route_list,
+                              int32_t* route_count, uint8_t* membership, int32_t* tile_class, void* stream) {
+  Sizes s;
+  if (int st = check_route_dims(B, S_q, K, &s)) return st;
+  if (routes == nullptr || route_strides == nullptr || route_list == nullptr || route_count == nullptr)
+    return QSA_ERR_NULL_POINTER;
+  if (kv_length < 1 || kv_length > kMaxKv) return QSA_ERR_KV_LENGTH;
+  if (routes_dtype != QSA_INT32 && routes_dtype != QSA_INT64) return QSA_ERR_ROUTE_DTYPE;
+  const int64_t relem = routes_dtype == QSA_INT64 ? 8 : 4;
+  if (!aligned(routes, relem) || !aligned(route_list, 4) || !aligned(route_count, 4)) return QSA_ERR_LAYOUT;
+  if (membership != nullptr && !aligned(membership, 16)) return QSA_ERR_LAYOUT;
+  if (tile_class != nullptr && !aligned(tile_class, 4)) return QSA_ERR_LAYOUT;
+
+  const int64_t ldm = (kv_length + QSA_TILE - 1) / QSA_TILE * QSA_TILE;
+  const int64_t n_ti = (S_q + QSA_TILE - 1) / QSA_TILE, n_tj = (kv_length + QSA_TILE - 1) / QSA_TILE;
+  int64_t mem_bytes = 0, tiles = 0;
+  if (membership != nullptr && !mul_ok(s.rows, ldm, &mem_bytes)) return QSA_ERR_LIMIT;
+  if (!mul_ok(B * n_ti, n_tj, &tiles) || tiles > (INT64_MAX >> 3)) return QSA_ERR_LIMIT;
+  if ((membership != nullptr || tile_class != nullptr) &&
+      B * n_ti * ((ldm + 65535) / 65536) > kMaxGrid)
+    return QSA_ERR_LIMIT;
+
+  const int64_t rshape[3] = {B, S_q, K};
+  const Range r_in = extent(routes, rshape, route_strides, 3, relem);
+  const Range outs[4] = {dense(route_list, s.list_bytes), dense(route_count, s.count_bytes),
+                         membership ? dense(membership, mem_bytes) : Range{},
+                         tile_class ? dense(tile_class, 4 * tiles) : Range{}};
+  for (int a = 0; a < 4; ++a) {
+    if (overlap(outs[a], r_in)) return QSA_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return QSA_ERR_ALIAS;
+  }
+
+  (void)hipGetLastError();  // clear a stale error so the checks below see only ours
+  hipStream_t st = as_stream(stream);
+  int rc = hip_status(qsa::launch_route_normalize(routes, routes_dtype == QSA_INT64, B, S_q, K, route_strides,
+                                                  kv_length, route_list, route_count, st));
+  if (rc != QSA_OK) return rc;
+  return hip_status(
+      qsa::launch_membership_tiles(route_list, route_count, B, S_q, K, kv_length, membership, tile_class, st));
+}
+
+namespace {
+
+int check_attention(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
+                    const void* v, const int64_t v_strides[4], int64_t B, int64_t S_q, int64_t S_kv,
+                    int64_t Hq, int64_t Hkv, int64_t D, int64_t K, float scale, void* out, Sizes* s,
+                    Range* r_q, Range* r_k, Range* r_v, Range* r_out) {
+  if (S_kv < 1 || Hq < 1 || Hkv < 1 || D < 1) return QSA_ERR_EMPTY_DIM;
+  if (int st = check_route_dims(B, S_q, K, s)) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || q_strides == nullptr ||
+      k_strides == nullptr || v_strides == nullptr)
+    return QSA_ERR_NULL_POINTER;
+  if (S_kv > kMaxKv) return QSA_ERR_KV_LENGTH;
+  if (Hq % Hkv != 0) return QSA_ERR_HEADS;
+  if (D != 64 && D != 128 && D != 256) return QSA_ERR_HEAD_DIM;
+  if (Hq / Hkv > QSA_MAX_GROUP) return QSA_ERR_LIMIT;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return QSA_ERR_SCALE;
+  if (int st = check_bf16_tensor(q, q_strides)) return st;
+  if (int st = check_bf16_tensor(k, k_strides)) return st;
+  if (int st = check_bf16_tensor(v, v_strides)) return st;
+  if (!aligned(out, 16)) return QSA_ERR_LAYOUT;
+  int64_t units = 0, out_elems = 0;
+  if (!mul_ok(s->rows, Hkv, &units) || (units + 3) / 4 > kMaxGrid) return QSA_ERR_LIMIT;
+  if (!mul_ok(s->rows, Hq * D, &out_elems) || out_elems > (INT64_MAX >> 2)) return QSA_ERR_LIMIT;
+  const int64_t qshape[4] = {B, S_q, Hq, D}, kshape[4] = {B, S_kv, Hkv, D};
+  *r_q = extent(q, qshape, q_strides, 4, 2);
+  *r_k = extent(k, kshape, k_strides, 4, 2);
+  *r_v = extent(v, kshape, v_strides, 4, 2);
+  *r_out = dense(out, 2 * out_elems);
+  if (overlap(*r_out, *r_q) || overlap(*r_out, *r_k) || overlap(*r_out, *r_v)) return QSA_ERR_ALIAS;
+  return QSA_OK;
+}
+
+qsa::AttnArgs attn_args(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
+                        const void* v, const int64_t v_strides[4], const int32_t* list, const int32_t* count,
+                        int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,
+                        float scale, void* out) {
+  qsa::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  std::memcpy(a.qs, q_strides, sizeof a.qs);
+  std::memcpy(a.ks, k_strides, sizeof a.ks);
+  std::memcpy(a.vs, v_strides, sizeof a.vs);
+  a.route_list = list;
+  a.route_count = count;
+  a.B = B; a.S_q = S_q; a.S_kv = S_kv; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.K = K;
+  a.scale = scale;
+  a.out = static_cast<uint16_t*>(out);
+  return a;
+}
+
+}  // namespace
+
+QSA_EXPORT int qsa_forward(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
+                           const void* v, const int64_t v_strides[4], const void* routes, int routes_dtype,
+                           const int64_t route_strides[3], int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq,
+                           int64_t Hkv, int64_t D, int64_t K, float scale, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  Sizes s;
+  Range r_q, r_k, r_v, r_out;
+  if (int st = check_attention(q, q_strides, k, k_strides, v, v_strides, B, S_q, S_kv, Hq, Hkv, D, K, scale,
+                               out, &s, &r_q, &r_k, &r_v, &r_out))
+    return st;
+  if (routes == nullptr || route_strides == nullptr) return QSA_ERR_NULL_POINTER;
+  if (routes_dtype != QSA_INT32 && routes_dtype != QSA_INT64) return QSA_ERR_ROUTE_DTYPE;
+  const int64_t relem = routes_dtype == QSA_INT64 ? 8 : 4;
+  if (!aligned(routes, relem)) return QSA_ERR_LAYOUT;
+  if (workspace == nullptr) return QSA_ERR_WORKSPACE;
+  const size_t need = qsa_forward_workspace_size(B, S_q, K);
+  if (need == 0 || workspace_bytes < need || !aligned(workspace, kWorkspaceAlign)) return QSA_ERR_WORKSPACE;
+  const int64_t rshape[3] = {B, S_q, K};
+  const Range r_in = extent(routes, rshape, route_strides, 3, relem);
+  const Range r_ws = dense(workspace, static_cast<int64_t>(need));
+  if (overlap(r_out, r_in) || overlap(r_out, r_ws) || overlap(r_ws, r_q) || overlap(r_ws, r_k) ||
+      overlap(r_ws, r_v) || overlap(r_ws, r_in))
+    return QSA_ERR_ALIAS;
+
+  int32_t* list = static_cast<int32_t*>(workspace);
+  int32_t* count = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                              round_up(static_cast<size_t>(s.list_bytes), kWorkspaceAlign));
+  (void)hipGetLastError();
+  hipStream_t st = as_stream(stream);
+  int rc = hip_status(qsa::launch_route_normalize(routes, routes_dtype == QSA_INT64, B, S_q, K, route_strides,
+                                                  S_kv, list, count, st));
+  if (rc != QSA_OK) return rc;
+  const qsa::AttnArgs a =
+      attn_args(q, q_strides, k, k_strides, v, v_strides, list, count, B, S_q, S_kv, Hq, Hkv, D, K, scale, out);
+  return hip_status(qsa::launch_gather_attention(a, st));
+}
+
+QSA_EXPORT int qsa_forward_preprocessed(const void* q, const int64_t q_strides[4], const void* k,
+                                        const int64_t k_strides[4], const void* v, const int64_t v_strides[4],
+                                        const int32_t* route_list, const int32_t* route_count, int64_t B,
+                                        int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,
+                                        float scale, void* out, void* stream) {
+  Sizes s;
+  Range r_q, r_k, r_v, r_out;
+  if (int st = check_attention(q, q_strides, k, k_strides, v, v_strides, B, S_q, S_kv, Hq, Hkv, D, K, scale,
+                               out, &s, &r_q, &r_k, &r_v, &r_out))
+    return st;
+  if (route_list == nullptr || route_count == nullptr) return QSA_ERR_NULL_POINTER;
+  if (!aligned(route_list, 4) || !aligned(route_count, 4)) return QSA_ERR_LAYOUT;
+  if (overlap(r_out, dense(route_list, s.list_bytes)) || overlap(r_out, dense(route_count, s.count_bytes)))
+    return QSA_ERR_ALIAS;
+  (void)hipGetLastError();
+  const qsa::AttnArgs a = attn_args(q, q_strides, k, k_strides, v, v_strides, route_list, route_count, B, S_q,
+                                    S_kv, Hq, Hkv, D, K, scale, out);
+  return hip_status(qsa::launch_gather_attention(a, as_stream(stream)));
+}

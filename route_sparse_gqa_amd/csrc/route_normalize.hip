@@ -1,0 +1,203 @@
+// Route normalisation for gfx950: per query row, keep the valid route IDs
+// (0 <= id < kv_length, int32 inputs sign-extended), sort them ascending,
+// drop duplicates and compact them into an int32 list padded with -1.
+//
+// Definition: fa4_qsa page, `_preprocess` (duplicates collapse; invalid IDs,
+// including large int64 values, are discarded before indexing); flex_qsa
+// page, `_routes_to_membership` (negative or out-of-range entries are
+// padding); qsa page, `QSARouteSelection` (int32 IDs, -1 marks padding).
+//
+// Design: one row is sorted by T = 64*W threads holding E keys each in
+// registers (P = T*E >= K positions; position of register e of thread t is
+// t*E + e).  Invalid slots become the key 0xFFFFFFFF, which sorts last.  The
+// bitonic network exchanges partners in registers (distance < E), through
+// wavefront shuffles (distance < 64*E) or through LDS (larger distances).
+// Slots are loaded strided (slot e*T + t) so every load is coalesced; the
+// network sorts any initial placement.  Duplicates are adjacent after the
+// sort; per-thread keep counts are prefix-summed with one ballot per count
+// bit, then the kept keys are compacted through LDS and written out
+// coalesced.
+#include <hip/hip_runtime.h>
+
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+constexpr uint32_t kAbsent = 0xFFFFFFFFu;
+
+__device__ __forceinline__ uint32_t route_key(int64_t x, int64_t kv_length) {
+  return (x >= 0 && x < kv_length) ? static_cast<uint32_t>(x) : kAbsent;
+}
+
+// Keep the smaller key at the lower position of an ascending pair, the larger
+// one for a descending pair.
+__device__ __forceinline__ uint32_t exchange(uint32_t mine, uint32_t other, int pos, int k, int s) {
+  const bool ascending = (pos & k) == 0;
+  const bool lower = (pos & s) == 0;
+  return (lower == ascending) ? min(mine, other) : max(mine, other);
+}
+
+template <int W>
+struct RowsPerBlock {
+  static constexpr int value = W >= 4 ? 1 : 4 / W;
+};
+
+template <int E, int W, typename RouteT>
+__global__ void __launch_bounds__(64 * W * RowsPerBlock<W>::value)
+    route_normalize_kernel(const RouteT* __restrict__ routes, int64_t rs0, int64_t rs1, int64_t rs2,
+                           int64_t S_q, int64_t K, int64_t kv_length, int64_t n_rows,
+                           int32_t* __restrict__ route_list, int32_t* __restrict__ route_count) {
+  constexpr int T = 64 * W;
+  constexpr int ROWS = RowsPerBlock<W>::value;
+  constexpr int P = T * E;
+  __shared__ uint32_t xch[ROWS][P];
+  __shared__ uint32_t wave_last[ROWS][W];
+  __shared__ int wave_kept[ROWS][W];
+
+  const int tid = threadIdx.x;
+  const int sub = tid / T;
+  const int t = tid % T;
+  const int lane = tid & 63;
+  const int wave = t >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * ROWS + sub;
+  const bool active = row < n_rows;  // whole rows; every thread still meets every barrier
+
+  // ---- load (strided slots, coalesced) -----------------------------------
+  uint32_t x[E];
+  {
+    const int64_t b = active ? row / S_q : 0;
+    const int64_t i = active ? row % S_q : 0;
+    const RouteT* src = routes + b * rs0 + i * rs1;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int64_t slot = static_cast<int64_t>(e) * T + t;
+      x[e] = (active && slot < K) ? route_key(static_cast<int64_t>(src[slot * rs2]), kv_length) : kAbsent;
+    }
+  }
+
+  // ---- bitonic sort over positions t*E + e --------------------------------
+#pragma unroll
+  for (int k = 2; k <= P; k <<= 1) {
+#pragma unroll
+    for (int s = k >> 1; s > 0; s >>= 1) {
+      if (s >= 64 * E) {  // partner in another wave of this row
+#pragma unroll
+        for (int e = 0; e < E; ++e) xch[sub][t * E + e] = x[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int pos = t * E + e;
+          x[e] = exchange(x[e], xch[sub][pos ^ s], pos, k, s);
+        }
+        __syncthreads();
+      } else if (s >= E) {  // partner lane in this wave, same register
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(x[e]), s / E));
+          x[e] = exchange(x[e], other, t * E + e, k, s);
+        }
+      } else {  // both positions in this thread
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & s) == 0) {
+            const bool ascending = ((t * E + e) & k) == 0;
+            const uint32_t a = x[e], c = x[e + s];
+            x[e] = ascending ? min(a, c) : max(a, c);
+            x[e + s] = ascending ? max(a, c) : min(a, c);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- drop duplicates (equal keys are adjacent) --------------------------
+  uint32_t prev = static_cast<uint32_t>(__shfl_up(static_cast<int>(x[E - 1]), 1));
+  if (lane == 63) wave_last[sub][wave] = x[E - 1];
+  __syncthreads();
+  if (lane == 0) prev = wave > 0 ? wave_last[sub][wave - 1] : kAbsent;
+  // position 0 has no predecessor; kAbsent never equals a valid key
+  bool keep[E];
+  int kept = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t before = e == 0 ? prev : x[e - 1];
+    keep[e] = x[e] != kAbsent && x[e] != before;
+    kept += keep[e] ? 1 : 0;
+  }
+
+  // ---- ballot prefix sum of per-thread counts (kept <= E < 32) -------------
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int offset = 0, wave_total = 0;
+#pragma unroll
+  for (int bit = 0; (1 << bit) <= E; ++bit) {
+    const uint64_t m = __ballot((kept >> bit) & 1);
+    offset += __popcll(m & below) << bit;
+    wave_total += __popcll(m) << bit;
+  }
+  if (lane == 0) wave_kept[sub][wave] = wave_total;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const int c = wave_kept[sub][w];
+    offset += w < wave ? c : 0;
+    total += c;
+  }
+
+  // ---- compact through LDS, then write the padded list coalesced ----------
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (keep[e]) xch[sub][offset++] = x[e];
+  }
+  __syncthreads();
+  if (active) {
+    int32_t* dst = route_list + row * K;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int64_t slot = static_cast<int64_t>(e) * T + t;
+      if (slot < K) dst[slot] = slot < total ? static_cast<int32_t>(xch[sub][slot]) : -1;
+    }
+    if (t == 0) route_count[row] = total;
+  }
+}
+
+template <int E, int W, typename RouteT>
+hipError_t launch_sorted(const RouteT* routes, const int64_t* st, int64_t B, int64_t S_q, int64_t K,
+                         int64_t kv_length, int32_t* list, int32_t* count, hipStream_t stream) {
+  constexpr int ROWS = RowsPerBlock<W>::value;
+  const int64_t n_rows = B * S_q;
+  const int64_t blocks = (n_rows + ROWS - 1) / ROWS;
+  hipLaunchKernelGGL((route_normalize_kernel<E, W, RouteT>), dim3(static_cast<uint32_t>(blocks)),
+                     dim3(64 * W * ROWS), 0, stream, routes, st[0], st[1], st[2], S_q, K, kv_length,
+                     n_rows, list, count);
+  return hipGetLastError();
+}
+
+template <typename RouteT>
+hipError_t dispatch(const RouteT* routes, const int64_t* st, int64_t B, int64_t S_q, int64_t K,
+                    int64_t kv_length, int32_t* list, int32_t* count, hipStream_t stream) {
+  if (K <= 64) return launch_sorted<1, 1>(routes, st, B, S_q, K, kv_length, list, count, stream);
+  if (K <= 128) return launch_sorted<2, 1>(routes, st, B, S_q, K, kv_length, list, count, stream);
+  if (K <= 256) return launch_sorted<4, 1>(routes, st, B, S_q, K, kv_length, list, count, stream);
+  if (K <= 512) return launch_sorted<8, 1>(routes, st, B, S_q, K, kv_length, list, count, stream);
+  if (K <= 1024) return launch_sorted<8, 2>(routes, st, B, S_q, K, kv_length, list, count, stream);
+  if (K <= 2048) return launch_sorted<8, 4>(routes, st, B, S_q, K, kv_length, list, count, stream);
+  if (K <= 4096) return launch_sorted<8, 8>(routes, st, B, S_q, K, kv_length, list, count, stream);
+  if (K <= 8192) return launch_sorted<8, 16>(routes, st, B, S_q, K, kv_length, list, count, stream);
+  return launch_sorted<16, 16>(routes, st, B, S_q, K, kv_length, list, count, stream);
+}
+
+}  // namespace
+
+hipError_t launch_route_normalize(const void* routes, bool routes_int64, int64_t B, int64_t S_q,
+                                  int64_t K, const int64_t route_strides[3], int64_t kv_length,
+                                  int32_t* route_list, int32_t* route_count, hipStream_t stream) {
+  if (routes_int64)
+    return dispatch(static_cast<const int64_t*>(routes), route_strides, B, S_q, K, kv_length, route_list,
+                    route_count, stream);
+  return dispatch(static_cast<const int32_t*>(routes), route_strides, B, S_q, K, kv_length, route_list,
+                  route_count, stream);
+}
+
+}  // namespace qsa

@@ -1,0 +1,93 @@
+"""The C ABI library loads, exports every entry point its header declares and
+rejects bad arguments on the host (CPU only: no call here reaches a launch)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import route_sparse_gqa_amd as qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int|size_t)\s*\*?\s*(qsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def _declared_constants():
+    text = open(HEADER).read()
+    return {m[0]: int(m[1]) for m in re.findall(r"#define\s+(QSA_\w+)\s+(-?\d+)", text)}
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted([
+        "qsa_preprocess", "qsa_forward", "qsa_forward_preprocessed", "qsa_forward_workspace_size",
+        "qsa_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = qsa.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), f"libqsa.so does not export {name}"
+
+
+def test_python_constants_match_header():
+    c = _declared_constants()
+    assert c["QSA_INT32"] == qsa.QSA_INT32 and c["QSA_INT64"] == qsa.QSA_INT64
+    assert c["QSA_TILE"] == qsa.TILE and c["QSA_MAX_ROUTES"] == qsa.MAX_ROUTES
+    assert c["QSA_MAX_GROUP"] == qsa.MAX_GROUP and c["QSA_ERR_HIP"] == qsa._HIP_ERROR
+
+
+def test_status_strings():
+    codes = [v for k, v in _declared_constants().items() if k.startswith("QSA_ERR_") or k == "QSA_OK"]
+    texts = [qsa.qsa_status_string(c) for c in codes]
+    assert len(set(texts)) == len(codes) and "unknown status" not in texts
+    assert qsa.qsa_status_string(12345) == "unknown status"
+
+
+def test_workspace_size():
+    ws = qsa.qsa_forward_workspace_size
+    assert ws(2, 4096, 512) == 4 * 2 * 4096 * 512 + 4 * 2 * 4096
+    assert ws(1, 3, 5) == 256 + 256  # lists and counts each rounded to 256 bytes
+    assert ws(0, 10, 10) == 0 and ws(1, 1, 0) == 0
+    assert ws(1 << 40, 1 << 40, 1) == 0  # overflow
+
+
+def _call_forward(B=1, S_q=4, S_kv=4, Hq=2, Hkv=1, D=64, K=2, scale=0.1, null_routes=False):
+    """Every call made with this helper carries one invalid argument (fake pointers never reach a launch)."""
+    L = qsa.lib()
+    sq = (ctypes.c_int64 * 4)(S_q * Hq * D, Hq * D, D, 1)
+    sk = (ctypes.c_int64 * 4)(S_kv * Hkv * D, Hkv * D, D, 1)
+    s3 = (ctypes.c_int64 * 3)(S_q * K, K, 1)
+    fq, fk, fv, fr, fo, fw = (ctypes.c_void_p(n << 32) for n in range(1, 7))  # distinct, never dereferenced
+    return L.qsa_forward(fq, sq, fk, sk, fv, sk, None if null_routes else fr, 1, s3, B, S_q, S_kv, Hq, Hkv,
+                         D, K, scale, fo, fw, 1 << 20, None)
+
+
+@pytest.mark.parametrize("dims", [dict(B=0), dict(S_q=0), dict(S_kv=0), dict(Hq=0), dict(Hkv=0), dict(D=0),
+                                  dict(K=0)])
+def test_empty_dimensions_rejected_before_anything_runs(dims):
+    assert _call_forward(**dims) == -2
+
+
+def test_other_host_checks():
+    assert _call_forward(Hq=3, Hkv=2) == -4
+    assert _call_forward(D=96) == -5
+    assert _call_forward(Hq=64, Hkv=2) == -11
+    assert _call_forward(K=20000) == -11
+    assert _call_forward(S_kv=(1 << 31) + 1) == -3
+    assert _call_forward(null_routes=True) == -1
+    L = qsa.lib()
+    s3 = (ctypes.c_int64 * 3)(1, 1, 1)
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.qsa_preprocess(fake, 1, 1, 2, 0, s3, 5, fake, fake, None, None, None) == -2
+    assert L.qsa_preprocess(fake, 1, 1, 2, 3, s3, 0, fake, fake, None, None, None) == -3
+    assert L.qsa_preprocess(fake, 9, 1, 2, 3, s3, 5, fake, fake, None, None, None) == -6
+    assert L.qsa_preprocess(None, 1, 1, 2, 3, s3, 5, fake, fake, None, None, None) == -1

@@ -108,7 +108,7 @@ def cpu_baseline(w, q, k, v, routes, counts, target_s: float):
 
     S_q = w.S_q
     per_row_routes = counts.sum(axis=0)  # summed over the batch
-    start = S_q // 2
+    start = 0
 
     def run(nrows):
         r0, r1 = start, min(S_q, start + nrows)

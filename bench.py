@@ -49,7 +49,26 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="JSON with rocprofv3-derived HBM bytes per launch of the attention kernel")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run plain device-to-device copies of this many MiB (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int, reps: int = 5) -> None:
+    """Plain copies of a known size: FETCH_SIZE / WRITE_SIZE per dispatch of this kernel
+    give the scale factor between the counters and bytes actually moved."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "copies": reps}), flush=True)
 
 
 class Plan:
@@ -136,6 +155,9 @@ def cpu_baseline(w, q, k, v, routes, counts, target_s: float):
 
 def main():
     args = parse_args()
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)

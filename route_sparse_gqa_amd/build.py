@@ -33,6 +33,9 @@ COMMON_FLAGS = [
     "-Wall",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the online-softmax rescale then needs
+    # no AGPR round trips and the attention kernel fits two waves per SIMD
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
 ]
 

@@ -7,22 +7,28 @@
 // [B, Q, Hkv, G, D]: query head h reads KV head h / G).
 //
 // Design (one wavefront per (b, i, hk) work unit, four per workgroup):
-//  * The G query heads of the unit are the N = 16 columns of
-//    v_mfma_f32_16x16x32_bf16 (padded with zero heads when G < 16).  Scores
-//    are computed transposed, S^T = K Q^T, with 16 routed keys as the M rows,
-//    so each lane ends up owning one head (lane % 16) and four keys per
-//    16-key tile.  Row max/sum reductions are then two cross-lane xors.
-//  * Routed K rows are loaded straight from global memory into the MFMA A
-//    operand: lane (c, g) = (lane % 16, lane / 16) loads 16 bytes (8 dims)
-//    of key c, so one load instruction gathers 16 keys x 64 contiguous bytes.
-//  * PV is computed transposed too, O^T = V^T P^T, so the probabilities stay
-//    in the lane that produced them (the B operand needs no shuffle) and the
-//    online-softmax rescale is lane-local.  The V^T operand needs 8 keys of
-//    one dim per lane, so the 32 routed V rows of a chunk are gathered with
-//    coalesced 16-byte loads into this wave's LDS slab and read back
-//    transposed.
-//  * Online softmax in fp32 with exp2 and the scale folded into log2(e);
-//    probabilities are rounded to bf16 once and the same rounded values feed
+//  * The G query heads of the unit are the N = 16 columns of the MFMA (zero
+//    padded when G < 16).  Scores are computed transposed, S^T = K Q^T with
+//    v_mfma_f32_16x16x32_bf16, 16 routed keys as the M rows: the gathered K
+//    rows load straight into the A operand (lane (c, g) = (lane % 16,
+//    lane / 16) loads 16 bytes = 8 dims of key c, so one load instruction
+//    gathers 16 keys x 64 contiguous bytes), and each lane ends up owning one
+//    head and four keys.  Row max/sum reductions are two cross-lane xors.
+//  * PV is computed transposed too, O^T = V^T P^T with
+//    v_mfma_f32_16x16x16_bf16: the four probabilities of a lane are exactly
+//    its B operand (no shuffle) and the online-softmax rescale is
+//    lane-local.  The V^T operand needs 4 keys of one dim per lane: the 16
+//    routed V rows of a chunk are gathered with coalesced 16-byte loads, put
+//    in this wave's LDS slab and read back with one gfx950 transposing LDS
+//    load per 16-dim tile.
+//  * Software pipeline: while chunk c is computed, the K and V rows of chunk
+//    c + 1 (in registers) and the route IDs of chunk c + 2 are in flight.
+//    The IDs are issued before the rows and used one iteration later, so the
+//    in-order load counter never makes the rows wait for them.
+//  * Online softmax in fp32 with exp2 and the scale folded into log2(e).  The
+//    reference max is raised only when a chunk exceeds it by more than 2^8,
+//    so the accumulator rescale is skipped once the max has settled.
+//    Probabilities are rounded to bf16 once; the same rounded values feed
 //    both the PV product and the normaliser.
 #include <hip/hip_runtime.h>
 
@@ -32,25 +38,35 @@ namespace qsa {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in registers
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vectors stay in registers
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kWaves = 4;     // work units per workgroup
-constexpr int kChunk = 32;    // routes per inner iteration (PV contraction depth)
+constexpr int kWaves = 4;   // work units per workgroup
+constexpr int kChunk = 16;  // routes per inner iteration (M of S^T, K of PV)
+constexpr float kMaxSlack = 8.0f;  // log2 headroom before the reference max is raised
 
 template <int D>
 struct Geometry {
-  static constexpr int kSteps = D / 32;                // QK^T k-steps of 32 dims
-  static constexpr int kDimTiles = D / 16;             // O^T row tiles of 16 dims
-  static constexpr int kLanesPerRow = D / 8;           // 16-byte pieces per V row
+  static constexpr int kSteps = D / 32;                 // QK^T k-steps of 32 dims
+  static constexpr int kDimTiles = D / 16;              // O^T row tiles of 16 dims
+  static constexpr int kLanesPerRow = D / 8;            // 16-byte pieces per V row
   static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   static constexpr int kLoads = kChunk / kRowsPerLoad;  // V load instructions per chunk
-  static constexpr int kStride = D + 8;                // LDS row stride in bf16 (16-byte aligned rows)
+  static constexpr int kStride = D + 16;                // LDS row stride in bf16 (2D + 32 bytes)
 };
 
-__device__ __forceinline__ bf16x8 load16(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+__device__ __forceinline__ u32x4 load16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Transposed LDS read (gfx950): within each 16-lane group, slot j of lane i
+// receives element i % 4 of the 4-element row piece addressed by lane
+// 4 * j + i / 4.  With lane L addressing row L / 4, columns 16t + 4 * (L % 4),
+// lane (c, g) receives rows 4g .. 4g+3 of column 16t + c.
+__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));  // generic -> LDS address-space cast
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -59,7 +75,22 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D>
+// Byte offset of a gathered row: 32-bit when every row of the tensor lies
+// within 4 GiB of its (batch, head) base, else 64-bit.
+template <bool kNarrow>
+struct RowOffset {
+  __device__ static __forceinline__ uint32_t of(int32_t id, int64_t stride_bytes) {
+    return static_cast<uint32_t>(id) * static_cast<uint32_t>(stride_bytes);
+  }
+};
+template <>
+struct RowOffset<false> {
+  __device__ static __forceinline__ int64_t of(int32_t id, int64_t stride_bytes) {
+    return static_cast<int64_t>(id) * stride_bytes;
+  }
+};
+
+template <int D, bool kNarrow>
 __global__ void __launch_bounds__(64 * kWaves)
     gather_attention_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                             const uint16_t* __restrict__ v, int64_t qs0, int64_t qs1, int64_t qs2,
@@ -71,7 +102,7 @@ __global__ void __launch_bounds__(64 * kWaves)
   __shared__ __attribute__((aligned(16))) uint16_t slab[kWaves][kChunk * Geo::kStride];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));  // wave-uniform
   const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   if (unit >= n_units) return;  // no workgroup barriers in this kernel
   const int64_t hk = unit % Hkv;
@@ -98,58 +129,56 @@ __global__ void __launch_bounds__(64 * kWaves)
   {
     const uint16_t* qp = q + b * qs0 + i * qs1 + (hk * G + (head_ok ? c : 0)) * qs2 + 8 * g;
 #pragma unroll
-    for (int s = 0; s < Geo::kSteps; ++s) {
-      qf[s] = head_ok ? load16(qp + 32 * s) : bf16x8{};
-    }
+    for (int s = 0; s < Geo::kSteps; ++s)
+      qf[s] = head_ok ? __builtin_bit_cast(bf16x8, load16(reinterpret_cast<const char*>(qp + 32 * s)))
+                      : bf16x8{};
   }
 
   f32x4 acc[Geo::kDimTiles];
 #pragma unroll
   for (int t = 0; t < Geo::kDimTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max (log2 domain) of head c
+  float m_run = -INFINITY;  // reference max (log2 domain) of head c
   float l_run = 0.f;        // this lane's share of the running sum of head c
 
   const int32_t* lst = route_list + row * K;
-  const uint16_t* kb = k + b * ks0 + hk * ks2 + 8 * g;
-  const uint16_t* vb = v + b * vs0 + hk * vs2 + 8 * (lane % Geo::kLanesPerRow);
+  const int64_t ks1b = 2 * ks1, vs1b = 2 * vs1;  // row strides in bytes
+  const char* kb = reinterpret_cast<const char*>(k + b * ks0 + hk * ks2) + 16 * g;
+  const char* vb = reinterpret_cast<const char*>(v + b * vs0 + hk * vs2) + 16 * (lane % Geo::kLanesPerRow);
   uint16_t* my_slab = slab[wave];
   const int32_t id_max = static_cast<int32_t>(S_kv - 1);
-
-  for (int base = 0; base < n; base += kChunk) {
-    // Route IDs of keys base + c and base + 16 + c (tails repeat the last route).
-    const int32_t id0 = min(max(lst[min(base + c, n - 1)], 0), id_max);
-    const int32_t id1 = min(max(lst[min(base + 16 + c, n - 1)], 0), id_max);
-
-    // Gather K straight into the A operand of S^T = K Q^T.
-    bf16x8 kf0[Geo::kSteps], kf1[Geo::kSteps];
-    {
-      const uint16_t* k0 = kb + static_cast<int64_t>(id0) * ks1;
-      const uint16_t* k1 = kb + static_cast<int64_t>(id1) * ks1;
+  auto clamp_id = [&](int32_t x) { return min(max(x, 0), id_max); };
+  // Raw route ID of key base + c (tails repeat the last route; clamped later).
+  auto load_id = [&](int base) { return lst[min(base + c, n - 1)]; };
+  // K rows of the chunk straight into the A operand of S^T = K Q^T.
+  auto load_k = [&](int32_t id, bf16x8* kf) {
+    const char* kp = kb + RowOffset<kNarrow>::of(id, ks1b);
 #pragma unroll
-      for (int s = 0; s < Geo::kSteps; ++s) {
-        kf0[s] = load16(k0 + 32 * s);
-        kf1[s] = load16(k1 + 32 * s);
-      }
-    }
-    // Gather the chunk's V rows (coalesced 16-byte pieces) into registers.
-    u32x4 vr[Geo::kLoads];
+    for (int s = 0; s < Geo::kSteps; ++s) kf[s] = __builtin_bit_cast(bf16x8, load16(kp + 64 * s));
+  };
+  // V rows of the chunk in 16-byte pieces; row r's ID lives in lane r.
+  auto load_v = [&](int32_t id, u32x4* vr) {
 #pragma unroll
     for (int u = 0; u < Geo::kLoads; ++u) {
-      const int r = u * Geo::kRowsPerLoad + lane / Geo::kLanesPerRow;  // chunk row of this lane
-      const int src = (u * Geo::kRowsPerLoad < 16) ? id0 : id1;       // uniform per u
-      const int32_t idr = __shfl(src, r & 15);
-      vr[u] = *reinterpret_cast<const u32x4*>(vb + static_cast<int64_t>(idr) * vs1);
+      const int32_t idr = __shfl(id, u * Geo::kRowsPerLoad + lane / Geo::kLanesPerRow);
+      vr[u] = load16(vb + RowOffset<kNarrow>::of(idr, vs1b));
     }
+  };
 
-    // Scores: lane holds S^T[key 16*tau + 4g + r][head c].
-    f32x4 st0 = {0.f, 0.f, 0.f, 0.f}, st1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < Geo::kSteps; ++s) {
-      st0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf0[s], qf[s], st0, 0, 0, 0);
-      st1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf1[s], qf[s], st1, 0, 0, 0);
-    }
+  bf16x8 kf[Geo::kSteps];
+  u32x4 vr[Geo::kLoads];
+  int32_t raw_next = load_id(kChunk);  // issued first: used after the rows below
+  {
+    const int32_t id0 = clamp_id(load_id(0));
+    load_k(id0, kf);
+    load_v(id0, vr);
+  }
+  int32_t id_next = clamp_id(raw_next);
 
-    // Stage V rows in LDS (row-major, padded stride).
+  const uint16_t* tr = my_slab + (lane >> 2) * Geo::kStride + 4 * (lane & 3);
+  for (int base = 0; base < n; base += kChunk) {
+    const bool more = base + kChunk < n;  // wave-uniform
+
+    // Stage this chunk's V rows in LDS (row-major, padded stride).
     wave_lds_sync();  // previous chunk's transposed reads are complete
 #pragma unroll
     for (int u = 0; u < Geo::kLoads; ++u) {
@@ -157,46 +186,49 @@ __global__ void __launch_bounds__(64 * kWaves)
       *reinterpret_cast<u32x4*>(my_slab + r * Geo::kStride + 8 * (lane % Geo::kLanesPerRow)) = vr[u];
     }
 
-    // Online softmax (log2 domain).
-    float x[8];
+    // Scores: lane holds S^T[key 4g + r][head c].
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < Geo::kSteps; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], st, 0, 0, 0);
+
+    // Prefetch: IDs two chunks ahead first, then the next chunk's K and V rows.
+    if (more) {
+      raw_next = load_id(base + 2 * kChunk);
+      load_k(id_next, kf);
+      load_v(id_next, vr);
+    }
+
+    // Online softmax (log2 domain) against a lazily raised reference max.
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = base + 4 * g + r < n ? st[r] * scale_log2e : -INFINITY;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));      // finite: the chunk holds at least one key
+    if (__ballot(mx > m_run + kMaxSlack)) {  // wave-uniform; always taken on the first chunk
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < Geo::kDimTiles; ++t) acc[t] *= alpha;
+    }
+    bf16x4 pf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int key0 = base + 4 * g + r, key1 = base + 16 + 4 * g + r;
-      x[r] = key0 < n ? st0[r] * scale_log2e : -INFINITY;
-      x[4 + r] = key1 < n ? st1[r] * scale_log2e : -INFINITY;
+      pf[r] = static_cast<__bf16>(exp2f(x[r] - m_run));
+      l_run += static_cast<float>(pf[r]);
     }
-    float mx = x[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);  // finite: the chunk holds at least one key
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    bf16x8 pf;
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 p = static_cast<__bf16>(exp2f(x[j] - m_new));
-      pf[j] = p;
-      psum += static_cast<float>(p);
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < Geo::kDimTiles; ++t) acc[t] *= alpha;
+    const i16x4 pb = __builtin_bit_cast(i16x4, pf);
 
-    // O^T += V^T P^T; element j of lane group g is key 16*(j/4) + 4g + j%4.
+    // O^T += V^T P^T: one transposed LDS read gives lane (c, g) keys 4g..4g+3
+    // of dim 16t + c, matching its four probabilities.
     wave_lds_sync();  // V rows visible to every lane of this wave
 #pragma unroll
-    for (int t = 0; t < Geo::kDimTiles; ++t) {
-      bf16x8 va;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = 16 * (j >> 2) + 4 * g + (j & 3);
-        va[j] = __builtin_bit_cast(__bf16, my_slab[key * Geo::kStride + 16 * t + c]);
-      }
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, acc[t], 0, 0, 0);
-    }
+    for (int t = 0; t < Geo::kDimTiles; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(tr + 16 * t), pb, acc[t], 0, 0, 0);
+
+    if (more) id_next = clamp_id(raw_next);
   }
 
   // Normalise and store: lane holds O[head c][dims 16t + 4g .. +3].
@@ -206,36 +238,45 @@ __global__ void __launch_bounds__(64 * kWaves)
   if (head_ok) {
 #pragma unroll
     for (int t = 0; t < Geo::kDimTiles; ++t) {
-      const __bf16 o0 = static_cast<__bf16>(acc[t][0] * inv), o1 = static_cast<__bf16>(acc[t][1] * inv);
-      const __bf16 o2 = static_cast<__bf16>(acc[t][2] * inv), o3 = static_cast<__bf16>(acc[t][3] * inv);
-      const uint32_t lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o0)) |
-                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o1)) << 16);
-      const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o2)) |
-                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, o3)) << 16);
-      *reinterpret_cast<u32x2*>(out_row + 16 * t + 4 * g) = u32x2{lo, hi};
+      bf16x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(acc[t][r] * inv);
+      *reinterpret_cast<u32x2*>(out_row + 16 * t + 4 * g) = __builtin_bit_cast(u32x2, o);
     }
   }
 }
 
-template <int D>
+template <int D, bool kNarrow>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const int64_t n_units = a.B * a.S_q * a.Hkv;
   const int64_t blocks = (n_units + kWaves - 1) / kWaves;
   const float scale_log2e = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((gather_attention_kernel<D>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0,
-                     stream, a.q, a.k, a.v, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0],
+  hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves),
+                     0, stream, a.q, a.k, a.v, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0],
                      a.vs[1], a.vs[2], a.route_list, a.route_count, a.S_q, a.S_kv, a.Hq, a.Hkv, a.K,
                      static_cast<int>(a.Hq / a.Hkv), scale_log2e, n_units, a.out);
   return hipGetLastError();
+}
+
+// True when (S_kv - 1) * row stride + one row fits in 32 bits for both K and V.
+bool narrow_offsets(const AttnArgs& a) {
+  const int64_t lim = (int64_t{1} << 32) - 1;
+  if (a.ks[1] < 0 || a.vs[1] < 0) return false;
+  return (a.S_kv - 1) * a.ks[1] * 2 + 2 * a.D <= lim && (a.S_kv - 1) * a.vs[1] * 2 + 2 * a.D <= lim;
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
+  return narrow_offsets(a) ? launch<D, true>(a, stream) : launch<D, false>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gather_attention(const AttnArgs& a, hipStream_t stream) {
   switch (a.D) {
-    case 64: return launch<64>(a, stream);
-    case 128: return launch<128>(a, stream);
-    case 256: return launch<256>(a, stream);
+    case 64: return launch_d<64>(a, stream);
+    case 128: return launch_d<128>(a, stream);
+    case 256: return launch_d<256>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

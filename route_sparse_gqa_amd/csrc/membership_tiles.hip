@@ -6,13 +6,17 @@
 // 1 partial, 2 full); flex_qsa page, `_membership_flat_offset` (table
 // offsets must be 64-bit once B*S_q*kv_length passes 2^31).
 //
-// Design: one workgroup owns one 128-row tile row of one batch and one
-// segment of up to 65536 columns.  For each of its rows it scatters the
-// row's list into an LDS bitmap of the segment (atomic OR, integer only),
-// expands the bitmap to bytes with 16-byte stores (every byte of the row,
-// padding included, is written exactly once) and adds each 128-column
-// tile's popcount to a register counter owned by the thread that handles
-// that tile.  Counts are integers, so the classes are deterministic.
+// Design: one workgroup owns 16 rows of one 128-row tile row of one batch and
+// one segment of up to 65536 columns; each of its four wavefronts owns one
+// row at a time with a private LDS bitmap of the segment.  Per row the wave
+// scatters the row's list into the bitmap (atomic OR, integer only), expands
+// it to bytes with 16-byte stores (every byte of the row, padding included,
+// is written exactly once) and adds each 128-column tile's popcount to a
+// register counter of the lane that owns the tile.  The workgroup sums its
+// waves' counters in LDS and adds them to the tile's member count with one
+// integer atomic per tile (the count buffer is the tile_class output, zeroed
+// beforehand); a final pass turns counts into classes.  Integer sums make
+// the classes deterministic.
 #include <hip/hip_runtime.h>
 
 #include "qsa_internal.h"
@@ -21,23 +25,33 @@ namespace qsa {
 namespace {
 
 constexpr int kTile = 128;
-constexpr int kSegCols = 65536;            // columns per workgroup segment
-constexpr int kSegWords = kSegCols / 32;   // bitmap words
+constexpr int kSegCols = 65536;              // columns per workgroup segment
 constexpr int kSegTiles = kSegCols / kTile;  // 512 tiles per segment
-constexpr int kThreads = 256;
-constexpr int kTilesPerThread = kSegTiles / kThreads;  // 2
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGroupRows = 16;                   // rows per workgroup
+constexpr int kGroups = kTile / kGroupRows;      // workgroups per tile row and segment
+constexpr int kTilesPerLane = kSegTiles / 64;  // 8
 
 // Four bits -> four bytes holding 0 or 1 (bit k lands in byte k).
 __device__ __forceinline__ uint32_t spread4(uint32_t nibble) { return (nibble * 0x00204081u) & 0x01010101u; }
 
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __global__ void __launch_bounds__(kThreads)
     membership_tiles_kernel(const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count,
-                            int64_t S_q, int64_t K, int64_t kv_length, int64_t ldm, int64_t n_ti,
-                            int64_t n_tj, int64_t n_seg, uint8_t* __restrict__ membership,
-                            int32_t* __restrict__ tile_class) {
-  __shared__ uint32_t bits[kSegWords];
-  const int t = threadIdx.x;
+                            int64_t S_q, int64_t K, int64_t ldm, int64_t n_ti, int64_t n_tj, int64_t n_seg,
+                            uint8_t* __restrict__ membership, int32_t* __restrict__ tile_count) {
+  __shared__ uint32_t lds[kWaves * (kSegCols / 32) + kSegTiles];  // per-wave bitmaps, then tile counters
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   int64_t blk = blockIdx.x;
+  const int grp = static_cast<int>(blk % kGroups);
+  blk /= kGroups;
   const int64_t seg = blk % n_seg;
   blk /= n_seg;
   const int64_t ti = blk % n_ti;
@@ -45,27 +59,33 @@ __global__ void __launch_bounds__(kThreads)
 
   const int64_t c0 = seg * kSegCols;
   const int seg_cols = static_cast<int>(min(static_cast<int64_t>(kSegCols), ldm - c0));  // multiple of 128
-  const int n_words = seg_cols / 32;
+  const int seg_words = seg_cols / 32;
   const int n_chunks = seg_cols / 16;
   const int n_tiles = seg_cols / kTile;
-  const int64_t r0 = ti * kTile;
-  const int64_t r1 = min(r0 + kTile, S_q);
+  uint32_t* bits = lds + wave * seg_words;
+  int* tile_sum = reinterpret_cast<int*>(lds + kWaves * seg_words);
+  const int64_t r0 = ti * kTile + grp * kGroupRows;
+  const int64_t r1 = min(r0 + kGroupRows, min(ti * kTile + kTile, S_q));
 
-  int members[kTilesPerThread] = {};
-  for (int64_t i = r0; i < r1; ++i) {
+  if (tile_count != nullptr) {
+    for (int t = threadIdx.x; t < n_tiles; t += kThreads) tile_sum[t] = 0;
+  }
+
+  int members[kTilesPerLane] = {};
+  for (int64_t i = r0 + wave; i < r1; i += kWaves) {
     const int64_t row = b * S_q + i;
-    for (int w = t; w < n_words; w += kThreads) bits[w] = 0u;
-    __syncthreads();
+    for (int w = lane; w < seg_words; w += 64) bits[w] = 0u;
+    wave_lds_sync();
     const int n = static_cast<int>(min(max(static_cast<int64_t>(route_count[row]), int64_t{0}), K));
     const int32_t* lst = route_list + row * K;
-    for (int j = t; j < n; j += kThreads) {
-      const int64_t c = static_cast<int64_t>(lst[j]) - c0;
-      if (c >= 0 && c < seg_cols) atomicOr(&bits[c >> 5], 1u << (c & 31));
+    for (int j = lane; j < n; j += 64) {
+      const int64_t col = static_cast<int64_t>(lst[j]) - c0;
+      if (col >= 0 && col < seg_cols) atomicOr(&bits[col >> 5], 1u << (col & 31));
     }
-    __syncthreads();
+    wave_lds_sync();
     if (membership != nullptr) {
       uint8_t* dst = membership + row * ldm + c0;  // 64-bit offset
-      for (int ch = t; ch < n_chunks; ch += kThreads) {
+      for (int ch = lane; ch < n_chunks; ch += 64) {
         const uint32_t h = (bits[ch >> 1] >> ((ch & 1) * 16)) & 0xFFFFu;
         uint4 o;
         o.x = spread4(h & 0xFu);
@@ -75,31 +95,46 @@ __global__ void __launch_bounds__(kThreads)
         *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(ch) * 16) = o;
       }
     }
-    if (tile_class != nullptr) {
+    if (tile_count != nullptr) {
 #pragma unroll
-      for (int u = 0; u < kTilesPerThread; ++u) {
-        const int tj = t + u * kThreads;
+      for (int u = 0; u < kTilesPerLane; ++u) {
+        const int tj = lane + 64 * u;
         if (tj < n_tiles) {
-          const uint32_t* w = bits + tj * 4;
+          const uint32_t* w = bits + 4 * tj;
           members[u] += __popc(w[0]) + __popc(w[1]) + __popc(w[2]) + __popc(w[3]);
         }
       }
     }
-    __syncthreads();
+    wave_lds_sync();  // this row's bitmap reads are done before the next clear
   }
 
-  if (tile_class != nullptr) {
+  if (tile_count != nullptr) {
+    __syncthreads();  // counters zeroed by every thread before any wave adds
 #pragma unroll
-    for (int u = 0; u < kTilesPerThread; ++u) {
-      const int64_t tj = seg * kSegTiles + t + u * kThreads;
-      if (t + u * kThreads < n_tiles && tj < n_tj) {
-        const int64_t cols = min(static_cast<int64_t>(kTile), kv_length - tj * kTile);
-        const int64_t pairs = (r1 - r0) * cols;
-        const int cls = members[u] == 0 ? 0 : (members[u] == pairs ? 2 : 1);
-        tile_class[(b * n_ti + ti) * n_tj + tj] = cls;
-      }
+    for (int u = 0; u < kTilesPerLane; ++u) {
+      const int tj = lane + 64 * u;
+      if (tj < n_tiles && members[u] != 0) atomicAdd(&tile_sum[tj], members[u]);
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < n_tiles; t += kThreads) {
+      const int64_t tj = seg * kSegTiles + t;
+      if (tj < n_tj && tile_sum[t] != 0) atomicAdd(&tile_count[(b * n_ti + ti) * n_tj + tj], tile_sum[t]);
     }
   }
+}
+
+// Member counts -> classes: 0 none, 2 every in-range pair, 1 otherwise.
+__global__ void __launch_bounds__(256)
+    tile_class_kernel(int32_t* __restrict__ tile, int64_t n_tiles, int64_t S_q, int64_t kv_length, int64_t n_ti,
+                      int64_t n_tj) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= n_tiles) return;
+  const int64_t tj = idx % n_tj;
+  const int64_t ti = (idx / n_tj) % n_ti;
+  const int64_t pairs = min(static_cast<int64_t>(kTile), S_q - ti * kTile) *
+                        min(static_cast<int64_t>(kTile), kv_length - tj * kTile);
+  const int32_t m = tile[idx];
+  tile[idx] = m == 0 ? 0 : (m == pairs ? 2 : 1);
 }
 
 }  // namespace
@@ -112,10 +147,16 @@ hipError_t launch_membership_tiles(const int32_t* route_list, const int32_t* rou
   const int64_t n_ti = (S_q + kTile - 1) / kTile;
   const int64_t n_tj = (kv_length + kTile - 1) / kTile;
   const int64_t n_seg = (ldm + kSegCols - 1) / kSegCols;
-  const int64_t blocks = B * n_ti * n_seg;
+  const int64_t blocks = B * n_ti * n_seg * kGroups;
+  // tile_class holds member counts until the final pass; the route-normalise
+  // launch that precedes this one on the stream has zeroed it.
   hipLaunchKernelGGL(membership_tiles_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream,
-                     route_list, route_count, S_q, K, kv_length, ldm, n_ti, n_tj, n_seg, membership,
-                     tile_class);
+                     route_list, route_count, S_q, K, ldm, n_ti, n_tj, n_seg, membership, tile_class);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || tile_class == nullptr) return e;
+  const int64_t n_tiles = B * n_ti * n_tj;
+  hipLaunchKernelGGL(tile_class_kernel, dim3(static_cast<uint32_t>((n_tiles + 255) / 256)), dim3(256), 0, stream,
+                     tile_class, n_tiles, S_q, kv_length, n_ti, n_tj);
   return hipGetLastError();
 }
 

@@ -137,7 +137,7 @@ QSA_EXPORT int qsa_preprocess(const void* routes, int routes_dtype, int64_t B, i
   if (membership != nullptr && !mul_ok(s.rows, ldm, &mem_bytes)) return QSA_ERR_LIMIT;
   if (!mul_ok(B * n_ti, n_tj, &tiles) || tiles > (INT64_MAX >> 3)) return QSA_ERR_LIMIT;
   if ((membership != nullptr || tile_class != nullptr) &&
-      B * n_ti * ((ldm + 65535) / 65536) > kMaxGrid)
+      (B * n_ti * ((ldm + 65535) / 65536) * 8 > kMaxGrid || (tiles + 255) / 256 > kMaxGrid))
     return QSA_ERR_LIMIT;
 
   const int64_t rshape[3] = {B, S_q, K};
@@ -154,7 +154,8 @@ QSA_EXPORT int qsa_preprocess(const void* routes, int routes_dtype, int64_t B, i
   (void)hipGetLastError();  // clear a stale error so the checks below see only ours
   hipStream_t st = as_stream(stream);
   int rc = hip_status(qsa::launch_route_normalize(routes, routes_dtype == QSA_INT64, B, S_q, K, route_strides,
-                                                  kv_length, route_list, route_count, st));
+                                                  kv_length, route_list, route_count, tile_class,
+                                                  tile_class ? tiles : 0, st));
   if (rc != QSA_OK) return rc;
   return hip_status(
       qsa::launch_membership_tiles(route_list, route_count, B, S_q, K, kv_length, membership, tile_class, st));
@@ -243,7 +244,7 @@ QSA_EXPORT int qsa_forward(const void* q, const int64_t q_strides[4], const void
   (void)hipGetLastError();
   hipStream_t st = as_stream(stream);
   int rc = hip_status(qsa::launch_route_normalize(routes, routes_dtype == QSA_INT64, B, S_q, K, route_strides,
-                                                  S_kv, list, count, st));
+                                                  S_kv, list, count, nullptr, 0, st));
   if (rc != QSA_OK) return rc;
   const qsa::AttnArgs a =
       attn_args(q, q_strides, k, k_strides, v, v_strides, list, count, B, S_q, S_kv, Hq, Hkv, D, K, scale, out);

@@ -47,7 +47,8 @@ template <int E, int W, typename RouteT>
 __global__ void __launch_bounds__(64 * W * RowsPerBlock<W>::value)
     route_normalize_kernel(const RouteT* __restrict__ routes, int64_t rs0, int64_t rs1, int64_t rs2,
                            int64_t S_q, int64_t K, int64_t kv_length, int64_t n_rows,
-                           int32_t* __restrict__ route_list, int32_t* __restrict__ route_count) {
+                           int32_t* __restrict__ route_list, int32_t* __restrict__ route_count,
+                           int32_t* __restrict__ zero_buf, int64_t zero_count) {
   constexpr int T = 64 * W;
   constexpr int ROWS = RowsPerBlock<W>::value;
   constexpr int P = T * E;
@@ -160,44 +161,52 @@ __global__ void __launch_bounds__(64 * W * RowsPerBlock<W>::value)
     }
     if (t == 0) route_count[row] = total;
   }
+  if (zero_buf != nullptr) {  // side job: clear the tile member counters (grid-stride)
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t z = static_cast<int64_t>(blockIdx.x) * blockDim.x + tid; z < zero_count; z += stride)
+      zero_buf[z] = 0;
+  }
 }
 
 template <int E, int W, typename RouteT>
 hipError_t launch_sorted(const RouteT* routes, const int64_t* st, int64_t B, int64_t S_q, int64_t K,
-                         int64_t kv_length, int32_t* list, int32_t* count, hipStream_t stream) {
+                         int64_t kv_length, int32_t* list, int32_t* count, int32_t* zb, int64_t zn,
+                         hipStream_t stream) {
   constexpr int ROWS = RowsPerBlock<W>::value;
   const int64_t n_rows = B * S_q;
   const int64_t blocks = (n_rows + ROWS - 1) / ROWS;
   hipLaunchKernelGGL((route_normalize_kernel<E, W, RouteT>), dim3(static_cast<uint32_t>(blocks)),
                      dim3(64 * W * ROWS), 0, stream, routes, st[0], st[1], st[2], S_q, K, kv_length,
-                     n_rows, list, count);
+                     n_rows, list, count, zb, zn);
   return hipGetLastError();
 }
 
 template <typename RouteT>
 hipError_t dispatch(const RouteT* routes, const int64_t* st, int64_t B, int64_t S_q, int64_t K,
-                    int64_t kv_length, int32_t* list, int32_t* count, hipStream_t stream) {
-  if (K <= 64) return launch_sorted<1, 1>(routes, st, B, S_q, K, kv_length, list, count, stream);
-  if (K <= 128) return launch_sorted<2, 1>(routes, st, B, S_q, K, kv_length, list, count, stream);
-  if (K <= 256) return launch_sorted<4, 1>(routes, st, B, S_q, K, kv_length, list, count, stream);
-  if (K <= 512) return launch_sorted<8, 1>(routes, st, B, S_q, K, kv_length, list, count, stream);
-  if (K <= 1024) return launch_sorted<8, 2>(routes, st, B, S_q, K, kv_length, list, count, stream);
-  if (K <= 2048) return launch_sorted<8, 4>(routes, st, B, S_q, K, kv_length, list, count, stream);
-  if (K <= 4096) return launch_sorted<8, 8>(routes, st, B, S_q, K, kv_length, list, count, stream);
-  if (K <= 8192) return launch_sorted<8, 16>(routes, st, B, S_q, K, kv_length, list, count, stream);
-  return launch_sorted<16, 16>(routes, st, B, S_q, K, kv_length, list, count, stream);
+                    int64_t kv_length, int32_t* list, int32_t* count, int32_t* zb, int64_t zn,
+                    hipStream_t stream) {
+  if (K <= 64) return launch_sorted<1, 1>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
+  if (K <= 128) return launch_sorted<2, 1>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
+  if (K <= 256) return launch_sorted<4, 1>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
+  if (K <= 512) return launch_sorted<8, 1>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
+  if (K <= 1024) return launch_sorted<8, 2>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
+  if (K <= 2048) return launch_sorted<8, 4>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
+  if (K <= 4096) return launch_sorted<8, 8>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
+  if (K <= 8192) return launch_sorted<8, 16>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
+  return launch_sorted<16, 16>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
 }
 
 }  // namespace
 
 hipError_t launch_route_normalize(const void* routes, bool routes_int64, int64_t B, int64_t S_q,
                                   int64_t K, const int64_t route_strides[3], int64_t kv_length,
-                                  int32_t* route_list, int32_t* route_count, hipStream_t stream) {
+                                  int32_t* route_list, int32_t* route_count, int32_t* zero_buf,
+                                  int64_t zero_count, hipStream_t stream) {
   if (routes_int64)
     return dispatch(static_cast<const int64_t*>(routes), route_strides, B, S_q, K, kv_length, route_list,
-                    route_count, stream);
+                    route_count, zero_buf, zero_count, stream);
   return dispatch(static_cast<const int32_t*>(routes), route_strides, B, S_q, K, kv_length, route_list,
-                  route_count, stream);
+                  route_count, zero_buf, zero_count, stream);
 }
 
 }  // namespace qsa

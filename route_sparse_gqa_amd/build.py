@@ -22,7 +22,12 @@ BUILD_DIR = os.path.join(ROOT, "_build", "libqsa")
 LIB_PATH = os.path.join(PKG, "libqsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["route_normalize.hip", "membership_tiles.hip", "gather_attention.hip", "qsa_api.cpp"]
+SOURCES = [
+    "route_normalize.hip",
+    "membership_tiles.hip",
+    "gather_attention.hip",
+    "qsa_api.cpp",
+]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

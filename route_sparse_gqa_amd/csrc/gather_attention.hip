@@ -6,7 +6,8 @@
 // qsa page, `_gathered_qsa_gqa_attention_chunk` (grouped layout
 // [B, Q, Hkv, G, D]: query head h reads KV head h / G).
 //
-// Design (one wavefront per (b, i, hk) work unit, four per workgroup):
+// Design (one wavefront per (b, i, hk) work unit, four rows of one KV head
+// per workgroup, mapped so that each XCD serves one KV head):
 //  * The G query heads of the unit are the N = 16 columns of the MFMA (zero
 //    padded when G < 16).  Scores are computed transposed, S^T = K Q^T with
 //    v_mfma_f32_16x16x32_bf16, 16 routed keys as the M rows: the gathered K
@@ -103,10 +104,14 @@ __global__ void __launch_bounds__(64 * kWaves)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));  // wave-uniform
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  if (unit >= n_units) return;  // no workgroup barriers in this kernel
-  const int64_t hk = unit % Hkv;
-  const int64_t row = unit / Hkv;  // b * S_q + i
+  // Workgroup x -> (KV head x % Hkv, rows 4 (x / Hkv) ..): workgroups are
+  // dealt round-robin to the 8 XCDs, so when Hkv divides 8 each XCD serves a
+  // single KV head (half the K/V working set per L2 at Hkv = 2), while rows
+  // still spread evenly over the XCDs.
+  const int64_t x = blockIdx.x;
+  const int64_t hk = x % Hkv;
+  const int64_t row = (x / Hkv) * kWaves + wave;  // b * S_q + i
+  if (row >= n_units / Hkv) return;  // no workgroup barriers in this kernel
   const int64_t b = row / S_q;
   const int64_t i = row % S_q;
   const int c = lane & 15;  // head column of this lane; also key/dim row within a 16-tile
@@ -249,7 +254,7 @@ __global__ void __launch_bounds__(64 * kWaves)
 template <int D, bool kNarrow>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const int64_t n_units = a.B * a.S_q * a.Hkv;
-  const int64_t blocks = (n_units + kWaves - 1) / kWaves;
+  const int64_t blocks = (a.B * a.S_q + kWaves - 1) / kWaves * a.Hkv;
   const float scale_log2e = a.scale * 1.4426950408889634f;
   hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves),
                      0, stream, a.q, a.k, a.v, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0],

@@ -182,7 +182,7 @@ int check_attention(const void* q, const int64_t q_strides[4], const void* k, co
   if (int st = check_bf16_tensor(v, v_strides)) return st;
   if (!aligned(out, 16)) return QSA_ERR_LAYOUT;
   int64_t units = 0, out_elems = 0;
-  if (!mul_ok(s->rows, Hkv, &units) || (units + 3) / 4 > kMaxGrid) return QSA_ERR_LIMIT;
+  if (!mul_ok(s->rows, Hkv, &units) || (s->rows + 3) / 4 * Hkv > kMaxGrid) return QSA_ERR_LIMIT;
   if (!mul_ok(s->rows, Hq * D, &out_elems) || out_elems > (INT64_MAX >> 2)) return QSA_ERR_LIMIT;
   const int64_t qshape[4] = {B, S_q, Hq, D}, kshape[4] = {B, S_kv, Hkv, D};
   *r_q = extent(q, qshape, q_strides, 4, 2);

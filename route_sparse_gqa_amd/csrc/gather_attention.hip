@@ -10,18 +10,20 @@
 // per workgroup, mapped so that each XCD serves one KV head):
 //  * The G query heads of the unit are the N = 16 columns of the MFMA (zero
 //    padded when G < 16).  Scores are computed transposed, S^T = K Q^T with
-//    v_mfma_f32_16x16x32_bf16, 16 routed keys as the M rows: the gathered K
-//    rows load straight into the A operand (lane (c, g) = (lane % 16,
-//    lane / 16) loads 16 bytes = 8 dims of key c, so one load instruction
-//    gathers 16 keys x 64 contiguous bytes), and each lane ends up owning one
-//    head and four keys.  Row max/sum reductions are two cross-lane xors.
+//    v_mfma_f32_16x16x32_bf16, 16 routed keys as the M rows, so each lane
+//    ends up owning one head and four keys; row max/sum reductions are two
+//    cross-lane xors.  Routed K and V rows are both gathered two full rows
+//    per 16-byte-per-lane load instruction (fewest cache lines per
+//    instruction for the address unit) and staged in this wave's LDS slabs;
+//    the K slab's 2D + 16 byte stride makes the A-operand reads (lane
+//    (c, g) = (lane % 16, lane / 16) reads dims 32s + 8g .. +7 of key c)
+//    conflict-free.
 //  * PV is computed transposed too, O^T = V^T P^T with
 //    v_mfma_f32_16x16x16_bf16: the four probabilities of a lane are exactly
 //    its B operand (no shuffle) and the online-softmax rescale is
-//    lane-local.  The V^T operand needs 4 keys of one dim per lane: the 16
-//    routed V rows of a chunk are gathered with coalesced 16-byte loads, put
-//    in this wave's LDS slab and read back with one gfx950 transposing LDS
-//    load per 16-dim tile.
+//    lane-local.  The V^T operand needs 4 keys of one dim per lane: it is
+//    read from the V slab with one gfx950 transposing LDS load per 16-dim
+//    tile.
 //  * Software pipeline: while chunk c is computed, the K and V rows of chunk
 //    c + 1 (in registers) and the route IDs of chunk c + 2 are in flight.
 //    The IDs are issued before the rows and used one iteration later, so the
@@ -57,7 +59,8 @@ struct Geometry {
   static constexpr int kLanesPerRow = D / 8;            // 16-byte pieces per V row
   static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   static constexpr int kLoads = kChunk / kRowsPerLoad;  // V load instructions per chunk
-  static constexpr int kStride = D + 16;                // LDS row stride in bf16 (2D + 32 bytes)
+  static constexpr int kStride = D + 16;                // V slab row stride in bf16 (2D + 32 bytes)
+  static constexpr int kKStride = D + 8;                // K slab row stride in bf16 (2D + 16 bytes)
 };
 
 __device__ __forceinline__ u32x4 load16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -101,6 +104,7 @@ __global__ void __launch_bounds__(64 * kWaves)
                             float scale_log2e, int64_t n_units, uint16_t* __restrict__ out) {
   using Geo = Geometry<D>;
   __shared__ __attribute__((aligned(16))) uint16_t slab[kWaves][kChunk * Geo::kStride];
+  __shared__ __attribute__((aligned(16))) uint16_t kslab[kWaves][kChunk * Geo::kKStride];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));  // wave-uniform
@@ -147,18 +151,24 @@ __global__ void __launch_bounds__(64 * kWaves)
 
   const int32_t* lst = route_list + row * K;
   const int64_t ks1b = 2 * ks1, vs1b = 2 * vs1;  // row strides in bytes
-  const char* kb = reinterpret_cast<const char*>(k + b * ks0 + hk * ks2) + 16 * g;
+  const char* kb = reinterpret_cast<const char*>(k + b * ks0 + hk * ks2) + 16 * (lane % Geo::kLanesPerRow);
   const char* vb = reinterpret_cast<const char*>(v + b * vs0 + hk * vs2) + 16 * (lane % Geo::kLanesPerRow);
   uint16_t* my_slab = slab[wave];
+  uint16_t* my_kslab = kslab[wave];
   const int32_t id_max = static_cast<int32_t>(S_kv - 1);
   auto clamp_id = [&](int32_t x) { return min(max(x, 0), id_max); };
   // Raw route ID of key base + c (tails repeat the last route; clamped later).
   auto load_id = [&](int base) { return lst[min(base + c, n - 1)]; };
-  // K rows of the chunk straight into the A operand of S^T = K Q^T.
-  auto load_k = [&](int32_t id, bf16x8* kf) {
-    const char* kp = kb + RowOffset<kNarrow>::of(id, ks1b);
+  // K rows of the chunk in 16-byte pieces, two full rows per load
+  // instruction (the pattern the address unit handles best); they reach the
+  // A operand of S^T = K Q^T through this wave's K slab.  Row r's ID lives in
+  // lane r.
+  auto load_k = [&](int32_t id, u32x4* kr) {
 #pragma unroll
-    for (int s = 0; s < Geo::kSteps; ++s) kf[s] = __builtin_bit_cast(bf16x8, load16(kp + 64 * s));
+    for (int u = 0; u < Geo::kLoads; ++u) {
+      const int32_t idr = __shfl(id, u * Geo::kRowsPerLoad + lane / Geo::kLanesPerRow);
+      kr[u] = load16(kb + RowOffset<kNarrow>::of(idr, ks1b));
+    }
   };
   // V rows of the chunk in 16-byte pieces; row r's ID lives in lane r.
   auto load_v = [&](int32_t id, u32x4* vr) {
@@ -169,12 +179,12 @@ __global__ void __launch_bounds__(64 * kWaves)
     }
   };
 
-  bf16x8 kf[Geo::kSteps];
+  u32x4 kr[Geo::kLoads];
   u32x4 vr[Geo::kLoads];
   int32_t raw_next = load_id(kChunk);  // issued first: used after the rows below
   {
     const int32_t id0 = clamp_id(load_id(0));
-    load_k(id0, kf);
+    load_k(id0, kr);
     load_v(id0, vr);
   }
   int32_t id_next = clamp_id(raw_next);
@@ -183,23 +193,30 @@ __global__ void __launch_bounds__(64 * kWaves)
   for (int base = 0; base < n; base += kChunk) {
     const bool more = base + kChunk < n;  // wave-uniform
 
-    // Stage this chunk's V rows in LDS (row-major, padded stride).
-    wave_lds_sync();  // previous chunk's transposed reads are complete
+    // Stage this chunk's K and V rows in LDS (row-major, padded strides).
+    wave_lds_sync();  // previous chunk's reads of both slabs are complete
 #pragma unroll
     for (int u = 0; u < Geo::kLoads; ++u) {
       const int r = u * Geo::kRowsPerLoad + lane / Geo::kLanesPerRow;
-      *reinterpret_cast<u32x4*>(my_slab + r * Geo::kStride + 8 * (lane % Geo::kLanesPerRow)) = vr[u];
+      const int col = 8 * (lane % Geo::kLanesPerRow);
+      *reinterpret_cast<u32x4*>(my_kslab + r * Geo::kKStride + col) = kr[u];
+      *reinterpret_cast<u32x4*>(my_slab + r * Geo::kStride + col) = vr[u];
     }
+    wave_lds_sync();  // K and V rows visible to every lane of this wave
 
-    // Scores: lane holds S^T[key 4g + r][head c].
+    // Scores: lane holds S^T[key 4g + r][head c]; the A operand is key c,
+    // dims 32s + 8g .. +7 (row stride 2D + 16 bytes: conflict-free).
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* ka = my_kslab + c * Geo::kKStride + 8 * g;
 #pragma unroll
-    for (int s = 0; s < Geo::kSteps; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], st, 0, 0, 0);
+    for (int s = 0; s < Geo::kSteps; ++s)
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ka + 32 * s)),
+                                                  qf[s], st, 0, 0, 0);
 
     // Prefetch: IDs two chunks ahead first, then the next chunk's K and V rows.
     if (more) {
       raw_next = load_id(base + 2 * kChunk);
-      load_k(id_next, kf);
+      load_k(id_next, kr);
       load_v(id_next, vr);
     }
 
@@ -228,7 +245,6 @@ __global__ void __launch_bounds__(64 * kWaves)
 
     // O^T += V^T P^T: one transposed LDS read gives lane (c, g) keys 4g..4g+3
     // of dim 16t + c, matching its four probabilities.
-    wave_lds_sync();  // V rows visible to every lane of this wave
 #pragma unroll
     for (int t = 0; t < Geo::kDimTiles; ++t)
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(tr + 16 * t), pb, acc[t], 0, 0, 0);

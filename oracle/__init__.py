@@ -12,6 +12,9 @@ their ``uint16`` bit patterns):
 * ``membership(routes, kv_length)``       -> uint8 [B,S_q,round_up(kv_length,128)]
 * ``tile_class(routes, kv_length)``       -> int32 [B,ceil(S_q/128),ceil(kv_length/128)]
 * ``forward(q, k, v, routes, scale, rows=None)`` -> float64 [B,rows,Hq,D]
+* ``lse(q, k, routes, scale, rows=None)`` -> float64 [B,rows,Hq] (natural log; -inf for empty rows)
+* ``backward(q, k, v, dout, routes, scale, rows=None, keys=None)``
+  -> (dq [B,rows,Hq,D], dk [B,keys,Hkv,D], dv [B,keys,Hkv,D]) float64
 
 See ``qsa_oracle.c`` for the definitions and the passages they follow.
 """
@@ -55,7 +58,11 @@ class Oracle:
         lib.oracle_tile_class.argtypes = [p, i64, i64, i64, i64, p]
         lib.oracle_forward.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i64,
                                        ctypes.c_double, i64, i64, p]
-        for f in (lib.oracle_route_lists, lib.oracle_membership, lib.oracle_tile_class, lib.oracle_forward):
+        lib.oracle_lse.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double, i64, i64, p]
+        lib.oracle_backward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64,
+                                        ctypes.c_double, i64, i64, i64, i64, p, p, p]
+        for f in (lib.oracle_route_lists, lib.oracle_membership, lib.oracle_tile_class, lib.oracle_forward,
+                  lib.oracle_lse, lib.oracle_backward):
             f.restype = None
         self.lib = lib
 
@@ -103,6 +110,46 @@ class Oracle:
                                 float(scale), r0, r1, _ptr(out))
         return out
 
+    def lse(self, q, k, routes, scale, rows=None):
+        q, k = _bf16_bits(q=q, k=k)
+        r = _routes64(routes)
+        B, S_q, Hq, D = q.shape
+        _, S_kv, Hkv, _ = k.shape
+        if Hkv < 1 or Hq % Hkv != 0:
+            raise ValueError("Hq must be a positive multiple of Hkv")
+        r0, r1 = (0, S_q) if rows is None else (int(rows[0]), int(rows[1]))
+        out = np.empty((B, r1 - r0, Hq), dtype=np.float64)
+        self.lib.oracle_lse(_ptr(q), _ptr(k), _ptr(r), B, S_q, S_kv, Hq, Hkv, D, r.shape[2], float(scale),
+                            r0, r1, _ptr(out))
+        return out
+
+    def backward(self, q, k, v, dout, routes, scale, rows=None, keys=None):
+        q, k, v, dout = _bf16_bits(q=q, k=k, v=v, dout=dout)
+        r = _routes64(routes)
+        B, S_q, Hq, D = q.shape
+        _, S_kv, Hkv, _ = k.shape
+        if Hkv < 1 or Hq % Hkv != 0:
+            raise ValueError("Hq must be a positive multiple of Hkv")
+        if dout.shape != q.shape:
+            raise ValueError("dout must have the shape of q")
+        r0, r1 = (0, S_q) if rows is None else (int(rows[0]), int(rows[1]))
+        k0, k1 = (0, S_kv) if keys is None else (int(keys[0]), int(keys[1]))
+        dq = np.empty((B, r1 - r0, Hq, D), dtype=np.float64)
+        dk = np.empty((B, k1 - k0, Hkv, D), dtype=np.float64)
+        dv = np.empty((B, k1 - k0, Hkv, D), dtype=np.float64)
+        self.lib.oracle_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(r), B, S_q, S_kv, Hq, Hkv, D,
+                                 r.shape[2], float(scale), r0, r1, k0, k1, _ptr(dq), _ptr(dk), _ptr(dv))
+        return dq, dk, dv
+
+
+def _bf16_bits(**tensors):
+    out = []
+    for name, t in tensors.items():
+        if t.dtype != np.uint16:
+            raise TypeError(f"{name} must hold bfloat16 bits as uint16")
+        out.append(np.ascontiguousarray(t))
+    return out
+
 
 def _load() -> Oracle:
     global _lib
@@ -148,3 +195,15 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, routes: np.ndarray, sca
             rows: tuple[int, int] | None = None) -> np.ndarray:
     """fp64 attention output [B, rows, Hq, D] for query rows ``rows`` (default: all)."""
     return _load().forward(q, k, v, routes, scale, rows)
+
+
+def lse(q: np.ndarray, k: np.ndarray, routes: np.ndarray, scale: float,
+        rows: tuple[int, int] | None = None) -> np.ndarray:
+    """fp64 natural-log log-sum-exp of the scaled scores, [B, rows, Hq]; -inf for empty rows."""
+    return _load().lse(q, k, routes, scale, rows)
+
+
+def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, routes: np.ndarray, scale: float,
+             rows: tuple[int, int] | None = None, keys: tuple[int, int] | None = None):
+    """fp64 (dq [B,rows,Hq,D], dk [B,keys,Hkv,D], dv [B,keys,Hkv,D]) for upstream gradient ``dout``."""
+    return _load().backward(q, k, v, dout, routes, scale, rows, keys)

@@ -30,6 +30,10 @@
  *    s_j = scale * <q[b,i,h,:], k[b,j,hk,:]>, o = sum_j softmax(s)_j v[b,j,hk,:];
  *    an empty R gives exactly zero; no causal or other mask is added.
  *    All arithmetic is fp64 on the exact bfloat16 input values.
+ *  - Log-sum-exp of each row's scaled scores and the first-order gradients
+ *    dq, dk, dv of that attention (fa4_qsa page: FA4 owns first-order
+ *    autograd; empty rows have zero output and zero gradients): the softmax
+ *    Jacobian written out per (row, head), see `oracle_backward`.
  *
  * Rows are independent, so each entry point runs its outer row loop under
  * OpenMP; that changes no per-row arithmetic.
@@ -185,5 +189,141 @@ void oracle_forward(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
         }
         free(set);
         free(score);
+    }
+}
+
+/*
+ * lse [B, row_end - row_begin, Hq] fp64: natural-log log-sum-exp of the
+ * scaled scores of each (query row, head), log sum_j exp(s_j) over j in
+ * R(b,i); -inf for an empty route set.  This is the per-row statistic a
+ * forward pass keeps for its backward (fa4_qsa page: the FA4 kernel owns
+ * first-order autograd).
+ */
+void oracle_lse(const uint16_t *q, const uint16_t *k, const int64_t *routes, int64_t B, int64_t S_q,
+                int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K, double scale, int64_t row_begin,
+                int64_t row_end, double *lse) {
+    const int64_t G = Hq / Hkv;
+    const int64_t n_rows = row_end - row_begin;
+#pragma omp parallel
+    {
+        int64_t *set = (int64_t *)malloc((size_t)K * sizeof(int64_t));
+        double *score = (double *)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(dynamic, 4) collapse(2)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t i = row_begin; i < row_end; ++i) {
+                int64_t n = route_set(routes + (b * S_q + i) * K, K, S_kv, set);
+                for (int64_t h = 0; h < Hq; ++h) {
+                    int64_t hk = h / G;
+                    const uint16_t *qv = q + ((b * S_q + i) * Hq + h) * D;
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < n; ++j) {
+                        const uint16_t *kv = k + ((b * S_kv + set[j]) * Hkv + hk) * D;
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d) dot += bf16_to_double(qv[d]) * bf16_to_double(kv[d]);
+                        score[j] = scale * dot;
+                        if (score[j] > m) m = score[j];
+                    }
+                    double sum = 0.0;
+                    for (int64_t j = 0; j < n; ++j) sum += exp(score[j] - m);
+                    lse[(b * n_rows + (i - row_begin)) * Hq + h] = n == 0 ? -INFINITY : m + log(sum);
+                }
+            }
+        }
+        free(set);
+        free(score);
+    }
+}
+
+/*
+ * Gradients of the attention above for an upstream gradient dout
+ * [B,S_q,Hq,D] (bfloat16 bits), i.e. of L = sum dout * out (fa4_qsa page:
+ * first-order autograd; flex_qsa page, module description, and fa4_qsa
+ * page, `fa4_sparse_gqa_attention`: rows whose routes are all invalid have
+ * zero output and zero gradients).  For a (b, i, h) with non-empty R:
+ *
+ *   p_j   = softmax(s)_j                       (s_j as in the forward)
+ *   dp_j  = <dout[b,i,h,:], v[b,j,hk,:]>
+ *   ds_j  = p_j * (dp_j - sum_l p_l dp_l)      (softmax Jacobian)
+ *   dq[b,i,h,:]   = scale * sum_j ds_j k[b,j,hk,:]
+ *   dk[b,j,hk,:] += scale * ds_j q[b,i,h,:]     over every (i, h) routing j
+ *   dv[b,j,hk,:] += p_j dout[b,i,h,:]           over every (i, h) routing j
+ *
+ * dq is produced for query rows [row_begin, row_end) as [B, rows, Hq, D];
+ * dk and dv for keys [key_begin, key_end) as [B, keys, Hkv, D], summed over
+ * all query rows.  Keys that no row routes get zero.  Rows run in parallel;
+ * the dk/dv sums use atomic adds (fp64, so the summation order does not
+ * matter at the tolerances used).
+ */
+void oracle_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                     const int64_t *routes, int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv,
+                     int64_t D, int64_t K, double scale, int64_t row_begin, int64_t row_end, int64_t key_begin,
+                     int64_t key_end, double *dq, double *dk, double *dv) {
+    const int64_t G = Hq / Hkv;
+    const int64_t n_rows = row_end - row_begin, n_keys = key_end - key_begin;
+    for (int64_t x = 0; x < B * n_rows * Hq * D; ++x) dq[x] = 0.0;
+    for (int64_t x = 0; x < B * n_keys * Hkv * D; ++x) dk[x] = dv[x] = 0.0;
+#pragma omp parallel
+    {
+        int64_t *set = (int64_t *)malloc((size_t)K * sizeof(int64_t));
+        double *p = (double *)malloc((size_t)K * sizeof(double));
+        double *dp = (double *)malloc((size_t)K * sizeof(double));
+#pragma omp for schedule(dynamic, 4) collapse(2)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t i = 0; i < S_q; ++i) {
+                int64_t n = route_set(routes + (b * S_q + i) * K, K, S_kv, set);
+                int want_dq = i >= row_begin && i < row_end;
+                int touches = 0;
+                for (int64_t j = 0; j < n; ++j) touches |= set[j] >= key_begin && set[j] < key_end;
+                if (n == 0 || (!want_dq && !touches)) continue; /* empty rows: zero gradients */
+                for (int64_t h = 0; h < Hq; ++h) {
+                    int64_t hk = h / G;
+                    const uint16_t *qv = q + ((b * S_q + i) * Hq + h) * D;
+                    const uint16_t *gv = dout + ((b * S_q + i) * Hq + h) * D;
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < n; ++j) {
+                        const uint16_t *kv = k + ((b * S_kv + set[j]) * Hkv + hk) * D;
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d) dot += bf16_to_double(qv[d]) * bf16_to_double(kv[d]);
+                        p[j] = scale * dot;
+                        if (p[j] > m) m = p[j];
+                    }
+                    double denom = 0.0;
+                    for (int64_t j = 0; j < n; ++j) {
+                        p[j] = exp(p[j] - m);
+                        denom += p[j];
+                    }
+                    double pdp = 0.0;
+                    for (int64_t j = 0; j < n; ++j) {
+                        p[j] /= denom;
+                        const uint16_t *vv = v + ((b * S_kv + set[j]) * Hkv + hk) * D;
+                        double dot = 0.0;
+                        for (int64_t d = 0; d < D; ++d) dot += bf16_to_double(gv[d]) * bf16_to_double(vv[d]);
+                        dp[j] = dot;
+                        pdp += p[j] * dp[j];
+                    }
+                    for (int64_t j = 0; j < n; ++j) {
+                        double ds = p[j] * (dp[j] - pdp);
+                        const uint16_t *kv = k + ((b * S_kv + set[j]) * Hkv + hk) * D;
+                        if (want_dq) {
+                            double *o = dq + ((b * n_rows + (i - row_begin)) * Hq + h) * D;
+                            for (int64_t d = 0; d < D; ++d) o[d] += scale * ds * bf16_to_double(kv[d]);
+                        }
+                        if (set[j] >= key_begin && set[j] < key_end) {
+                            double *gk = dk + ((b * n_keys + (set[j] - key_begin)) * Hkv + hk) * D;
+                            double *gw = dv + ((b * n_keys + (set[j] - key_begin)) * Hkv + hk) * D;
+                            for (int64_t d = 0; d < D; ++d) {
+#pragma omp atomic
+                                gk[d] += scale * ds * bf16_to_double(qv[d]);
+#pragma omp atomic
+                                gw[d] += p[j] * bf16_to_double(gv[d]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(set);
+        free(p);
+        free(dp);
     }
 }

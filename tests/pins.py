@@ -8,7 +8,9 @@ oracle's per-row gather loop:
 * ``brute_membership``  - dense boolean table filled from those sets.
 * ``block_classes``     - numpy block reduction of a membership table.
 * ``dense_attention``   - dense [S_q, S_kv] fp64 scores, -inf outside the
-                          membership table, textbook softmax.
+                          membership table, textbook softmax (also on
+                          float64 arrays: ``dense_attention_f64``).
+* ``dense_lse``         - per-row log-sum-exp over the dense masked scores.
 """
 
 from __future__ import annotations
@@ -61,13 +63,11 @@ def block_classes(member: np.ndarray, kv_length: int, tile: int = 128) -> np.nda
     return np.where(sums == 0, 0, np.where(sums == size, 2, 1)).astype(np.int32)
 
 
-def dense_attention(q_bits, k_bits, v_bits, routes, scale: float) -> np.ndarray:
-    """Dense masked-softmax attention in fp64; empty rows give zeros."""
-    q, k, v = bf16_to_f64(q_bits), bf16_to_f64(k_bits), bf16_to_f64(v_bits)
+def dense_attention_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray, scale: float) -> np.ndarray:
+    """Dense masked-softmax attention on float64 arrays; ``mask`` [B,S_q,S_kv] bool; empty rows give zeros."""
     B, S_q, Hq, D = q.shape
-    S_kv, Hkv = k.shape[1], k.shape[2]
+    Hkv = k.shape[2]
     G = Hq // Hkv
-    mask = brute_membership(routes, S_kv).astype(bool)
     out = np.zeros((B, S_q, Hq, D), dtype=np.float64)
     for b in range(B):
         for h in range(Hq):
@@ -80,4 +80,30 @@ def dense_attention(q_bits, k_bits, v_bits, routes, scale: float) -> np.ndarray:
             den = w.sum(axis=1)
             o = (w @ vv) / np.where(has, den, 1.0)[:, None]
             out[b, :, h, :] = np.where(has[:, None], o, 0.0)
+    return out
+
+
+def dense_attention(q_bits, k_bits, v_bits, routes, scale: float) -> np.ndarray:
+    """Dense masked-softmax attention in fp64 on bfloat16 bit inputs; empty rows give zeros."""
+    S_kv = k_bits.shape[1]
+    mask = brute_membership(routes, S_kv).astype(bool)
+    return dense_attention_f64(bf16_to_f64(q_bits), bf16_to_f64(k_bits), bf16_to_f64(v_bits), mask, scale)
+
+
+def dense_lse(q_bits, k_bits, routes, scale: float) -> np.ndarray:
+    """log sum_j exp(s_j) over the membership table, [B,S_q,Hq]; -inf for empty rows."""
+    q, k = bf16_to_f64(q_bits), bf16_to_f64(k_bits)
+    B, S_q, Hq, D = q.shape
+    S_kv, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    mask = brute_membership(routes, S_kv).astype(bool)
+    out = np.full((B, S_q, Hq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            s = scale * (q[b, :, h, :] @ k[b, :, h // G, :].T)
+            for i in range(S_q):
+                if mask[b, i].any():
+                    x = s[i][mask[b, i]]
+                    mx = x.max()
+                    out[b, i, h] = mx + np.log(np.exp(x - mx).sum())
     return out

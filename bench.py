@@ -99,7 +99,7 @@ class Plan:
                          w.S_kv, i8(self.lst), i8(self.cnt), i8(self.mem), i8(self.tc), self.stream)
         self.fwd_args = (i8(self.q), st(self.q), i8(self.k), st(self.k), i8(self.v), st(self.v), i8(self.lst),
                          i8(self.cnt), B, S_q, w.S_kv, w.Hq, w.Hkv, w.D, K, ctypes.c_float(w.scale),
-                         i8(self.out), self.stream)
+                         i8(self.out), None, self.stream)
 
     def preprocess(self):
         rc = self.L.qsa_preprocess(*self.pre_args)

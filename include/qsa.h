@@ -1,6 +1,6 @@
 /*
- * qsa.h -- C ABI of libqsa: route-sparse grouped-query attention (forward)
- * on AMD Instinct MI355X (gfx950).
+ * qsa.h -- C ABI of libqsa: route-sparse grouped-query attention (forward
+ * and first-order backward) on AMD Instinct MI355X (gfx950).
  *
  * Every query row attends exactly to its own set of key/value token IDs
  * ("routes").  The operation is the one defined on the route-sparse GQA
@@ -143,13 +143,66 @@ int qsa_forward(const void *q, const int64_t q_strides[4], const void *k, const 
  *   exactly as qsa_preprocess writes them (with kv_length = S_kv).  Counts
  *   are clamped to [0, K] and IDs to [0, S_kv) before any address is formed,
  *   so malformed lists cannot fault, but their result is unspecified.
+ *   lse      OUT, nullable: [B, S_q, Hq] float32, contiguous, 4-B aligned:
+ *            the natural-log log-sum-exp of each row's scaled scores,
+ *            log sum_j exp(s_j) (the statistic the backward needs, fa4_qsa
+ *            page: the FA4 kernel owns first-order autograd); -inf for an
+ *            empty route set.  Must not overlap any other argument.
  *   Other arguments as in qsa_forward.
  */
 int qsa_forward_preprocessed(const void *q, const int64_t q_strides[4], const void *k,
                              const int64_t k_strides[4], const void *v, const int64_t v_strides[4],
                              const int32_t *route_list, const int32_t *route_count, int64_t B,
                              int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,
-                             float scale, void *out, void *stream);
+                             float scale, void *out, float *lse, void *stream);
+
+/*
+ * qsa_backward_workspace_size -- bytes of device workspace qsa_backward
+ * needs: delta (4*B*S_q*Hq), the key-segment counters
+ * (4*B*ceil(S_q/64)*ceil(S_kv/16)), tile totals and starts
+ * (about 8*B*ceil(S_kv/16)) and the segments (8*B*S_q*min(K, ceil(S_kv/16))),
+ * each 256-B aligned.  Returns 0 when a size is < 1 or beyond the library's
+ * int32 segment indexing (more than 2^31 - 1 segments, counters or tiles).
+ */
+size_t qsa_backward_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t K);
+
+/*
+ * qsa_backward -- first-order gradients of qsa_forward, BF16 in and out,
+ * fp32 arithmetic, deterministic (bitwise-repeatable for equal inputs).
+ *
+ * Definition (fa4_qsa page: FA4 owns first-order autograd; flex_qsa page,
+ * module description: rows whose routes are all invalid have zero output and
+ * zero gradients): for each (b, i, h) with hk = h / G, R = R(b,i) non-empty
+ * and p = softmax over j in R of s_j = scale <q[b,i,h], k[b,j,hk]>:
+ *   dp_j = <dout[b,i,h], v[b,j,hk]>,   ds_j = p_j (dp_j - <dout[b,i,h], out[b,i,h]>),
+ *   dq[b,i,h]    = scale sum_j ds_j k[b,j,hk],
+ *   dk[b,j,hk]  += scale ds_j q[b,i,h],   dv[b,j,hk] += p_j dout[b,i,h],
+ * summed over every (i, h) whose route set holds j.  Rows with an empty R get
+ * dq = +0.0 and add nothing; keys that no row routes get dk = dv = +0.0.
+ *
+ *   q, k, v       as in qsa_forward.
+ *   out           [B, S_q, Hq, D] bf16 contiguous: this forward's output.
+ *   dout          [B, S_q, Hq, D] bf16, strides as for q (last stride 1).
+ *   lse           [B, S_q, Hq] float32 contiguous: the forward's lse output.
+ *   route_list, route_count   as for qsa_forward_preprocessed.
+ *   dq            OUT [B, S_q, Hq, D] bf16 contiguous.
+ *   dk, dv        OUT [B, S_kv, Hkv, D] bf16 contiguous.
+ *   workspace, workspace_bytes   device scratch of at least
+ *                 qsa_backward_workspace_size(B, S_q, S_kv, Hq, K) bytes,
+ *                 256-B aligned (overwritten each call).
+ * Outputs and workspace must not overlap each other or any input.
+ *
+ * Runs the dq kernel (which also forms <dout, out> per row and head), the
+ * key-segment construction and the dk/dv kernel, in that order on `stream`.
+ * Errors: NULL_POINTER, EMPTY_DIM, KV_LENGTH, HEADS, HEAD_DIM, SCALE,
+ * LAYOUT, ALIAS, WORKSPACE, LIMIT, HIP.
+ */
+int qsa_backward(const void *q, const int64_t q_strides[4], const void *k, const int64_t k_strides[4],
+                 const void *v, const int64_t v_strides[4], const void *out, const void *dout,
+                 const int64_t dout_strides[4], const float *lse, const int32_t *route_list,
+                 const int32_t *route_count, int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv,
+                 int64_t D, int64_t K, float scale, void *dq, void *dk, void *dv, void *workspace,
+                 size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *qsa_status_string(int status);

@@ -1,4 +1,4 @@
-"""Route-sparse GQA attention (forward) on AMD Instinct MI355X.
+"""Route-sparse GQA attention (forward and backward) on AMD Instinct MI355X.
 
 Thin Python binding over the C ABI of ``libqsa.so`` (declared in
 ``include/qsa.h``).  The functions below only marshal arguments: they check
@@ -10,8 +10,9 @@ runs in the library's HIP kernels; there is no other code path.
 
 * ``qsa_preprocess(routes, kv_length, membership=False, tile_class=False)``
 * ``qsa_forward(q, k, v, routes, scale=None)``
-* ``qsa_forward_preprocessed(q, k, v, route_list, route_count, scale=None)``
-* ``qsa_forward_workspace_size(B, S_q, K)``
+* ``qsa_forward_preprocessed(q, k, v, route_list, route_count, scale=None, return_lse=False)``
+* ``qsa_backward(q, k, v, out, dout, lse, route_list, route_count, scale=None)``
+* ``qsa_forward_workspace_size(B, S_q, K)``, ``qsa_backward_workspace_size(B, S_q, S_kv, Hq, K)``
 * ``qsa_status_string(status)``
 """
 
@@ -69,8 +70,13 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_float, p, p, ctypes.c_size_t, p]
         L.qsa_forward.restype = i32
         L.qsa_forward_preprocessed.argtypes = [p, P64, p, P64, p, P64, p, p, i64, i64, i64, i64, i64, i64, i64,
-                                               ctypes.c_float, p, p]
+                                               ctypes.c_float, p, p, p]
         L.qsa_forward_preprocessed.restype = i32
+        L.qsa_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+        L.qsa_backward_workspace_size.restype = ctypes.c_size_t
+        L.qsa_backward.argtypes = [p, P64, p, P64, p, P64, p, p, P64, p, p, p, i64, i64, i64, i64, i64, i64, i64,
+                                   ctypes.c_float, p, p, p, p, ctypes.c_size_t, p]
+        L.qsa_backward.restype = i32
         _lib = L
     return _lib
 
@@ -81,6 +87,10 @@ def qsa_status_string(status: int) -> str:
 
 def qsa_forward_workspace_size(B: int, S_q: int, K: int) -> int:
     return int(lib().qsa_forward_workspace_size(int(B), int(S_q), int(K)))
+
+
+def qsa_backward_workspace_size(B: int, S_q: int, S_kv: int, Hq: int, K: int) -> int:
+    return int(lib().qsa_backward_workspace_size(int(B), int(S_q), int(S_kv), int(Hq), int(K)))
 
 
 def _check(status: int, where: str) -> None:
@@ -202,32 +212,79 @@ def qsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, routes: torch
     return out
 
 
-def qsa_forward_preprocessed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, route_list: torch.Tensor,
-                             route_count: torch.Tensor, scale: Optional[float] = None,
-                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Gather-attention alone, on lists produced by ``qsa_preprocess(routes, S_kv)``."""
-    dev = _require_gpu(q, k, v, route_list, route_count)
-    q, k, v = _bf16_operand(q, "query"), _bf16_operand(k, "key"), _bf16_operand(v, "value")
-    B, S_q, Hq, D, S_kv, Hkv = _attention_shapes(q, k, v)
+def _lists(route_list: torch.Tensor, route_count: torch.Tensor, B: int, S_q: int):
     if route_list.dtype != torch.int32 or route_count.dtype != torch.int32:
         raise ValueError("route_list and route_count must be int32")
     if route_list.dim() != 3 or tuple(route_list.shape[:2]) != (B, S_q) or tuple(route_count.shape) != (B, S_q):
         raise ValueError("route_list must be [B, S_q, K] and route_count [B, S_q]")
-    route_list, route_count = route_list.contiguous(), route_count.contiguous()
+    return route_list.contiguous(), route_count.contiguous()
+
+
+def qsa_forward_preprocessed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, route_list: torch.Tensor,
+                             route_count: torch.Tensor, scale: Optional[float] = None,
+                             out: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Gather-attention alone, on lists produced by ``qsa_preprocess(routes, S_kv)``.
+
+    Returns ``out``, or ``(out, lse)`` with ``lse`` float32 [B,S_q,Hq] (natural-log
+    log-sum-exp of each row's scaled scores, -inf for empty rows) when ``return_lse``.
+    """
+    dev = _require_gpu(q, k, v, route_list, route_count)
+    q, k, v = _bf16_operand(q, "query"), _bf16_operand(k, "key"), _bf16_operand(v, "value")
+    B, S_q, Hq, D, S_kv, Hkv = _attention_shapes(q, k, v)
+    route_list, route_count = _lists(route_list, route_count, B, S_q)
     K = route_list.shape[2]
     out = _output(out, (B, S_q, Hq, D), dev)
+    lse = torch.empty((B, S_q, Hq), dtype=torch.float32, device=dev) if return_lse else None
     st = lib().qsa_forward_preprocessed(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                         _ptr(route_list), _ptr(route_count), B, S_q, S_kv, Hq, Hkv, D, K,
-                                        _scale(scale, D), _ptr(out), _stream(dev))
+                                        _scale(scale, D), _ptr(out), _ptr(lse), _stream(dev))
     _check(st, "qsa_forward_preprocessed")
-    return out
+    return (out, lse) if return_lse else out
+
+
+def qsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                 lse: torch.Tensor, route_list: torch.Tensor, route_count: torch.Tensor,
+                 scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv), bfloat16, of ``qsa_forward_preprocessed`` for upstream gradient ``dout``.
+
+    ``out`` and ``lse`` are that forward's output and log-sum-exp (``return_lse=True``).
+    Deterministic: equal inputs give bitwise-equal gradients.
+    """
+    dev = _require_gpu(q, k, v, out, dout, lse, route_list, route_count)
+    q, k, v = _bf16_operand(q, "query"), _bf16_operand(k, "key"), _bf16_operand(v, "value")
+    dout = _bf16_operand(dout, "dout")
+    B, S_q, Hq, D, S_kv, Hkv = _attention_shapes(q, k, v)
+    if tuple(dout.shape) != (B, S_q, Hq, D) or tuple(out.shape) != (B, S_q, Hq, D):
+        raise ValueError("out and dout must have the query's shape")
+    if out.dtype != torch.bfloat16:
+        raise ValueError("out must be bfloat16")
+    out = out.contiguous()
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, S_q, Hq):
+        raise ValueError(f"lse must be float32 [B, S_q, Hq] = [{B}, {S_q}, {Hq}]")
+    lse = lse.contiguous()
+    route_list, route_count = _lists(route_list, route_count, B, S_q)
+    K = route_list.shape[2]
+    dq = torch.empty((B, S_q, Hq, D), dtype=torch.bfloat16, device=dev)
+    dk = torch.empty((B, S_kv, Hkv, D), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((B, S_kv, Hkv, D), dtype=torch.bfloat16, device=dev)
+    ws_bytes = qsa_backward_workspace_size(B, S_q, S_kv, Hq, K)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().qsa_backward(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(out),
+                            _ptr(dout), _strides(dout), _ptr(lse), _ptr(route_list), _ptr(route_count), B, S_q,
+                            S_kv, Hq, Hkv, D, K, _scale(scale, D), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "qsa_backward")
+    return dq, dk, dv
 
 
 __all__ = [
     "qsa_preprocess",
     "qsa_forward",
     "qsa_forward_preprocessed",
+    "qsa_backward",
     "qsa_forward_workspace_size",
+    "qsa_backward_workspace_size",
     "qsa_status_string",
     "lib",
     "QSAError",

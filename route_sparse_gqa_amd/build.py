@@ -26,6 +26,8 @@ SOURCES = [
     "route_normalize.hip",
     "membership_tiles.hip",
     "gather_attention.hip",
+    "attention_backward.hip",
+    "key_segments.hip",
     "qsa_api.cpp",
 ]
 
@@ -63,10 +65,11 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: an entry point whose kernel file is missing fails here, not at load time
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

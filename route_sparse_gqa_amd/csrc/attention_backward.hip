@@ -1,0 +1,411 @@
+// Backward pass of route-sparse GQA attention for gfx950 over compacted
+// route lists.
+//
+// Definition: fa4_qsa page (the FA4 kernel owns first-order autograd of this
+// attention) and flex_qsa page, module description (rows whose routes are all
+// invalid have zero output and zero gradients).  For a (b, i, h) with a
+// non-empty route set R, hk = h / G and p = softmax over j in R of
+// s_j = scale <q, k_j>:
+//   dp_j  = <dO, v_j>,   delta = <dO, O> = sum_j p_j dp_j,
+//   ds_j  = p_j (dp_j - delta),
+//   dq    = scale sum_j ds_j k_j,
+//   dk_j += scale ds_j q,     dv_j += p_j dO     (over every (i, h) routing j).
+// p is recomputed from the forward's log-sum-exp: p_j = exp(s_j - lse).
+//
+// Two kernels, both deterministic (each sum is taken in a fixed order; no
+// floating-point atomics), which is the part the pages leave unsupported:
+//  * dq_kernel: one wavefront per (b, i, hk) unit, mapped like the forward
+//    (one KV head per XCD).  It gathers the unit's routed K and V rows in
+//    16-key chunks through the wave's LDS slabs, recomputes S^T = K Q^T and
+//    dP^T = V dO^T with v_mfma_f32_16x16x32_bf16 (heads on the N side, so
+//    every per-head statistic is lane-local), forms dS^T, and accumulates
+//    dQ^T += K^T dS^T with v_mfma_f32_16x16x16_bf16, reading K^T with the
+//    transposing LDS load.  It also writes delta for the second kernel.
+//  * dkdv_kernel: one wavefront per (b, 16-key tile, hk).  The tile's K and
+//    V rows stay in registers as MFMA B operands; the wave walks the tile's
+//    key segments (query rows that route at least one key of the tile, in
+//    ascending row order, each with a 16-bit mask of the keys it routes) in
+//    batches of floor(16 / G) rows whose G heads fill the 16 MFMA rows.  Per
+//    batch it stages Q and dO of those rows in LDS, recomputes S = Q K^T and
+//    dP = dO V^T, and accumulates dV^T += dO^T P and dK^T += Q^T dS.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kWaves = 4;   // work units per workgroup
+constexpr int kChunk = 16;  // keys per dq iteration; keys per dkdv tile; MFMA rows per dkdv batch
+
+template <int D>
+struct Geo {
+  static constexpr int kSteps = D / 32;                 // 32-dim k-steps of the score products
+  static constexpr int kDimTiles = D / 16;              // 16-dim output tiles
+  static constexpr int kLanesPerRow = D / 8;            // 16-byte pieces per row
+  static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+  static constexpr int kLoads = kChunk / kRowsPerLoad;  // load instructions per 16 rows
+  static constexpr int kTrStride = D + 16;              // slabs read transposed: 2D + 32 bytes per row
+  static constexpr int kRowStride = D + 8;              // slabs read by rows only: 2D + 16 bytes per row
+};
+
+// ---------------------------------------------------------------------------
+// dq (and delta)
+// ---------------------------------------------------------------------------
+
+template <int D, bool kNarrow>
+__global__ void __launch_bounds__(64 * kWaves)
+    dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+              const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, int64_t qs0, int64_t qs1,
+              int64_t qs2, int64_t ks0, int64_t ks1, int64_t ks2, int64_t vs0, int64_t vs1, int64_t vs2,
+              int64_t gs0, int64_t gs1, int64_t gs2, const float* __restrict__ lse,
+              const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count, int64_t S_q,
+              int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t K, int G, float scale_log2e, float scale,
+              int64_t n_rows, uint16_t* __restrict__ dq, float* __restrict__ delta) {
+  using Gm = Geo<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t kslab[kWaves][kChunk * Gm::kTrStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vslab[kWaves][kChunk * Gm::kRowStride];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t x = blockIdx.x;
+  const int64_t hk = x % Hkv;  // one KV head per XCD, as in the forward
+  const int64_t row = (x / Hkv) * kWaves + wave;
+  if (row >= n_rows) return;  // no workgroup barriers in this kernel
+  const int64_t b = row / S_q;
+  const int64_t i = row % S_q;
+  const int c = lane & 15;  // head column (N side); key / dim row within a 16-tile
+  const int g = lane >> 4;
+  const bool head_ok = c < G;
+  const int64_t hq = hk * G + (head_ok ? c : 0);
+  uint16_t* dq_row = dq + (row * Hq + hk * G + c) * D;  // only dereferenced when head_ok
+
+  const int n = static_cast<int>(min(max(static_cast<int64_t>(route_count[row]), int64_t{0}), K));
+  if (n == 0) {  // empty route set: zero gradient, nothing reaches dk / dv
+    if (head_ok) {
+#pragma unroll
+      for (int t = 0; t < Gm::kDimTiles; ++t)
+        *reinterpret_cast<u32x2*>(dq_row + 16 * t + 4 * g) = u32x2{0u, 0u};
+      if (g == 0) delta[row * Hq + hk * G + c] = 0.f;
+    }
+    return;
+  }
+
+  // Q^T and dO^T as MFMA B operands: lane (c, g) holds head c, dims 32s + 8g .. +7.
+  bf16x8 qf[Gm::kSteps], gf[Gm::kSteps];
+  float dl = 0.f;  // this lane's share of delta = <dO, O> for head c
+  {
+    const uint16_t* qp = q + b * qs0 + i * qs1 + hq * qs2 + 8 * g;
+    const uint16_t* gp = dout + b * gs0 + i * gs1 + hq * gs2 + 8 * g;
+    const uint16_t* op = o + (row * Hq + hq) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < Gm::kSteps; ++s) {
+      const u32x4 qw = head_ok ? load16(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 gw = head_ok ? load16(gp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 ow = head_ok ? load16(op + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+      qf[s] = __builtin_bit_cast(bf16x8, qw);
+      gf[s] = __builtin_bit_cast(bf16x8, gw);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dl += bf16_lo(gw[e]) * bf16_lo(ow[e]) + bf16_hi(gw[e]) * bf16_hi(ow[e]);
+    }
+  }
+  dl += __shfl_xor(dl, 16);
+  dl += __shfl_xor(dl, 32);
+  const float lse2 = head_ok ? lse[row * Hq + hq] * kLog2e : 0.f;
+  if (head_ok && g == 0) delta[row * Hq + hq] = dl;
+
+  f32x4 acc[Gm::kDimTiles];
+#pragma unroll
+  for (int t = 0; t < Gm::kDimTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* lst = route_list + row * K;
+  const int64_t ks1b = 2 * ks1, vs1b = 2 * vs1;
+  const char* kb = reinterpret_cast<const char*>(k + b * ks0 + hk * ks2) + 16 * (lane % Gm::kLanesPerRow);
+  const char* vb = reinterpret_cast<const char*>(v + b * vs0 + hk * vs2) + 16 * (lane % Gm::kLanesPerRow);
+  uint16_t* my_k = kslab[wave];
+  uint16_t* my_v = vslab[wave];
+  const int32_t id_max = static_cast<int32_t>(S_kv - 1);
+  auto clamp_id = [&](int32_t xid) { return min(max(xid, 0), id_max); };
+  auto load_id = [&](int base) { return lst[min(base + c, n - 1)]; };
+  auto load_rows = [&](const char* base, int64_t stride_b, int32_t id, u32x4* r) {
+#pragma unroll
+    for (int u = 0; u < Gm::kLoads; ++u) {
+      const int32_t idr = __shfl(id, u * Gm::kRowsPerLoad + lane / Gm::kLanesPerRow);
+      r[u] = load16(base + RowOffset<kNarrow>::of(idr, stride_b));
+    }
+  };
+
+  u32x4 kr[Gm::kLoads], vr[Gm::kLoads];
+  int32_t raw_next = load_id(kChunk);
+  {
+    const int32_t id0 = clamp_id(load_id(0));
+    load_rows(kb, ks1b, id0, kr);
+    load_rows(vb, vs1b, id0, vr);
+  }
+  int32_t id_next = clamp_id(raw_next);
+
+  const uint16_t* ktr = my_k + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
+  for (int base = 0; base < n; base += kChunk) {
+    const bool more = base + kChunk < n;
+
+    wave_lds_sync();  // the previous chunk's slab reads are complete
+#pragma unroll
+    for (int u = 0; u < Gm::kLoads; ++u) {
+      const int r = u * Gm::kRowsPerLoad + lane / Gm::kLanesPerRow;
+      const int col = 8 * (lane % Gm::kLanesPerRow);
+      *reinterpret_cast<u32x4*>(my_k + r * Gm::kTrStride + col) = kr[u];
+      *reinterpret_cast<u32x4*>(my_v + r * Gm::kRowStride + col) = vr[u];
+    }
+    wave_lds_sync();
+
+    // S^T[key 4g + r][head c] and dP^T[key 4g + r][head c]; A operands are
+    // rows of the slabs (key c, dims 32s + 8g .. +7).
+    f32x4 st = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* ka = my_k + c * Gm::kTrStride + 8 * g;
+    const uint16_t* va = my_v + c * Gm::kRowStride + 8 * g;
+#pragma unroll
+    for (int s = 0; s < Gm::kSteps; ++s) {
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(ka + 32 * s)), qf[s], st, 0, 0, 0);
+      dpt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(va + 32 * s)), gf[s], dpt, 0, 0,
+                                                    0);
+    }
+
+    if (more) {
+      raw_next = load_id(base + 2 * kChunk);
+      load_rows(kb, ks1b, id_next, kr);
+      load_rows(vb, vs1b, id_next, vr);
+    }
+
+    // dS^T = P^T (dP^T - delta), P^T = exp2(S^T scale log2e - lse2); keys past n
+    // (the repeated tail) and padded heads contribute nothing.
+    bf16x4 dsb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool on = head_ok && base + 4 * g + r < n;
+      const float p = on ? exp2f(st[r] * scale_log2e - lse2) : 0.f;
+      dsb[r] = static_cast<__bf16>(p * (dpt[r] - dl));
+    }
+    const i16x4 db = __builtin_bit_cast(i16x4, dsb);
+
+    // dQ^T += K^T dS^T: the transposed read gives lane (c, g) keys 4g .. 4g+3 of dim 16t + c.
+#pragma unroll
+    for (int t = 0; t < Gm::kDimTiles; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(ktr + 16 * t), db, acc[t], 0, 0, 0);
+
+    if (more) id_next = clamp_id(raw_next);
+  }
+
+  if (head_ok) {
+#pragma unroll
+    for (int t = 0; t < Gm::kDimTiles; ++t) {
+      bf16x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = static_cast<__bf16>(acc[t][r] * scale);
+      *reinterpret_cast<u32x2*>(dq_row + 16 * t + 4 * g) = __builtin_bit_cast(u32x2, w);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ void __launch_bounds__(64 * kWaves)
+    dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                const uint16_t* __restrict__ dout, int64_t qs0, int64_t qs1, int64_t qs2, int64_t ks0, int64_t ks1,
+                int64_t ks2, int64_t vs0, int64_t vs1, int64_t vs2, int64_t gs0, int64_t gs1, int64_t gs2,
+                const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ seg_start,
+                const int2* __restrict__ segs, int64_t seg_capacity, int64_t S_q, int64_t S_kv, int64_t Hq,
+                int64_t Hkv, int G, int rows_per_batch, int64_t n_kt, int64_t n_units, float scale_log2e, float scale,
+                uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  using Gm = Geo<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t qslab[kWaves][kChunk * Gm::kTrStride];
+  __shared__ __attribute__((aligned(16))) uint16_t gslab[kWaves][kChunk * Gm::kTrStride];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t x = blockIdx.x;
+  const int64_t hk = x % Hkv;  // one KV head per XCD
+  const int64_t unit = (x / Hkv) * kWaves + wave;  // b * n_kt + tile
+  if (unit >= n_units) return;  // no workgroup barriers in this kernel
+  const int64_t b = unit / n_kt;
+  const int64_t key0 = (unit % n_kt) * kChunk;
+  const int c = lane & 15;  // key of the tile (N side); col / dim row within a 16-tile
+  const int g = lane >> 4;
+
+  // K and V of the tile as B operands: lane (c, g) holds key c, dims 32s + 8g .. +7.
+  bf16x8 kf[Gm::kSteps], vf[Gm::kSteps];
+  {
+    const int64_t key = min(key0 + c, S_kv - 1);
+    const uint16_t* kp = k + b * ks0 + key * ks1 + hk * ks2 + 8 * g;
+    const uint16_t* vp = v + b * vs0 + key * vs1 + hk * vs2 + 8 * g;
+#pragma unroll
+    for (int s = 0; s < Gm::kSteps; ++s) {
+      kf[s] = __builtin_bit_cast(bf16x8, load16(kp + 32 * s));
+      vf[s] = __builtin_bit_cast(bf16x8, load16(vp + 32 * s));
+    }
+  }
+  f32x4 acc_k[Gm::kDimTiles], acc_v[Gm::kDimTiles];
+#pragma unroll
+  for (int t = 0; t < Gm::kDimTiles; ++t) acc_k[t] = acc_v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint16_t* my_q = qslab[wave];
+  uint16_t* my_g = gslab[wave];
+  const uint16_t* qtr = my_q + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
+  const uint16_t* gtr = my_g + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
+  const int cols = rows_per_batch * G;  // MFMA rows in use: (row slot, head) = (col / G, col % G)
+  // Segment range of this tile (clamped to the buffer: malformed lists can
+  // count more segments than it holds, valid ones cannot).
+  const int32_t s_begin = static_cast<int32_t>(min(static_cast<int64_t>(seg_start[unit]), seg_capacity));
+  const int32_t s_end = static_cast<int32_t>(min(static_cast<int64_t>(seg_start[unit + 1]), seg_capacity));
+  const int64_t q_head0 = hk * G;
+
+  for (int32_t sb = s_begin; sb < s_end; sb += rows_per_batch) {
+    // Lane r < rows_per_batch holds segment sb + r: its query row and key mask.
+    int32_t seg_row = 0, seg_mask = 0;
+    if (lane < rows_per_batch && sb + lane < s_end) {
+      const int2 e = segs[sb + lane];
+      seg_row = min(max(e.x, 0), static_cast<int32_t>(S_q - 1));
+      seg_mask = e.y;
+    }
+
+    // Stage Q and dO of the batch's (row, head) columns, one 16-row tile each.
+    wave_lds_sync();  // the previous batch's slab reads are complete
+#pragma unroll
+    for (int u = 0; u < Gm::kLoads; ++u) {
+      const int col = u * Gm::kRowsPerLoad + lane / Gm::kLanesPerRow;
+      const int slot = col / G;
+      const int32_t ir = __shfl(seg_row, min(slot, 15));
+      const bool ok = col < cols && sb + slot < s_end;
+      const int64_t h = q_head0 + (ok ? col % G : 0);
+      const int piece = 8 * (lane % Gm::kLanesPerRow);
+      const u32x4 qw = ok ? load16(q + b * qs0 + ir * qs1 + h * qs2 + piece) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 gw = ok ? load16(dout + b * gs0 + ir * gs1 + h * gs2 + piece) : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(my_q + col * Gm::kTrStride + piece) = qw;
+      *reinterpret_cast<u32x4*>(my_g + col * Gm::kTrStride + piece) = gw;
+    }
+
+    // Per-column statistics for this lane's columns 4g .. 4g+3 and key c.
+    float lse2[4], dl[4];
+    bool on[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int col = 4 * g + r;
+      const int slot = col / G;
+      const int32_t ir = __shfl(seg_row, min(slot, 15));
+      const int32_t m = __shfl(seg_mask, min(slot, 15));
+      const bool ok = col < cols && sb + slot < s_end;
+      const int64_t idx = (b * S_q + ir) * Hq + q_head0 + (ok ? col % G : 0);
+      lse2[r] = ok ? lse[idx] * kLog2e : 0.f;
+      dl[r] = ok ? delta[idx] : 0.f;
+      on[r] = ok && ((m >> c) & 1) != 0;
+    }
+    wave_lds_sync();  // staged columns visible to the whole wave
+
+    // S[col 4g + r][key c] = Q K^T and dP = dO V^T; A operands are slab rows
+    // (col c, dims 32s + 8g .. +7).
+    f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* qa = my_q + c * Gm::kTrStride + 8 * g;
+    const uint16_t* ga = my_g + c * Gm::kTrStride + 8 * g;
+#pragma unroll
+    for (int s = 0; s < Gm::kSteps; ++s) {
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(qa + 32 * s)), kf[s], st, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(ga + 32 * s)), vf[s], dp, 0, 0, 0);
+    }
+
+    bf16x4 pb, dsb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = on[r] ? exp2f(st[r] * scale_log2e - lse2[r]) : 0.f;
+      pb[r] = static_cast<__bf16>(p);
+      dsb[r] = static_cast<__bf16>(p * (dp[r] - dl[r]));
+    }
+    const i16x4 pi = __builtin_bit_cast(i16x4, pb);
+    const i16x4 di = __builtin_bit_cast(i16x4, dsb);
+
+    // dV^T += dO^T P and dK^T += Q^T dS: the transposed reads give lane (c, g)
+    // columns 4g .. 4g+3 of dim 16t + c, matching its four P / dS values.
+#pragma unroll
+    for (int t = 0; t < Gm::kDimTiles; ++t) {
+      acc_v[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(gtr + 16 * t), pi, acc_v[t], 0, 0, 0);
+      acc_k[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(qtr + 16 * t), di, acc_k[t], 0, 0, 0);
+    }
+  }
+
+  // Lane (c, g) holds dims 16t + 4g .. +3 of key key0 + c.
+  if (key0 + c < S_kv) {
+    const int64_t off = ((b * S_kv + key0 + c) * Hkv + hk) * D + 4 * g;
+#pragma unroll
+    for (int t = 0; t < Gm::kDimTiles; ++t) {
+      bf16x4 wk, wv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        wk[r] = static_cast<__bf16>(acc_k[t][r] * scale);
+        wv[r] = static_cast<__bf16>(acc_v[t][r]);
+      }
+      *reinterpret_cast<u32x2*>(dk + off + 16 * t) = __builtin_bit_cast(u32x2, wk);
+      *reinterpret_cast<u32x2*>(dv + off + 16 * t) = __builtin_bit_cast(u32x2, wv);
+    }
+  }
+}
+
+bool narrow_offsets(const BwdArgs& a) {
+  const int64_t lim = (int64_t{1} << 32) - 1;
+  if (a.ks[1] < 0 || a.vs[1] < 0) return false;
+  return (a.S_kv - 1) * a.ks[1] * 2 + 2 * a.D <= lim && (a.S_kv - 1) * a.vs[1] * 2 + 2 * a.D <= lim;
+}
+
+template <int D, bool kNarrow>
+hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
+  const int64_t rows = a.B * a.S_q;
+  const int64_t blocks = (rows + kWaves - 1) / kWaves * a.Hkv;
+  hipLaunchKernelGGL((dq_kernel<D, kNarrow>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0, stream,
+                     a.q, a.k, a.v, a.out, a.dout, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0],
+                     a.vs[1], a.vs[2], a.gs[0], a.gs[1], a.gs[2], a.lse, a.route_list, a.route_count, a.S_q, a.S_kv,
+                     a.Hq, a.Hkv, a.K, static_cast<int>(a.Hq / a.Hkv), a.scale * kLog2e, a.scale, rows, a.dq,
+                     a.delta);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t stream) {
+  const int64_t n_kt = (a.S_kv + kChunk - 1) / kChunk;
+  const int64_t units = a.B * n_kt;
+  const int64_t blocks = (units + kWaves - 1) / kWaves * a.Hkv;
+  const int G = static_cast<int>(a.Hq / a.Hkv);
+  hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0, stream, a.q, a.k,
+                     a.v, a.dout, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0], a.vs[1], a.vs[2],
+                     a.gs[0], a.gs[1], a.gs[2], a.lse, a.delta, a.seg_start, a.segs, a.seg_capacity, a.S_q, a.S_kv, a.Hq,
+                     a.Hkv, G,
+                     kChunk / G, n_kt, units, a.scale * kLog2e, a.scale, a.dk, a.dv);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_any(const BwdArgs& a, hipStream_t stream) {
+  return narrow_offsets(a) ? launch_dq_d<D, true>(a, stream) : launch_dq_d<D, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_attention_dq(const BwdArgs& a, hipStream_t stream) {
+  switch (a.D) {
+    case 64: return launch_dq_any<64>(a, stream);
+    case 128: return launch_dq_any<128>(a, stream);
+    case 256: return launch_dq_any<256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attention_dkdv(const BwdArgs& a, hipStream_t stream) {
+  switch (a.D) {
+    case 64: return launch_dkdv_d<64>(a, stream);
+    case 128: return launch_dkdv_d<128>(a, stream);
+    case 256: return launch_dkdv_d<256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qsa

@@ -35,18 +35,11 @@
 //    both the PV product and the normaliser.
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vectors stay in registers
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 4;   // work units per workgroup
 constexpr int kChunk = 16;  // routes per inner iteration (M of S^T, K of PV)
@@ -63,37 +56,6 @@ struct Geometry {
   static constexpr int kKStride = D + 8;                // K slab row stride in bf16 (2D + 16 bytes)
 };
 
-__device__ __forceinline__ u32x4 load16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// Transposed LDS read (gfx950): within each 16-lane group, slot j of lane i
-// receives element i % 4 of the 4-element row piece addressed by lane
-// 4 * j + i / 4.  With lane L addressing row L / 4, columns 16t + 4 * (L % 4),
-// lane (c, g) receives rows 4g .. 4g+3 of column 16t + c.
-__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));  // generic -> LDS address-space cast
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Byte offset of a gathered row: 32-bit when every row of the tensor lies
-// within 4 GiB of its (batch, head) base, else 64-bit.
-template <bool kNarrow>
-struct RowOffset {
-  __device__ static __forceinline__ uint32_t of(int32_t id, int64_t stride_bytes) {
-    return static_cast<uint32_t>(id) * static_cast<uint32_t>(stride_bytes);
-  }
-};
-template <>
-struct RowOffset<false> {
-  __device__ static __forceinline__ int64_t of(int32_t id, int64_t stride_bytes) {
-    return static_cast<int64_t>(id) * stride_bytes;
-  }
-};
-
 template <int D, bool kNarrow>
 __global__ void __launch_bounds__(64 * kWaves)
     gather_attention_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -101,7 +63,8 @@ __global__ void __launch_bounds__(64 * kWaves)
                             int64_t ks0, int64_t ks1, int64_t ks2, int64_t vs0, int64_t vs1, int64_t vs2,
                             const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count,
                             int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t K, int G,
-                            float scale_log2e, int64_t n_units, uint16_t* __restrict__ out) {
+                            float scale_log2e, int64_t n_units, uint16_t* __restrict__ out,
+                            float* __restrict__ lse) {
   using Geo = Geometry<D>;
   __shared__ __attribute__((aligned(16))) uint16_t slab[kWaves][kChunk * Geo::kStride];
   __shared__ __attribute__((aligned(16))) uint16_t kslab[kWaves][kChunk * Geo::kKStride];
@@ -124,11 +87,12 @@ __global__ void __launch_bounds__(64 * kWaves)
   uint16_t* out_row = out + (row * Hq + hk * G + c) * D;  // only dereferenced when head_ok
 
   const int n = static_cast<int>(min(max(static_cast<int64_t>(route_count[row]), int64_t{0}), K));
-  if (n == 0) {  // empty route set: exactly +0.0
+  if (n == 0) {  // empty route set: exactly +0.0 (and a log-sum-exp of -inf)
     if (head_ok) {
 #pragma unroll
       for (int t = 0; t < Geo::kDimTiles; ++t)
         *reinterpret_cast<u32x2*>(out_row + 16 * t + 4 * g) = u32x2{0u, 0u};
+      if (lse != nullptr && g == 0) lse[row * Hq + hk * G + c] = -INFINITY;
     }
     return;
   }
@@ -256,6 +220,10 @@ __global__ void __launch_bounds__(64 * kWaves)
   float l_tot = l_run + __shfl_xor(l_run, 16);  // butterfly over the four lane groups of head c
   l_tot += __shfl_xor(l_tot, 32);
   const float inv = 1.0f / l_tot;
+  // Natural-log log-sum-exp of the scaled scores: the sum is taken against
+  // the reference max m_run (log2 domain), from the same bf16-rounded
+  // probabilities as the output.
+  if (lse != nullptr && head_ok && g == 0) lse[row * Hq + hk * G + c] = (m_run + log2f(l_tot)) * kLn2;
   if (head_ok) {
 #pragma unroll
     for (int t = 0; t < Geo::kDimTiles; ++t) {
@@ -271,11 +239,11 @@ template <int D, bool kNarrow>
 hipError_t launch(const AttnArgs& a, hipStream_t stream) {
   const int64_t n_units = a.B * a.S_q * a.Hkv;
   const int64_t blocks = (a.B * a.S_q + kWaves - 1) / kWaves * a.Hkv;
-  const float scale_log2e = a.scale * 1.4426950408889634f;
+  const float scale_log2e = a.scale * kLog2e;
   hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves),
                      0, stream, a.q, a.k, a.v, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0],
                      a.vs[1], a.vs[2], a.route_list, a.route_count, a.S_q, a.S_kv, a.Hq, a.Hkv, a.K,
-                     static_cast<int>(a.Hq / a.Hkv), scale_log2e, n_units, a.out);
+                     static_cast<int>(a.Hq / a.Hkv), scale_log2e, n_units, a.out, a.lse);
   return hipGetLastError();
 }
 

@@ -196,7 +196,7 @@ int check_attention(const void* q, const int64_t q_strides[4], const void* k, co
 qsa::AttnArgs attn_args(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
                         const void* v, const int64_t v_strides[4], const int32_t* list, const int32_t* count,
                         int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,
-                        float scale, void* out) {
+                        float scale, void* out, float* lse = nullptr) {
   qsa::AttnArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -209,6 +209,7 @@ qsa::AttnArgs attn_args(const void* q, const int64_t q_strides[4], const void* k
   a.B = B; a.S_q = S_q; a.S_kv = S_kv; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.K = K;
   a.scale = scale;
   a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
   return a;
 }
 
@@ -255,7 +256,7 @@ QSA_EXPORT int qsa_forward_preprocessed(const void* q, const int64_t q_strides[4
                                         const int64_t k_strides[4], const void* v, const int64_t v_strides[4],
                                         const int32_t* route_list, const int32_t* route_count, int64_t B,
                                         int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,
-                                        float scale, void* out, void* stream) {
+                                        float scale, void* out, float* lse, void* stream) {
   Sizes s;
   Range r_q, r_k, r_v, r_out;
   if (int st = check_attention(q, q_strides, k, k_strides, v, v_strides, B, S_q, S_kv, Hq, Hkv, D, K, scale,
@@ -263,10 +264,140 @@ QSA_EXPORT int qsa_forward_preprocessed(const void* q, const int64_t q_strides[4
     return st;
   if (route_list == nullptr || route_count == nullptr) return QSA_ERR_NULL_POINTER;
   if (!aligned(route_list, 4) || !aligned(route_count, 4)) return QSA_ERR_LAYOUT;
-  if (overlap(r_out, dense(route_list, s.list_bytes)) || overlap(r_out, dense(route_count, s.count_bytes)))
-    return QSA_ERR_ALIAS;
+  const Range r_list = dense(route_list, s.list_bytes), r_count = dense(route_count, s.count_bytes);
+  if (overlap(r_out, r_list) || overlap(r_out, r_count)) return QSA_ERR_ALIAS;
+  if (lse != nullptr) {
+    if (!aligned(lse, 4)) return QSA_ERR_LAYOUT;
+    const Range r_lse = dense(lse, 4 * s.rows * Hq);
+    if (overlap(r_lse, r_out) || overlap(r_lse, r_q) || overlap(r_lse, r_k) || overlap(r_lse, r_v) ||
+        overlap(r_lse, r_list) || overlap(r_lse, r_count))
+      return QSA_ERR_ALIAS;
+  }
   (void)hipGetLastError();
   const qsa::AttnArgs a = attn_args(q, q_strides, k, k_strides, v, v_strides, route_list, route_count, B, S_q,
-                                    S_kv, Hq, Hkv, D, K, scale, out);
+                                    S_kv, Hq, Hkv, D, K, scale, out, lse);
   return hip_status(qsa::launch_gather_attention(a, as_stream(stream)));
+}
+
+namespace {
+
+// Backward workspace: delta, then the key-segment buffers, each 256-B aligned.
+struct BwdLayout {
+  size_t delta = 0, counters = 0, totals = 0, tile_start = 0, segs = 0, total = 0;
+  int64_t n_kt = 0, capacity = 0;
+};
+
+bool bwd_layout(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t K, BwdLayout* l) {
+  if (B < 1 || S_q < 1 || S_kv < 1 || Hq < 1 || K < 1) return false;
+  int64_t rows = 0, heads = 0, counters = 0, tiles = 0, cap = 0;
+  const int64_t n_rb = (S_q + qsa::kSegRowBlock - 1) / qsa::kSegRowBlock;
+  l->n_kt = (S_kv + qsa::kSegKeyTile - 1) / qsa::kSegKeyTile;
+  if (!mul_ok(B, S_q, &rows) || !mul_ok(rows, Hq, &heads) || !mul_ok(B * n_rb, l->n_kt, &counters) ||
+      !mul_ok(B, l->n_kt, &tiles) || !mul_ok(rows, K < l->n_kt ? K : l->n_kt, &cap))
+    return false;
+  // segment positions, counters and tile starts are int32
+  if (cap > kMaxGrid || counters > kMaxGrid || tiles + 1 > kMaxGrid || heads > (INT64_MAX >> 3)) return false;
+  l->capacity = cap;
+  size_t off = 0;
+  l->delta = off;
+  off += round_up(static_cast<size_t>(4 * heads), kWorkspaceAlign);
+  l->counters = off;
+  off += round_up(static_cast<size_t>(4 * counters), kWorkspaceAlign);
+  l->totals = off;
+  off += round_up(static_cast<size_t>(4 * tiles), kWorkspaceAlign);
+  l->tile_start = off;
+  off += round_up(static_cast<size_t>(4 * (tiles + 1)), kWorkspaceAlign);
+  l->segs = off;
+  off += round_up(static_cast<size_t>(8 * cap), kWorkspaceAlign);
+  l->total = off;
+  return true;
+}
+
+}  // namespace
+
+QSA_EXPORT size_t qsa_backward_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t K) {
+  BwdLayout l;
+  return bwd_layout(B, S_q, S_kv, Hq, K, &l) ? l.total : 0;
+}
+
+QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
+                            const void* v, const int64_t v_strides[4], const void* out, const void* dout,
+                            const int64_t dout_strides[4], const float* lse, const int32_t* route_list,
+                            const int32_t* route_count, int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq,
+                            int64_t Hkv, int64_t D, int64_t K, float scale, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  Sizes s;
+  Range r_q, r_k, r_v, r_dq;
+  if (int st = check_attention(q, q_strides, k, k_strides, v, v_strides, B, S_q, S_kv, Hq, Hkv, D, K, scale, dq,
+                               &s, &r_q, &r_k, &r_v, &r_dq))
+    return st;
+  if (out == nullptr || dout == nullptr || dout_strides == nullptr || lse == nullptr || route_list == nullptr ||
+      route_count == nullptr || dk == nullptr || dv == nullptr)
+    return QSA_ERR_NULL_POINTER;
+  if (int st = check_bf16_tensor(dout, dout_strides)) return st;
+  if (!aligned(out, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(route_list, 4) ||
+      !aligned(route_count, 4))
+    return QSA_ERR_LAYOUT;
+  BwdLayout l;
+  if (!bwd_layout(B, S_q, S_kv, Hq, K, &l)) return QSA_ERR_LIMIT;
+  int64_t kv_elems = 0;
+  if (!mul_ok(B * S_kv, Hkv * D, &kv_elems) || kv_elems > (INT64_MAX >> 2)) return QSA_ERR_LIMIT;
+  if ((l.n_kt * B + 3) / 4 * Hkv > kMaxGrid || (B * ((S_q + 63) / 64) + 3) / 4 > kMaxGrid) return QSA_ERR_LIMIT;
+  if (workspace == nullptr || workspace_bytes < l.total || !aligned(workspace, kWorkspaceAlign))
+    return QSA_ERR_WORKSPACE;
+
+  const int64_t qshape[4] = {B, S_q, Hq, D};
+  const Range r_o = dense(out, 2 * s.rows * Hq * D);
+  const Range r_g = extent(dout, qshape, dout_strides, 4, 2);
+  const Range r_lse = dense(lse, 4 * s.rows * Hq);
+  const Range r_list = dense(route_list, s.list_bytes), r_count = dense(route_count, s.count_bytes);
+  const Range r_dk = dense(dk, 2 * kv_elems), r_dv = dense(dv, 2 * kv_elems);
+  const Range r_ws = dense(workspace, static_cast<int64_t>(l.total));
+  const Range ins[8] = {r_q, r_k, r_v, r_o, r_g, r_lse, r_list, r_count};
+  const Range outs[4] = {r_dq, r_dk, r_dv, r_ws};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 8; ++b)
+      if (overlap(outs[a], ins[b])) return QSA_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return QSA_ERR_ALIAS;
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  qsa::SegmentBuffers w;
+  w.counters = reinterpret_cast<int32_t*>(ws + l.counters);
+  w.totals = reinterpret_cast<int32_t*>(ws + l.totals);
+  w.tile_start = reinterpret_cast<int32_t*>(ws + l.tile_start);
+  w.segs = reinterpret_cast<int2*>(ws + l.segs);
+  w.capacity = l.capacity;
+
+  qsa::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<const uint16_t*>(out);
+  a.dout = static_cast<const uint16_t*>(dout);
+  std::memcpy(a.qs, q_strides, sizeof a.qs);
+  std::memcpy(a.ks, k_strides, sizeof a.ks);
+  std::memcpy(a.vs, v_strides, sizeof a.vs);
+  std::memcpy(a.gs, dout_strides, sizeof a.gs);
+  a.lse = lse;
+  a.delta = reinterpret_cast<float*>(ws + l.delta);
+  a.route_list = route_list;
+  a.route_count = route_count;
+  a.seg_start = w.tile_start;
+  a.segs = w.segs;
+  a.seg_capacity = w.capacity;
+  a.B = B; a.S_q = S_q; a.S_kv = S_kv; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.K = K;
+  a.scale = scale;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+
+  (void)hipGetLastError();
+  hipStream_t st = as_stream(stream);
+  int rc = hip_status(qsa::launch_attention_dq(a, st));
+  if (rc != QSA_OK) return rc;
+  rc = hip_status(qsa::launch_key_segments(route_list, route_count, B, S_q, K, S_kv, w, st));
+  if (rc != QSA_OK) return rc;
+  return hip_status(qsa::launch_attention_dkdv(a, st));
 }

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <hip/hip_vector_types.h>
 #include <stdint.h>
 
 namespace qsa {
@@ -29,9 +30,51 @@ struct AttnArgs {
   int64_t B, S_q, S_kv, Hq, Hkv, D, K;
   float scale;
   uint16_t* out;
+  float* lse;  // nullable: [B*S_q*Hq] natural-log log-sum-exp
 };
 
 // Fused gather-attention over compacted lists.
 hipError_t launch_gather_attention(const AttnArgs& a, hipStream_t stream);
+
+// Key segments (route lists regrouped by 16-key tile, rows ascending).
+constexpr int64_t kSegKeyTile = 16;   // keys per tile of the key-side backward
+constexpr int64_t kSegRowBlock = 64;  // query rows per counting block
+
+struct SegmentBuffers {
+  int32_t* counters;    // [B * ceil(S_q / 64) * n_kt]
+  int32_t* totals;      // [B * n_kt]
+  int32_t* tile_start;  // [B * n_kt + 1]: segments of (b, t) are [start[b*n_kt+t], start[b*n_kt+t+1])
+  int2* segs;           // [capacity] {query row within the batch, key mask}
+  int64_t capacity;
+};
+
+hipError_t launch_key_segments(const int32_t* route_list, const int32_t* route_count, int64_t B, int64_t S_q,
+                               int64_t K, int64_t S_kv, const SegmentBuffers& w, hipStream_t stream);
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;   // forward output [B, S_q, Hq, D], contiguous
+  const uint16_t* dout;  // upstream gradient, strided like q
+  int64_t qs[4], ks[4], vs[4], gs[4];
+  const float* lse;      // [B * S_q * Hq] natural-log log-sum-exp of the forward
+  float* delta;          // [B * S_q * Hq] <dout, out>, written by the dq pass
+  const int32_t* route_list;
+  const int32_t* route_count;
+  const int32_t* seg_start;
+  const int2* segs;
+  int64_t seg_capacity;
+  int64_t B, S_q, S_kv, Hq, Hkv, D, K;
+  float scale;
+  uint16_t* dq;  // [B, S_q, Hq, D] contiguous
+  uint16_t* dk;  // [B, S_kv, Hkv, D] contiguous
+  uint16_t* dv;  // [B, S_kv, Hkv, D] contiguous
+};
+
+// dq and delta (one wavefront per (b, i, hk)); then dk and dv (one wavefront
+// per (b, 16-key tile, hk)) over the key segments.
+hipError_t launch_attention_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attention_dkdv(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace qsa

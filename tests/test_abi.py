@@ -29,7 +29,7 @@ def _declared_constants():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "qsa_preprocess", "qsa_forward", "qsa_forward_preprocessed", "qsa_forward_workspace_size",
-        "qsa_status_string"])
+        "qsa_backward", "qsa_backward_workspace_size", "qsa_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -91,3 +91,40 @@ def test_other_host_checks():
     assert L.qsa_preprocess(fake, 1, 1, 2, 3, s3, 0, fake, fake, None, None, None) == -3
     assert L.qsa_preprocess(fake, 9, 1, 2, 3, s3, 5, fake, fake, None, None, None) == -6
     assert L.qsa_preprocess(None, 1, 1, 2, 3, s3, 5, fake, fake, None, None, None) == -1
+
+
+def test_backward_workspace_size():
+    ws = qsa.qsa_backward_workspace_size
+    r = lambda x: -(-x // 256) * 256
+    B, S_q, S_kv, Hq, K = 2, 4096, 4096, 16, 512
+    n_kt, n_rb = S_kv // 16, S_q // 64
+    want = r(4 * B * S_q * Hq) + r(4 * B * n_rb * n_kt) + r(4 * B * n_kt) + r(4 * (B * n_kt + 1)) + \
+        r(8 * B * S_q * min(K, n_kt))
+    assert ws(B, S_q, S_kv, Hq, K) == want
+    assert ws(1, 10, 17, 2, 100) == r(4 * 20) + r(4 * 2) + r(4 * 2) + r(4 * 3) + r(8 * 10 * 2)
+    assert ws(0, 1, 1, 1, 1) == 0 and ws(1, 1, 1, 1, 0) == 0
+    assert ws(1, 1 << 20, 1 << 24, 16, 2048) == 0  # more than 2^31 - 1 segments
+
+
+def _call_backward(B=1, S_q=4, S_kv=32, Hq=2, Hkv=1, D=64, K=2, scale=0.1, ws_bytes=1 << 30, alias_dq_q=False,
+                   null_lse=False):
+    """Every call made with this helper carries one invalid argument (fake pointers never reach a launch)."""
+    L = qsa.lib()
+    sq = (ctypes.c_int64 * 4)(S_q * Hq * D, Hq * D, D, 1)
+    sk = (ctypes.c_int64 * 4)(S_kv * Hkv * D, Hkv * D, D, 1)
+    f = [ctypes.c_void_p(n << 32) for n in range(1, 14)]  # distinct, never dereferenced
+    q, k, v, o, g, lse, lst, cnt, dq, dk, dv, ws = f[:12]
+    if alias_dq_q:
+        dq = q
+    return L.qsa_backward(q, sq, k, sk, v, sk, o, g, sq, None if null_lse else lse, lst, cnt, B, S_q, S_kv, Hq,
+                          Hkv, D, K, scale, dq, dk, dv, ws, ws_bytes, None)
+
+
+def test_backward_host_checks():
+    assert _call_backward(S_q=0) == -2
+    assert _call_backward(Hq=3, Hkv=2) == -4
+    assert _call_backward(D=48) == -5
+    assert _call_backward(scale=float("nan")) == -7
+    assert _call_backward(null_lse=True) == -1
+    assert _call_backward(alias_dq_q=True) == -9
+    assert _call_backward(ws_bytes=16) == -10

@@ -14,7 +14,9 @@ from .generators import (  # noqa: F401
     Workload,
     bf16_bits_to_float32,
     float32_to_bf16_bits,
+    make_dout,
     make_inputs,
     make_qkv,
     make_routes,
+    random_dout,
 )

@@ -119,6 +119,18 @@ def make_qkv(w: Workload):
     return q, k, v
 
 
+def make_dout(w: Workload) -> np.ndarray:
+    """Upstream gradient [B,S_q,Hq,D] for the backward: bfloat16 N(0,1) bits from a fifth stream."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(w.seed, spawn_key=(4,))))
+    return _normal_bf16(rng, (w.B, w.S_q, w.Hq, w.D))
+
+
+def random_dout(seed: int, shape) -> np.ndarray:
+    """bfloat16 N(0,1) bits of the given shape (upstream gradients of the small cases)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return float32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
 # --------------------------------------------------------------------------
 # route recipes
 # --------------------------------------------------------------------------

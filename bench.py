@@ -15,7 +15,13 @@ Prints ONE JSON line (rank 0):
                launch time, measured with HIP events on the launch stream;
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same rows.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With ``--pass backward`` it times the backward instead (one step = one
+qsa_backward call: the dq kernel, the key-segment construction and the dk/dv
+kernel, on the forward's output and log-sum-exp), reporting routed TFLOP/s
+with F = 10*D*Hq*N (scores, dP, dQ, dK, dV on routed pairs) and the
+algorithmic bytes of the whole call against the HBM roofline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass forward|backward]
 """
 
 from __future__ import annotations
@@ -45,6 +51,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -101,6 +108,49 @@ class Plan:
                          i8(self.cnt), B, S_q, w.S_kv, w.Hq, w.Hkv, w.D, K, ctypes.c_float(w.scale),
                          i8(self.out), None, self.stream)
 
+    def setup_backward(self, dev):
+        """Forward with log-sum-exp once, then pre-marshal qsa_backward (dout drawn from its own stream)."""
+        import torch
+
+        import route_sparse_gqa_amd as qsa
+        from workloads import make_dout
+
+        w = self.w
+        B, S_q, K = self.lst.shape
+        i8 = lambda t: ctypes.c_void_p(t.data_ptr())
+        st = lambda t: (ctypes.c_int64 * t.dim())(*t.stride())
+        self.lse = torch.empty((B, S_q, w.Hq), dtype=torch.float32, device=dev)
+        args = list(self.fwd_args)
+        args[-2] = i8(self.lse)
+        rc = self.L.qsa_forward_preprocessed(*args)
+        if rc != 0:
+            raise RuntimeError(f"qsa_forward_preprocessed failed with status {rc}")
+        self.dout = torch.from_numpy(make_dout(w).view(np.int16)).to(dev).view(torch.bfloat16)
+        self.dq = torch.empty_like(self.q)
+        self.dk = torch.empty_like(self.k)
+        self.dv = torch.empty_like(self.v)
+        ws_bytes = qsa.qsa_backward_workspace_size(B, S_q, w.S_kv, w.Hq, w.Hkv, w.D, K)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.bwd_args = (i8(self.q), st(self.q), i8(self.k), st(self.k), i8(self.v), st(self.v), i8(self.out),
+                         i8(self.dout), st(self.dout), i8(self.lse), i8(self.lst), i8(self.cnt), B, S_q, w.S_kv,
+                         w.Hq, w.Hkv, w.D, K, ctypes.c_float(w.scale), i8(self.dq), i8(self.dk), i8(self.dv),
+                         i8(self.ws), ctypes.c_size_t(ws_bytes), self.stream)
+
+    def backward(self):
+        rc = self.L.qsa_backward(*self.bwd_args)
+        if rc != 0:
+            raise RuntimeError(f"qsa_backward failed with status {rc}")
+
+    def segment_count(self) -> int:
+        """Number of (query row, 16-key tile) segments of the last backward (from its workspace)."""
+        w = self.w
+        B, S_q, _ = self.lst.shape
+        r = lambda x: -(-x // 256) * 256
+        n_kt, n_w, n_c = -(-w.S_kv // 16), -(-S_q // 32), -(-S_q // 256)
+        # workspace layout (include/qsa.h): delta, bit matrix, chunk prefixes, totals, tile starts, ...
+        off = r(4 * B * S_q * w.Hq) + r(4 * B * n_w * n_kt) + r(4 * B * n_c * n_kt) + r(4 * B * n_kt) + 4 * (B * n_kt)
+        return int(self.ws[off:off + 4].cpu().numpy().view(np.int32)[0])
+
     def preprocess(self):
         rc = self.L.qsa_preprocess(*self.pre_args)
         if rc != 0:
@@ -119,6 +169,24 @@ def algorithmic_counts(w, N: int):
     qo_bytes = 2 * 2 * rows * w.Hq * w.D         # Q read + O written, bf16
     list_bytes = 4 * N + 4 * rows                # compacted IDs read + counts
     return flops, kv_bytes + qo_bytes + list_bytes
+
+
+def backward_counts(w, N: int, segments: int):
+    """Algorithmic flops and bytes of one qsa_backward call.
+
+    dq kernel: routed K and V rows once per (query row, KV head), Q, dO and O
+    read and dq written, lse read and delta written, lists and counts.  Key
+    segments: the lists walked twice, one 8-byte record written per (row,
+    16-key tile).  dk/dv kernel: K and V read and dK and dV written once per
+    key, and per (segment, KV head) the G query heads' Q and dO rows, lse and
+    delta, and the record."""
+    rows = w.B * w.S_q
+    G = w.Hq // w.Hkv
+    flops = 10 * w.D * w.Hq * N
+    b_dq = 4 * w.D * w.Hkv * N + 4 * 2 * rows * w.Hq * w.D + 2 * 4 * rows * w.Hq + 4 * N + 4 * rows
+    b_seg = 2 * (4 * N + 4 * rows) + 8 * segments
+    b_kv = 8 * w.D * w.Hkv * w.B * w.S_kv + (4 * G * w.D + 8 * G + 8) * w.Hkv * segments
+    return flops, b_dq + b_seg + b_kv
 
 
 def cpu_baseline(w, q, k, v, routes, counts, target_s: float):
@@ -178,6 +246,10 @@ def main():
     counts = plan.cnt.cpu().numpy()
     N = int(counts.sum())
     flops, alg_bytes = algorithmic_counts(w, N)
+
+    if args.which == "backward":
+        run_backward(args, w, plan, dev, N)
+        return
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -248,6 +320,59 @@ def main():
         },
         "kernels_ms": {"preprocess(route_normalize+membership_tiles)": ms_pre, "gather_attention": ms_att},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def run_backward(args, w, plan, dev, N):
+    import torch
+
+    plan.setup_backward(dev)
+    print(f"[bench] backward warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(max(args.warmup, 1)):
+        plan.backward()
+    torch.cuda.synchronize()
+    segments = plan.segment_count()
+    flops, alg_bytes = backward_counts(w, N, segments)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        plan.backward()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "routed-attention backward TFLOP/s (dq, dk, dv; BF16) on 1 MI355X",
+        "value": flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "S_q": w.S_q, "S_kv": w.S_kv, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+            "K": w.K, "routes_N": N, "key_segments": segments,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "qsa_backward (dq_kernel + key segments + dkdv_kernel)",
+            "ms_per_launch": ms,
+            "alg_bytes_per_launch": alg_bytes,
+        },
+        "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)
 

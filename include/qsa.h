@@ -158,13 +158,20 @@ int qsa_forward_preprocessed(const void *q, const int64_t q_strides[4], const vo
 
 /*
  * qsa_backward_workspace_size -- bytes of device workspace qsa_backward
- * needs: delta (4*B*S_q*Hq), the key-segment counters
- * (4*B*ceil(S_q/64)*ceil(S_kv/16)), tile totals and starts
- * (about 8*B*ceil(S_kv/16)) and the segments (8*B*S_q*min(K, ceil(S_kv/16))),
- * each 256-B aligned.  Returns 0 when a size is < 1 or beyond the library's
- * int32 segment indexing (more than 2^31 - 1 segments, counters or tiles).
+ * needs, each part 256-B aligned:
+ *   delta                 4 * B*S_q*Hq
+ *   row x tile bit matrix 4 * B*ceil(S_q/32)*T,  T = ceil(S_kv/16)
+ *   chunk prefixes        4 * B*ceil(S_q/256)*T
+ *   tile totals, starts   about 8 * B*T
+ *   key segments          8 * B*S_q*min(K, T)
+ *   part starts, slots    about 8 * B*T, plus 8 bytes
+ *   partial sums          128*D * Hkv * 2*min(P, ceil(B*S_q*min(K, T)/64)),
+ *                         P = max(1, 16384 / Hkv)  (at most 1 GiB at D = 256)
+ * Returns 0 when a size is < 1 or beyond the library's int32 segment
+ * indexing (more than 2^31 - 1 segments or chunk prefixes).
  */
-size_t qsa_backward_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t K);
+size_t qsa_backward_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D,
+                                   int64_t K);
 
 /*
  * qsa_backward -- first-order gradients of qsa_forward, BF16 in and out,
@@ -188,7 +195,7 @@ size_t qsa_backward_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t
  *   dq            OUT [B, S_q, Hq, D] bf16 contiguous.
  *   dk, dv        OUT [B, S_kv, Hkv, D] bf16 contiguous.
  *   workspace, workspace_bytes   device scratch of at least
- *                 qsa_backward_workspace_size(B, S_q, S_kv, Hq, K) bytes,
+ *                 qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K) bytes,
  *                 256-B aligned (overwritten each call).
  * Outputs and workspace must not overlap each other or any input.
  *

@@ -12,7 +12,7 @@ runs in the library's HIP kernels; there is no other code path.
 * ``qsa_forward(q, k, v, routes, scale=None)``
 * ``qsa_forward_preprocessed(q, k, v, route_list, route_count, scale=None, return_lse=False)``
 * ``qsa_backward(q, k, v, out, dout, lse, route_list, route_count, scale=None)``
-* ``qsa_forward_workspace_size(B, S_q, K)``, ``qsa_backward_workspace_size(B, S_q, S_kv, Hq, K)``
+* ``qsa_forward_workspace_size(B, S_q, K)``, ``qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)``
 * ``qsa_status_string(status)``
 """
 
@@ -72,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.qsa_forward_preprocessed.argtypes = [p, P64, p, P64, p, P64, p, p, i64, i64, i64, i64, i64, i64, i64,
                                                ctypes.c_float, p, p, p]
         L.qsa_forward_preprocessed.restype = i32
-        L.qsa_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+        L.qsa_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64]
         L.qsa_backward_workspace_size.restype = ctypes.c_size_t
         L.qsa_backward.argtypes = [p, P64, p, P64, p, P64, p, p, P64, p, p, p, i64, i64, i64, i64, i64, i64, i64,
                                    ctypes.c_float, p, p, p, p, ctypes.c_size_t, p]
@@ -89,8 +89,8 @@ def qsa_forward_workspace_size(B: int, S_q: int, K: int) -> int:
     return int(lib().qsa_forward_workspace_size(int(B), int(S_q), int(K)))
 
 
-def qsa_backward_workspace_size(B: int, S_q: int, S_kv: int, Hq: int, K: int) -> int:
-    return int(lib().qsa_backward_workspace_size(int(B), int(S_q), int(S_kv), int(Hq), int(K)))
+def qsa_backward_workspace_size(B: int, S_q: int, S_kv: int, Hq: int, Hkv: int, D: int, K: int) -> int:
+    return int(lib().qsa_backward_workspace_size(int(B), int(S_q), int(S_kv), int(Hq), int(Hkv), int(D), int(K)))
 
 
 def _check(status: int, where: str) -> None:
@@ -267,7 +267,7 @@ def qsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
     dq = torch.empty((B, S_q, Hq, D), dtype=torch.bfloat16, device=dev)
     dk = torch.empty((B, S_kv, Hkv, D), dtype=torch.bfloat16, device=dev)
     dv = torch.empty((B, S_kv, Hkv, D), dtype=torch.bfloat16, device=dev)
-    ws_bytes = qsa_backward_workspace_size(B, S_q, S_kv, Hq, K)
+    ws_bytes = qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     st = lib().qsa_backward(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(out),

@@ -21,13 +21,16 @@
 //    every per-head statistic is lane-local), forms dS^T, and accumulates
 //    dQ^T += K^T dS^T with v_mfma_f32_16x16x16_bf16, reading K^T with the
 //    transposing LDS load.  It also writes delta for the second kernel.
-//  * dkdv_kernel: one wavefront per (b, 16-key tile, hk).  The tile's K and
-//    V rows stay in registers as MFMA B operands; the wave walks the tile's
-//    key segments (query rows that route at least one key of the tile, in
-//    ascending row order, each with a 16-bit mask of the keys it routes) in
-//    batches of floor(16 / G) rows whose G heads fill the 16 MFMA rows.  Per
-//    batch it stages Q and dO of those rows in LDS, recomputes S = Q K^T and
-//    dP = dO V^T, and accumulates dV^T += dO^T P and dK^T += Q^T dS.
+//  * dkdv_kernel: one wavefront per (part of a 16-key tile's segment list,
+//    hk).  The tile's K and V rows stay in registers as MFMA B operands; the
+//    wave walks its key segments (query rows that route at least one key of
+//    the tile, in ascending row order, each with a 16-bit mask of the keys
+//    it routes) in batches of floor(16 / G) rows whose G heads fill the 16
+//    MFMA rows.  Per batch it stages Q and dO of those rows in LDS,
+//    recomputes S = Q K^T and dP = dO V^T, and accumulates dV^T += dO^T P
+//    and dK^T += Q^T dS.  A tile whose list was cut into several parts
+//    (popular keys) writes fp32 partial sums, which dkdv_reduce_kernel adds
+//    in part order.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -217,9 +220,10 @@ __global__ void __launch_bounds__(64 * kWaves)
                 const uint16_t* __restrict__ dout, int64_t qs0, int64_t qs1, int64_t qs2, int64_t ks0, int64_t ks1,
                 int64_t ks2, int64_t vs0, int64_t vs1, int64_t vs2, int64_t gs0, int64_t gs1, int64_t gs2,
                 const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ seg_start,
-                const int2* __restrict__ segs, int64_t seg_capacity, int64_t S_q, int64_t S_kv, int64_t Hq,
-                int64_t Hkv, int G, int rows_per_batch, int64_t n_kt, int64_t n_units, float scale_log2e, float scale,
-                uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+                const int2* __restrict__ segs, const int32_t* __restrict__ part_start,
+                const int32_t* __restrict__ slot_start, const int32_t* __restrict__ plan, int64_t S_q, int64_t S_kv,
+                int64_t Hq, int64_t Hkv, int G, int rows_per_batch, int64_t n_kt, int64_t n_tiles, float scale_log2e,
+                float scale, float* __restrict__ partial, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   using Gm = Geo<D>;
   __shared__ __attribute__((aligned(16))) uint16_t qslab[kWaves][kChunk * Gm::kTrStride];
   __shared__ __attribute__((aligned(16))) uint16_t gslab[kWaves][kChunk * Gm::kTrStride];
@@ -228,8 +232,18 @@ __global__ void __launch_bounds__(64 * kWaves)
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t x = blockIdx.x;
   const int64_t hk = x % Hkv;  // one KV head per XCD
-  const int64_t unit = (x / Hkv) * kWaves + wave;  // b * n_kt + tile
-  if (unit >= n_units) return;  // no workgroup barriers in this kernel
+  // Work item: part f of the split (parts are numbered tile by tile).
+  const int32_t f = static_cast<int32_t>((x / Hkv) * kWaves + wave);
+  if (f >= plan[1]) return;  // no workgroup barriers in this kernel
+  int64_t lo = 0, hi = n_tiles;  // the tile u with part_start[u] <= f < part_start[u + 1]
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) / 2;
+    if (part_start[mid] <= f) lo = mid; else hi = mid;
+  }
+  const int64_t unit = lo;  // b * n_kt + tile
+  const int32_t part = f - part_start[unit];
+  const int32_t n_parts = part_start[unit + 1] - part_start[unit];
+  const int32_t part_len = plan[0];
   const int64_t b = unit / n_kt;
   const int64_t key0 = (unit % n_kt) * kChunk;
   const int c = lane & 15;  // key of the tile (N side); col / dim row within a 16-tile
@@ -256,10 +270,9 @@ __global__ void __launch_bounds__(64 * kWaves)
   const uint16_t* qtr = my_q + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
   const uint16_t* gtr = my_g + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
   const int cols = rows_per_batch * G;  // MFMA rows in use: (row slot, head) = (col / G, col % G)
-  // Segment range of this tile (clamped to the buffer: malformed lists can
-  // count more segments than it holds, valid ones cannot).
-  const int32_t s_begin = static_cast<int32_t>(min(static_cast<int64_t>(seg_start[unit]), seg_capacity));
-  const int32_t s_end = static_cast<int32_t>(min(static_cast<int64_t>(seg_start[unit + 1]), seg_capacity));
+  // Segments of this part: at most part_len of the tile's list.
+  const int32_t s_begin = seg_start[unit] + part * part_len;
+  const int32_t s_end = min(seg_start[unit + 1], s_begin + part_len);
   const int64_t q_head0 = hk * G;
 
   for (int32_t sb = s_begin; sb < s_end; sb += rows_per_batch) {
@@ -271,20 +284,24 @@ __global__ void __launch_bounds__(64 * kWaves)
       seg_mask = e.y;
     }
 
-    // Stage Q and dO of the batch's (row, head) columns, one 16-row tile each.
+    // Stage Q, then dO, of the batch's (row, head) columns, one 16-row tile each.
     wave_lds_sync();  // the previous batch's slab reads are complete
 #pragma unroll
-    for (int u = 0; u < Gm::kLoads; ++u) {
-      const int col = u * Gm::kRowsPerLoad + lane / Gm::kLanesPerRow;
-      const int slot = col / G;
-      const int32_t ir = __shfl(seg_row, min(slot, 15));
-      const bool ok = col < cols && sb + slot < s_end;
-      const int64_t h = q_head0 + (ok ? col % G : 0);
-      const int piece = 8 * (lane % Gm::kLanesPerRow);
-      const u32x4 qw = ok ? load16(q + b * qs0 + ir * qs1 + h * qs2 + piece) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 gw = ok ? load16(dout + b * gs0 + ir * gs1 + h * gs2 + piece) : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(my_q + col * Gm::kTrStride + piece) = qw;
-      *reinterpret_cast<u32x4*>(my_g + col * Gm::kTrStride + piece) = gw;
+    for (int m = 0; m < 2; ++m) {
+      const uint16_t* src = m == 0 ? q : dout;
+      const int64_t s0 = m == 0 ? qs0 : gs0, s1 = m == 0 ? qs1 : gs1, s2 = m == 0 ? qs2 : gs2;
+      uint16_t* slab = m == 0 ? my_q : my_g;
+#pragma unroll
+      for (int u = 0; u < Gm::kLoads; ++u) {
+        const int col = u * Gm::kRowsPerLoad + lane / Gm::kLanesPerRow;
+        const int slot = col / G;
+        const int32_t ir = __shfl(seg_row, min(slot, 15));
+        const bool ok = col < cols && sb + slot < s_end;
+        const int64_t h = q_head0 + (ok ? col % G : 0);
+        const int piece = 8 * (lane % Gm::kLanesPerRow);
+        const u32x4 wv = ok ? load16(src + b * s0 + ir * s1 + h * s2 + piece) : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(slab + col * Gm::kTrStride + piece) = wv;
+      }
     }
 
     // Per-column statistics for this lane's columns 4g .. 4g+3 and key c.
@@ -334,7 +351,66 @@ __global__ void __launch_bounds__(64 * kWaves)
     }
   }
 
+  if (n_parts > 1) {
+    // One part of a split tile: fp32 partial sums in the lane-native layout
+    // [slot][hk][dk tiles, dv tiles][lane][4], reduced in part order later.
+    float* dst = partial + ((static_cast<int64_t>(slot_start[unit]) + part) * Hkv + hk) * (2 * Gm::kDimTiles * 256);
+#pragma unroll
+    for (int t = 0; t < Gm::kDimTiles; ++t) {
+      *reinterpret_cast<f32x4*>(dst + (t * 64 + lane) * 4) = acc_k[t];
+      *reinterpret_cast<f32x4*>(dst + ((Gm::kDimTiles + t) * 64 + lane) * 4) = acc_v[t];
+    }
+    return;
+  }
   // Lane (c, g) holds dims 16t + 4g .. +3 of key key0 + c.
+  if (key0 + c < S_kv) {
+    const int64_t off = ((b * S_kv + key0 + c) * Hkv + hk) * D + 4 * g;
+#pragma unroll
+    for (int t = 0; t < Gm::kDimTiles; ++t) {
+      bf16x4 wk, wv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        wk[r] = static_cast<__bf16>(acc_k[t][r] * scale);
+        wv[r] = static_cast<__bf16>(acc_v[t][r]);
+      }
+      *reinterpret_cast<u32x2*>(dk + off + 16 * t) = __builtin_bit_cast(u32x2, wk);
+      *reinterpret_cast<u32x2*>(dv + off + 16 * t) = __builtin_bit_cast(u32x2, wv);
+    }
+  }
+}
+
+// Split tiles: sum the parts' partial sums in part order (a fixed order, so
+// the result is deterministic) and write dk and dv.  One wavefront per
+// (b, tile, hk); tiles that were not split were written by dkdv_kernel.
+template <int D>
+__global__ void __launch_bounds__(64 * kWaves)
+    dkdv_reduce_kernel(const int32_t* __restrict__ part_start, const int32_t* __restrict__ slot_start,
+                       const float* __restrict__ partial, int64_t S_kv, int64_t Hkv, int64_t n_kt, int64_t n_tiles,
+                       float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  using Gm = Geo<D>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t x = blockIdx.x;
+  const int64_t hk = x % Hkv;
+  const int64_t unit = (x / Hkv) * kWaves + wave;
+  if (unit >= n_tiles) return;
+  const int32_t n_parts = part_start[unit + 1] - part_start[unit];
+  if (n_parts <= 1) return;
+  const int64_t b = unit / n_kt;
+  const int64_t key0 = (unit % n_kt) * kChunk;
+  const int c = lane & 15;
+  const int g = lane >> 4;
+  f32x4 acc_k[Gm::kDimTiles], acc_v[Gm::kDimTiles];
+#pragma unroll
+  for (int t = 0; t < Gm::kDimTiles; ++t) acc_k[t] = acc_v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int32_t p = 0; p < n_parts; ++p) {
+    const float* src = partial + ((static_cast<int64_t>(slot_start[unit]) + p) * Hkv + hk) * (2 * Gm::kDimTiles * 256);
+#pragma unroll
+    for (int t = 0; t < Gm::kDimTiles; ++t) {
+      acc_k[t] += *reinterpret_cast<const f32x4*>(src + (t * 64 + lane) * 4);
+      acc_v[t] += *reinterpret_cast<const f32x4*>(src + ((Gm::kDimTiles + t) * 64 + lane) * 4);
+    }
+  }
   if (key0 + c < S_kv) {
     const int64_t off = ((b * S_kv + key0 + c) * Hkv + hk) * D + 4 * g;
 #pragma unroll
@@ -372,14 +448,20 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
 template <int D>
 hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t stream) {
   const int64_t n_kt = (a.S_kv + kChunk - 1) / kChunk;
-  const int64_t units = a.B * n_kt;
-  const int64_t blocks = (units + kWaves - 1) / kWaves * a.Hkv;
+  const int64_t n_tiles = a.B * n_kt;
+  // Parts never exceed n_tiles + max_parts; waves past the planned count exit.
+  const int64_t blocks = (n_tiles + a.max_parts + kWaves - 1) / kWaves * a.Hkv;
   const int G = static_cast<int>(a.Hq / a.Hkv);
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0, stream, a.q, a.k,
                      a.v, a.dout, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0], a.vs[1], a.vs[2],
-                     a.gs[0], a.gs[1], a.gs[2], a.lse, a.delta, a.seg_start, a.segs, a.seg_capacity, a.S_q, a.S_kv, a.Hq,
-                     a.Hkv, G,
-                     kChunk / G, n_kt, units, a.scale * kLog2e, a.scale, a.dk, a.dv);
+                     a.gs[0], a.gs[1], a.gs[2], a.lse, a.delta, a.seg_start, a.segs, a.part_start, a.slot_start,
+                     a.plan, a.S_q, a.S_kv, a.Hq, a.Hkv, G, kChunk / G, n_kt, n_tiles, a.scale * kLog2e, a.scale,
+                     a.partial, a.dk, a.dv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rblocks = (n_tiles + kWaves - 1) / kWaves * a.Hkv;
+  hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3(static_cast<uint32_t>(rblocks)), dim3(64 * kWaves), 0, stream,
+                     a.part_start, a.slot_start, a.partial, a.S_kv, a.Hkv, n_kt, n_tiles, a.scale, a.dk, a.dv);
   return hipGetLastError();
 }
 

@@ -281,43 +281,57 @@ QSA_EXPORT int qsa_forward_preprocessed(const void* q, const int64_t q_strides[4
 
 namespace {
 
-// Backward workspace: delta, then the key-segment buffers, each 256-B aligned.
+// Backward workspace: delta, then the key-segment buffers, then the partial
+// sums of split tiles, each 256-B aligned.
 struct BwdLayout {
-  size_t delta = 0, counters = 0, totals = 0, tile_start = 0, segs = 0, total = 0;
-  int64_t n_kt = 0, capacity = 0;
+  size_t delta = 0, bits = 0, chunk_prefix = 0, totals = 0, tile_start = 0, segs = 0, part_start = 0,
+         slot_start = 0, plan = 0, partial = 0, total = 0;
+  int64_t n_kt = 0, capacity = 0, max_parts = 0;
 };
 
-bool bwd_layout(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t K, BwdLayout* l) {
-  if (B < 1 || S_q < 1 || S_kv < 1 || Hq < 1 || K < 1) return false;
-  int64_t rows = 0, heads = 0, counters = 0, tiles = 0, cap = 0;
-  const int64_t n_rb = (S_q + qsa::kSegRowBlock - 1) / qsa::kSegRowBlock;
+bool bwd_layout(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K, BwdLayout* l) {
+  if (B < 1 || S_q < 1 || S_kv < 1 || Hq < 1 || Hkv < 1 || D < 1 || K < 1) return false;
+  int64_t rows = 0, heads = 0, words = 0, chunks = 0, tiles = 0, cap = 0, partial = 0;
   l->n_kt = (S_kv + qsa::kSegKeyTile - 1) / qsa::kSegKeyTile;
-  if (!mul_ok(B, S_q, &rows) || !mul_ok(rows, Hq, &heads) || !mul_ok(B * n_rb, l->n_kt, &counters) ||
-      !mul_ok(B, l->n_kt, &tiles) || !mul_ok(rows, K < l->n_kt ? K : l->n_kt, &cap))
+  const int64_t W = (S_q + 31) / 32;
+  const int64_t C = (S_q + qsa::kSegChunkRows - 1) / qsa::kSegChunkRows;
+  if (!mul_ok(B, S_q, &rows) || !mul_ok(rows, Hq, &heads) || !mul_ok(B * W, l->n_kt, &words) ||
+      !mul_ok(B * C, l->n_kt, &chunks) || !mul_ok(B, l->n_kt, &tiles) ||
+      !mul_ok(rows, K < l->n_kt ? K : l->n_kt, &cap))
     return false;
-  // segment positions, counters and tile starts are int32
-  if (cap > kMaxGrid || counters > kMaxGrid || tiles + 1 > kMaxGrid || heads > (INT64_MAX >> 3)) return false;
+  // segment positions, chunk prefixes, tile and part starts are int32
+  if (cap > kMaxGrid || chunks > kMaxGrid || tiles + 1 > kMaxGrid / 2 || heads > (INT64_MAX >> 3) ||
+      words > (INT64_MAX >> 3))
+    return false;
   l->capacity = cap;
+  l->max_parts = qsa::kSegPartsTotal / Hkv > 1 ? qsa::kSegPartsTotal / Hkv : 1;
+  const int64_t slots = qsa::seg_max_slots(l->max_parts, cap);
+  if (!mul_ok(slots * Hkv, 128 * D, &partial)) return false;
   size_t off = 0;
-  l->delta = off;
-  off += round_up(static_cast<size_t>(4 * heads), kWorkspaceAlign);
-  l->counters = off;
-  off += round_up(static_cast<size_t>(4 * counters), kWorkspaceAlign);
-  l->totals = off;
-  off += round_up(static_cast<size_t>(4 * tiles), kWorkspaceAlign);
-  l->tile_start = off;
-  off += round_up(static_cast<size_t>(4 * (tiles + 1)), kWorkspaceAlign);
-  l->segs = off;
-  off += round_up(static_cast<size_t>(8 * cap), kWorkspaceAlign);
+  auto take = [&](size_t* at, int64_t bytes) {
+    *at = off;
+    off += round_up(static_cast<size_t>(bytes), kWorkspaceAlign);
+  };
+  take(&l->delta, 4 * heads);
+  take(&l->bits, 4 * words);
+  take(&l->chunk_prefix, 4 * chunks);
+  take(&l->totals, 4 * tiles);
+  take(&l->tile_start, 4 * (tiles + 1));
+  take(&l->segs, 8 * cap);
+  take(&l->part_start, 4 * (tiles + 1));
+  take(&l->slot_start, 4 * tiles);
+  take(&l->plan, 8);
+  take(&l->partial, partial);
   l->total = off;
   return true;
 }
 
 }  // namespace
 
-QSA_EXPORT size_t qsa_backward_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t K) {
+QSA_EXPORT size_t qsa_backward_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv,
+                                              int64_t D, int64_t K) {
   BwdLayout l;
-  return bwd_layout(B, S_q, S_kv, Hq, K, &l) ? l.total : 0;
+  return bwd_layout(B, S_q, S_kv, Hq, Hkv, D, K, &l) ? l.total : 0;
 }
 
 QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
@@ -339,10 +353,12 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
       !aligned(route_count, 4))
     return QSA_ERR_LAYOUT;
   BwdLayout l;
-  if (!bwd_layout(B, S_q, S_kv, Hq, K, &l)) return QSA_ERR_LIMIT;
+  if (!bwd_layout(B, S_q, S_kv, Hq, Hkv, D, K, &l)) return QSA_ERR_LIMIT;
   int64_t kv_elems = 0;
   if (!mul_ok(B * S_kv, Hkv * D, &kv_elems) || kv_elems > (INT64_MAX >> 2)) return QSA_ERR_LIMIT;
-  if ((l.n_kt * B + 3) / 4 * Hkv > kMaxGrid || (B * ((S_q + 63) / 64) + 3) / 4 > kMaxGrid) return QSA_ERR_LIMIT;
+  if ((l.n_kt * B + l.max_parts + 3) / 4 * Hkv > kMaxGrid || (s.rows + 3) / 4 > kMaxGrid ||
+      (B * ((S_q + qsa::kSegChunkRows - 1) / qsa::kSegChunkRows) * l.n_kt + 255) / 256 > kMaxGrid)
+    return QSA_ERR_LIMIT;
   if (workspace == nullptr || workspace_bytes < l.total || !aligned(workspace, kWorkspaceAlign))
     return QSA_ERR_WORKSPACE;
 
@@ -364,11 +380,16 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
 
   char* ws = static_cast<char*>(workspace);
   qsa::SegmentBuffers w;
-  w.counters = reinterpret_cast<int32_t*>(ws + l.counters);
+  w.bits = reinterpret_cast<uint32_t*>(ws + l.bits);
+  w.chunk_prefix = reinterpret_cast<int32_t*>(ws + l.chunk_prefix);
   w.totals = reinterpret_cast<int32_t*>(ws + l.totals);
   w.tile_start = reinterpret_cast<int32_t*>(ws + l.tile_start);
   w.segs = reinterpret_cast<int2*>(ws + l.segs);
   w.capacity = l.capacity;
+  w.part_start = reinterpret_cast<int32_t*>(ws + l.part_start);
+  w.slot_start = reinterpret_cast<int32_t*>(ws + l.slot_start);
+  w.plan = reinterpret_cast<int32_t*>(ws + l.plan);
+  w.max_parts = l.max_parts;
 
   qsa::BwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -386,7 +407,11 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
   a.route_count = route_count;
   a.seg_start = w.tile_start;
   a.segs = w.segs;
-  a.seg_capacity = w.capacity;
+  a.part_start = w.part_start;
+  a.slot_start = w.slot_start;
+  a.plan = w.plan;
+  a.partial = reinterpret_cast<float*>(ws + l.partial);
+  a.max_parts = l.max_parts;
   a.B = B; a.S_q = S_q; a.S_kv = S_kv; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.K = K;
   a.scale = scale;
   a.dq = static_cast<uint16_t*>(dq);

@@ -36,16 +36,24 @@ struct AttnArgs {
 // Fused gather-attention over compacted lists.
 hipError_t launch_gather_attention(const AttnArgs& a, hipStream_t stream);
 
-// Key segments (route lists regrouped by 16-key tile, rows ascending).
-constexpr int64_t kSegKeyTile = 16;   // keys per tile of the key-side backward
-constexpr int64_t kSegRowBlock = 64;  // query rows per counting block
+// Key segments (route lists regrouped by 16-key tile, rows ascending) and
+// their split into parts for the key-side backward kernel.
+constexpr int64_t kSegKeyTile = 16;     // keys per tile of the key-side backward
+constexpr int64_t kSegChunkRows = 256;  // query rows per popcount-prefix chunk
+constexpr int64_t kSegMinPart = 64;     // smallest part length (segments)
+constexpr int64_t kSegPartsTotal = 16384;  // target parts over all KV heads
 
 struct SegmentBuffers {
-  int32_t* counters;    // [B * ceil(S_q / 64) * n_kt]
-  int32_t* totals;      // [B * n_kt]
-  int32_t* tile_start;  // [B * n_kt + 1]: segments of (b, t) are [start[b*n_kt+t], start[b*n_kt+t+1])
-  int2* segs;           // [capacity] {query row within the batch, key mask}
+  uint32_t* bits;         // [B][ceil(S_q/32)][n_kt] one bit per (query row, tile)
+  int32_t* chunk_prefix;  // [B][ceil(S_q/256)][n_kt]
+  int32_t* totals;        // [B * n_kt]
+  int32_t* tile_start;    // [B * n_kt + 1]: segments of (b, t) are [start[b*n_kt+t], start[b*n_kt+t+1])
+  int2* segs;             // [capacity] {query row within the batch, key mask}
   int64_t capacity;
+  int32_t* part_start;    // [B * n_kt + 1]
+  int32_t* slot_start;    // [B * n_kt]
+  int32_t* plan;          // [2]: part length, number of parts
+  int64_t max_parts;      // parts per KV head the split aims at
 };
 
 hipError_t launch_key_segments(const int32_t* route_list, const int32_t* route_count, int64_t B, int64_t S_q,
@@ -62,9 +70,13 @@ struct BwdArgs {
   float* delta;          // [B * S_q * Hq] <dout, out>, written by the dq pass
   const int32_t* route_list;
   const int32_t* route_count;
-  const int32_t* seg_start;
+  const int32_t* seg_start;   // tile_start of the key segments
   const int2* segs;
-  int64_t seg_capacity;
+  const int32_t* part_start;
+  const int32_t* slot_start;
+  const int32_t* plan;
+  float* partial;             // [slots][Hkv][2][D/16][64][4] fp32 partial sums of split tiles
+  int64_t max_parts;
   int64_t B, S_q, S_kv, Hq, Hkv, D, K;
   float scale;
   uint16_t* dq;  // [B, S_q, Hq, D] contiguous
@@ -76,5 +88,11 @@ struct BwdArgs {
 // per (b, 16-key tile, hk)) over the key segments.
 hipError_t launch_attention_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_attention_dkdv(const BwdArgs& a, hipStream_t stream);
+
+// Upper bound of the partial-sum slots the split can use, per KV head.
+inline int64_t seg_max_slots(int64_t max_parts, int64_t capacity) {
+  const int64_t by_capacity = (capacity + kSegMinPart - 1) / kSegMinPart;
+  return 2 * (max_parts < by_capacity ? max_parts : by_capacity);
+}
 
 }  // namespace qsa

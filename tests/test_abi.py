@@ -93,17 +93,25 @@ def test_other_host_checks():
     assert L.qsa_preprocess(None, 1, 1, 2, 3, s3, 5, fake, fake, None, None, None) == -1
 
 
+def _bwd_ws(B, S_q, S_kv, Hq, Hkv, D, K):
+    """The layout the header documents, from its formula."""
+    r = lambda x: -(-x // 256) * 256
+    T, n_w, n_c = -(-S_kv // 16), -(-S_q // 32), -(-S_q // 256)
+    cap = B * S_q * min(K, T)
+    P = max(1, 16384 // Hkv)
+    slots = 2 * min(P, -(-cap // 64))
+    return (r(4 * B * S_q * Hq) + r(4 * B * n_w * T) + r(4 * B * n_c * T) + r(4 * B * T) + r(4 * (B * T + 1)) +
+            r(8 * cap) + r(4 * (B * T + 1)) + r(4 * B * T) + r(8) + r(128 * D * Hkv * slots))
+
+
 def test_backward_workspace_size():
     ws = qsa.qsa_backward_workspace_size
-    r = lambda x: -(-x // 256) * 256
-    B, S_q, S_kv, Hq, K = 2, 4096, 4096, 16, 512
-    n_kt, n_rb = S_kv // 16, S_q // 64
-    want = r(4 * B * S_q * Hq) + r(4 * B * n_rb * n_kt) + r(4 * B * n_kt) + r(4 * (B * n_kt + 1)) + \
-        r(8 * B * S_q * min(K, n_kt))
-    assert ws(B, S_q, S_kv, Hq, K) == want
-    assert ws(1, 10, 17, 2, 100) == r(4 * 20) + r(4 * 2) + r(4 * 2) + r(4 * 3) + r(8 * 10 * 2)
-    assert ws(0, 1, 1, 1, 1) == 0 and ws(1, 1, 1, 1, 0) == 0
-    assert ws(1, 1 << 20, 1 << 24, 16, 2048) == 0  # more than 2^31 - 1 segments
+    for args in [(2, 4096, 4096, 16, 2, 256, 512), (1, 10, 17, 2, 1, 64, 100), (1, 65536, 65536, 16, 2, 256, 2048),
+                 (3, 257, 513, 8, 1, 128, 129)]:
+        assert ws(*args) == _bwd_ws(*args), args
+    assert ws(1, 65536, 65536, 16, 2, 256, 2048) < 3 << 30  # long sequences fit in a few GiB
+    assert ws(0, 1, 1, 1, 1, 64, 1) == 0 and ws(1, 1, 1, 1, 1, 64, 0) == 0
+    assert ws(1, 1 << 20, 1 << 24, 16, 2, 256, 2048) == 0  # more than 2^31 - 1 segments
 
 
 def _call_backward(B=1, S_q=4, S_kv=32, Hq=2, Hkv=1, D=64, K=2, scale=0.1, ws_bytes=1 << 30, alias_dq_q=False,

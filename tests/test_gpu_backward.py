@@ -91,8 +91,9 @@ def _r256(x):
 
 def read_segments(ws: torch.Tensor, B, S_q, S_kv, Hq):
     """tile_start and segments from the documented workspace layout."""
-    n_kt, n_rb = -(-S_kv // 16), -(-S_q // 64)
-    off = _r256(4 * B * S_q * Hq) + _r256(4 * B * n_rb * n_kt) + _r256(4 * B * n_kt)
+    n_kt, n_w, n_c = -(-S_kv // 16), -(-S_q // 32), -(-S_q // 256)
+    # delta, bit matrix, chunk prefixes, tile totals, then tile starts and segments
+    off = _r256(4 * B * S_q * Hq) + _r256(4 * B * n_w * n_kt) + _r256(4 * B * n_c * n_kt) + _r256(4 * B * n_kt)
     w = ws.cpu().numpy()
     start = w[off:off + 4 * (B * n_kt + 1)].view(np.int32)
     off += _r256(4 * (B * n_kt + 1))
@@ -124,7 +125,8 @@ def test_backward_matches_oracle(case):
     q, k, v, r = random_small_case(3000 + sum(case), B, S_q, S_kv, Hq, Hkv, D, K)
     dout = random_dout(4000 + sum(case), q.shape)
     scale = 1.0 / math.sqrt(D)
-    ws = torch.empty(qsa.qsa_backward_workspace_size(B, S_q, S_kv, Hq, K), dtype=torch.uint8, device=device())
+    ws = torch.empty(qsa.qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K), dtype=torch.uint8,
+                     device=device())
     (qg, kg, vg, gg, lst, cnt, out, lse), (dq, dk, dv) = run_forward_backward(q, k, v, r, dout, scale, ws)
     torch.cuda.synchronize()
 

@@ -142,11 +142,11 @@ class Plan:
             raise RuntimeError(f"qsa_backward failed with status {rc}")
 
     def segment_count(self) -> int:
-        """Number of (query row, 16-key tile) segments of the last backward (from its workspace)."""
+        """Number of (query row, 64-key tile) segments of the last backward (from its workspace)."""
         w = self.w
         B, S_q, _ = self.lst.shape
         r = lambda x: -(-x // 256) * 256
-        n_kt, n_w, n_c = -(-w.S_kv // 16), -(-S_q // 32), -(-S_q // 256)
+        n_kt, n_w, n_c = -(-w.S_kv // 64), -(-S_q // 32), -(-S_q // 256)
         # workspace layout (include/qsa.h): delta, bit matrix, chunk prefixes, totals, tile starts, ...
         off = r(4 * B * S_q * w.Hq) + r(4 * B * n_w * n_kt) + r(4 * B * n_c * n_kt) + r(4 * B * n_kt) + 4 * (B * n_kt)
         return int(self.ws[off:off + 4].cpu().numpy().view(np.int32)[0])
@@ -176,16 +176,16 @@ def backward_counts(w, N: int, segments: int):
 
     dq kernel: routed K and V rows once per (query row, KV head), Q, dO and O
     read and dq written, lse read and delta written, lists and counts.  Key
-    segments: the lists walked twice, one 8-byte record written per (row,
-    16-key tile).  dk/dv kernel: K and V read and dK and dV written once per
+    segments: the lists walked twice, one 16-byte record written per (row,
+    64-key tile).  dk/dv kernel: K and V read and dK and dV written once per
     key, and per (segment, KV head) the G query heads' Q and dO rows, lse and
     delta, and the record."""
     rows = w.B * w.S_q
     G = w.Hq // w.Hkv
     flops = 10 * w.D * w.Hq * N
     b_dq = 4 * w.D * w.Hkv * N + 4 * 2 * rows * w.Hq * w.D + 2 * 4 * rows * w.Hq + 4 * N + 4 * rows
-    b_seg = 2 * (4 * N + 4 * rows) + 8 * segments
-    b_kv = 8 * w.D * w.Hkv * w.B * w.S_kv + (4 * G * w.D + 8 * G + 8) * w.Hkv * segments
+    b_seg = 2 * (4 * N + 4 * rows) + 16 * segments
+    b_kv = 8 * w.D * w.Hkv * w.B * w.S_kv + (4 * G * w.D + 8 * G + 16) * w.Hkv * segments
     return flops, b_dq + b_seg + b_kv
 
 

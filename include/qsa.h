@@ -160,13 +160,13 @@ int qsa_forward_preprocessed(const void *q, const int64_t q_strides[4], const vo
  * qsa_backward_workspace_size -- bytes of device workspace qsa_backward
  * needs, each part 256-B aligned:
  *   delta                 4 * B*S_q*Hq
- *   row x tile bit matrix 4 * B*ceil(S_q/32)*T,  T = ceil(S_kv/16)
+ *   row x tile bit matrix 4 * B*ceil(S_q/32)*T,  T = ceil(S_kv/64)
  *   chunk prefixes        4 * B*ceil(S_q/256)*T
  *   tile totals, starts   about 8 * B*T
- *   key segments          8 * B*S_q*min(K, T)
+ *   key segments          16 * B*S_q*min(K, T)
  *   part starts, slots    about 8 * B*T, plus 8 bytes
- *   partial sums          128*D * Hkv * 2*min(P, ceil(B*S_q*min(K, T)/64)),
- *                         P = max(1, 16384 / Hkv)  (at most 1 GiB at D = 256)
+ *   partial sums          512*D * Hkv * 2*min(P, ceil(B*S_q*min(K, T)/64)),
+ *                         P = max(1, 4096 / Hkv)  (at most 1 GiB at D = 256)
  * Returns 0 when a size is < 1 or beyond the library's int32 segment
  * indexing (more than 2^31 - 1 segments or chunk prefixes).
  */

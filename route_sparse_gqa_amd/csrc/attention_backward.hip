@@ -21,16 +21,19 @@
 //    every per-head statistic is lane-local), forms dS^T, and accumulates
 //    dQ^T += K^T dS^T with v_mfma_f32_16x16x16_bf16, reading K^T with the
 //    transposing LDS load.  It also writes delta for the second kernel.
-//  * dkdv_kernel: one wavefront per (part of a 16-key tile's segment list,
-//    hk).  The tile's K and V rows stay in registers as MFMA B operands; the
-//    wave walks its key segments (query rows that route at least one key of
-//    the tile, in ascending row order, each with a 16-bit mask of the keys
-//    it routes) in batches of floor(16 / G) rows whose G heads fill the 16
-//    MFMA rows.  Per batch it stages Q and dO of those rows in LDS,
-//    recomputes S = Q K^T and dP = dO V^T, and accumulates dV^T += dO^T P
-//    and dK^T += Q^T dS.  A tile whose list was cut into several parts
-//    (popular keys) writes fp32 partial sums, which dkdv_reduce_kernel adds
-//    in part order.
+//  * dkdv_kernel: one workgroup per (part of a 64-key tile's segment list,
+//    hk); wave w owns keys 16w .. 16w+15 of the tile, whose K and V rows
+//    stay in registers as MFMA B operands.  The workgroup walks its key
+//    segments (query rows that route at least one key of the tile, in
+//    ascending row order, each with a 64-bit mask of the keys it routes) in
+//    batches of floor(16 / G) rows whose G heads fill the 16 MFMA rows.  Per
+//    batch the workgroup stages Q and dO of those rows once in LDS for all
+//    four waves (double-buffered: the next batch's loads are in flight while
+//    this one is computed); each wave recomputes S = Q K^T and dP = dO V^T
+//    for its keys and accumulates dV^T += dO^T P and dK^T += Q^T dS, or
+//    skips the batch when it routes none of them.  A tile whose list was cut
+//    into several parts (popular keys) writes fp32 partial sums, which
+//    dkdv_reduce_kernel adds in part order.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -220,36 +223,45 @@ __global__ void __launch_bounds__(64 * kWaves)
                 const uint16_t* __restrict__ dout, int64_t qs0, int64_t qs1, int64_t qs2, int64_t ks0, int64_t ks1,
                 int64_t ks2, int64_t vs0, int64_t vs1, int64_t vs2, int64_t gs0, int64_t gs1, int64_t gs2,
                 const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ seg_start,
-                const int2* __restrict__ segs, const int32_t* __restrict__ part_start,
+                const int4* __restrict__ segs, const int32_t* __restrict__ part_start,
                 const int32_t* __restrict__ slot_start, const int32_t* __restrict__ plan, int64_t S_q, int64_t S_kv,
                 int64_t Hq, int64_t Hkv, int G, int rows_per_batch, int64_t n_kt, int64_t n_tiles, float scale_log2e,
                 float scale, float* __restrict__ partial, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   using Gm = Geo<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t qslab[kWaves][kChunk * Gm::kTrStride];
-  __shared__ __attribute__((aligned(16))) uint16_t gslab[kWaves][kChunk * Gm::kTrStride];
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kPieces = 2 * kChunk * Gm::kLanesPerRow;  // 16-byte pieces of Q and dO per batch
+  constexpr int kPer = kPieces / kThreads;                  // per thread
+  static_assert(kPer * kThreads == kPieces, "staging must split evenly over the workgroup");
+  // Double-buffered staging of one batch: Q and dO of its 16 (row, head)
+  // columns, and per column (lse2, delta) and the 64-bit key mask.
+  __shared__ __attribute__((aligned(16))) uint16_t slab[2][2][kChunk * Gm::kTrStride];
+  __shared__ float2 stat[2][kChunk];
+  __shared__ uint2 cmask[2][kChunk];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t x = blockIdx.x;
   const int64_t hk = x % Hkv;  // one KV head per XCD
-  // Work item: part f of the split (parts are numbered tile by tile).
-  const int32_t f = static_cast<int32_t>((x / Hkv) * kWaves + wave);
-  if (f >= plan[1]) return;  // no workgroup barriers in this kernel
+  // Work item of this workgroup: part f of the split (parts numbered tile by tile).
+  const int32_t f = static_cast<int32_t>(x / Hkv);
+  if (f >= plan[1]) return;  // uniform over the workgroup
   int64_t lo = 0, hi = n_tiles;  // the tile u with part_start[u] <= f < part_start[u + 1]
   while (hi - lo > 1) {
     const int64_t mid = (lo + hi) / 2;
     if (part_start[mid] <= f) lo = mid; else hi = mid;
   }
-  const int64_t unit = lo;  // b * n_kt + tile
+  const int64_t unit = lo;  // b * n_kt + 64-key tile
   const int32_t part = f - part_start[unit];
   const int32_t n_parts = part_start[unit + 1] - part_start[unit];
   const int32_t part_len = plan[0];
   const int64_t b = unit / n_kt;
-  const int64_t key0 = (unit % n_kt) * kChunk;
-  const int c = lane & 15;  // key of the tile (N side); col / dim row within a 16-tile
+  const int kbit = 16 * wave + (lane & 15);         // this lane's key within the 64-key tile
+  const int64_t key0 = (unit % n_kt) * 64 + 16 * wave;  // this wave's first key
+  const int c = lane & 15;  // key (N side); col / dim row within a 16-tile
   const int g = lane >> 4;
 
-  // K and V of the tile as B operands: lane (c, g) holds key c, dims 32s + 8g .. +7.
+  // K and V of the wave's 16 keys as B operands: lane (c, g) holds key c, dims 32s + 8g .. +7.
   bf16x8 kf[Gm::kSteps], vf[Gm::kSteps];
   {
     const int64_t key = min(key0 + c, S_kv - 1);
@@ -265,96 +277,129 @@ __global__ void __launch_bounds__(64 * kWaves)
 #pragma unroll
   for (int t = 0; t < Gm::kDimTiles; ++t) acc_k[t] = acc_v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint16_t* my_q = qslab[wave];
-  uint16_t* my_g = gslab[wave];
-  const uint16_t* qtr = my_q + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
-  const uint16_t* gtr = my_g + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
   const int cols = rows_per_batch * G;  // MFMA rows in use: (row slot, head) = (col / G, col % G)
-  // Segments of this part: at most part_len of the tile's list.
   const int32_t s_begin = seg_start[unit] + part * part_len;
   const int32_t s_end = min(seg_start[unit + 1], s_begin + part_len);
+  const int32_t n_batches = (s_end - s_begin + rows_per_batch - 1) / rows_per_batch;
   const int64_t q_head0 = hk * G;
+  const int32_t row_max = static_cast<int32_t>(S_q - 1);
 
-  for (int32_t sb = s_begin; sb < s_end; sb += rows_per_batch) {
-    // Lane r < rows_per_batch holds segment sb + r: its query row and key mask.
-    int32_t seg_row = 0, seg_mask = 0;
-    if (lane < rows_per_batch && sb + lane < s_end) {
-      const int2 e = segs[sb + lane];
-      seg_row = min(max(e.x, 0), static_cast<int32_t>(S_q - 1));
-      seg_mask = e.y;
+  // Batch staging, in two halves so the loads of batch i + 1 overlap the
+  // MFMAs of batch i: fetch() issues the global loads into registers,
+  // stash() writes them to one LDS buffer.
+  u32x4 pre[kPer];
+  float2 pre_stat = {0.f, 0.f};
+  uint2 pre_mask = {0u, 0u};
+  auto fetch = [&](int32_t sb) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int pc = tid + kThreads * u;
+      const int m = pc / (kChunk * Gm::kLanesPerRow);  // 0: Q, 1: dO
+      const int col = (pc / Gm::kLanesPerRow) % kChunk;
+      const int piece = 8 * (pc % Gm::kLanesPerRow);
+      const int slot = col / G;
+      const bool ok = col < cols && sb + slot < s_end;
+      const int32_t ir = ok ? min(max(segs[sb + slot].x, 0), row_max) : 0;
+      const int64_t h = q_head0 + (ok ? col % G : 0);
+      const uint16_t* src = m == 0 ? q + b * qs0 + ir * qs1 + h * qs2 : dout + b * gs0 + ir * gs1 + h * gs2;
+      pre[u] = ok ? load16(src + piece) : u32x4{0u, 0u, 0u, 0u};
     }
-
-    // Stage Q, then dO, of the batch's (row, head) columns, one 16-row tile each.
-    wave_lds_sync();  // the previous batch's slab reads are complete
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const uint16_t* src = m == 0 ? q : dout;
-      const int64_t s0 = m == 0 ? qs0 : gs0, s1 = m == 0 ? qs1 : gs1, s2 = m == 0 ? qs2 : gs2;
-      uint16_t* slab = m == 0 ? my_q : my_g;
-#pragma unroll
-      for (int u = 0; u < Gm::kLoads; ++u) {
-        const int col = u * Gm::kRowsPerLoad + lane / Gm::kLanesPerRow;
-        const int slot = col / G;
-        const int32_t ir = __shfl(seg_row, min(slot, 15));
-        const bool ok = col < cols && sb + slot < s_end;
-        const int64_t h = q_head0 + (ok ? col % G : 0);
-        const int piece = 8 * (lane % Gm::kLanesPerRow);
-        const u32x4 wv = ok ? load16(src + b * s0 + ir * s1 + h * s2 + piece) : u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(slab + col * Gm::kTrStride + piece) = wv;
+    if (tid < kChunk) {
+      const int col = tid;
+      const int slot = col / G;
+      const bool ok = col < cols && sb + slot < s_end;
+      if (ok) {
+        const int4 e = segs[sb + slot];
+        const int64_t idx = (b * S_q + min(max(e.x, 0), row_max)) * Hq + q_head0 + col % G;
+        pre_stat = float2{lse[idx] * kLog2e, delta[idx]};
+        pre_mask = uint2{static_cast<uint32_t>(e.y), static_cast<uint32_t>(e.z)};
+      } else {
+        pre_stat = float2{0.f, 0.f};
+        pre_mask = uint2{0u, 0u};
       }
     }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int pc = tid + kThreads * u;
+      const int m = pc / (kChunk * Gm::kLanesPerRow);
+      const int col = (pc / Gm::kLanesPerRow) % kChunk;
+      const int piece = 8 * (pc % Gm::kLanesPerRow);
+      *reinterpret_cast<u32x4*>(&slab[buf][m][col * Gm::kTrStride + piece]) = pre[u];
+    }
+    if (tid < kChunk) {
+      stat[buf][tid] = pre_stat;
+      cmask[buf][tid] = pre_mask;
+    }
+  };
+
+  if (n_batches > 0) {
+    fetch(s_begin);
+    stash(0);
+  }
+  __syncthreads();
+  for (int32_t bi = 0; bi < n_batches; ++bi) {
+    const int cur = bi & 1;
+    const bool more = bi + 1 < n_batches;  // uniform over the workgroup
+    if (more) fetch(s_begin + (bi + 1) * rows_per_batch);
 
     // Per-column statistics for this lane's columns 4g .. 4g+3 and key c.
     float lse2[4], dl[4];
     bool on[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int col = 4 * g + r;
-      const int slot = col / G;
-      const int32_t ir = __shfl(seg_row, min(slot, 15));
-      const int32_t m = __shfl(seg_mask, min(slot, 15));
-      const bool ok = col < cols && sb + slot < s_end;
-      const int64_t idx = (b * S_q + ir) * Hq + q_head0 + (ok ? col % G : 0);
-      lse2[r] = ok ? lse[idx] * kLog2e : 0.f;
-      dl[r] = ok ? delta[idx] : 0.f;
-      on[r] = ok && ((m >> c) & 1) != 0;
+      const float2 st2 = stat[cur][4 * g + r];
+      const uint2 mk = cmask[cur][4 * g + r];
+      lse2[r] = st2.x;
+      dl[r] = st2.y;
+      on[r] = ((kbit < 32 ? mk.x >> kbit : mk.y >> (kbit - 32)) & 1u) != 0;
     }
-    wave_lds_sync();  // staged columns visible to the whole wave
-
-    // S[col 4g + r][key c] = Q K^T and dP = dO V^T; A operands are slab rows
-    // (col c, dims 32s + 8g .. +7).
-    f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* qa = my_q + c * Gm::kTrStride + 8 * g;
-    const uint16_t* ga = my_g + c * Gm::kTrStride + 8 * g;
+    // Waves whose 16 keys no row of the batch routes skip the products.
+    if (__ballot(on[0] || on[1] || on[2] || on[3])) {
+      const uint16_t* my_q = slab[cur][0];
+      const uint16_t* my_g = slab[cur][1];
+      // S[col 4g + r][key c] = Q K^T and dP = dO V^T; A operands are slab rows
+      // (col c, dims 32s + 8g .. +7).
+      f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* qa = my_q + c * Gm::kTrStride + 8 * g;
+      const uint16_t* ga = my_g + c * Gm::kTrStride + 8 * g;
 #pragma unroll
-    for (int s = 0; s < Gm::kSteps; ++s) {
-      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(qa + 32 * s)), kf[s], st, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(ga + 32 * s)), vf[s], dp, 0, 0, 0);
+      for (int s = 0; s < Gm::kSteps; ++s) {
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(qa + 32 * s)), kf[s], st, 0, 0,
+                                                     0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(ga + 32 * s)), vf[s], dp, 0, 0,
+                                                     0);
+      }
+      bf16x4 pb, dsb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = on[r] ? exp2f(st[r] * scale_log2e - lse2[r]) : 0.f;
+        pb[r] = static_cast<__bf16>(p);
+        dsb[r] = static_cast<__bf16>(p * (dp[r] - dl[r]));
+      }
+      const i16x4 pi = __builtin_bit_cast(i16x4, pb);
+      const i16x4 di = __builtin_bit_cast(i16x4, dsb);
+      // dV^T += dO^T P and dK^T += Q^T dS: the transposed reads give lane (c, g)
+      // columns 4g .. 4g+3 of dim 16t + c, matching its four P / dS values.
+      const uint16_t* qtr = my_q + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
+      const uint16_t* gtr = my_g + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
+#pragma unroll
+      for (int t = 0; t < Gm::kDimTiles; ++t) {
+        acc_v[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(gtr + 16 * t), pi, acc_v[t], 0, 0, 0);
+        acc_k[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(qtr + 16 * t), di, acc_k[t], 0, 0, 0);
+      }
     }
 
-    bf16x4 pb, dsb;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = on[r] ? exp2f(st[r] * scale_log2e - lse2[r]) : 0.f;
-      pb[r] = static_cast<__bf16>(p);
-      dsb[r] = static_cast<__bf16>(p * (dp[r] - dl[r]));
-    }
-    const i16x4 pi = __builtin_bit_cast(i16x4, pb);
-    const i16x4 di = __builtin_bit_cast(i16x4, dsb);
-
-    // dV^T += dO^T P and dK^T += Q^T dS: the transposed reads give lane (c, g)
-    // columns 4g .. 4g+3 of dim 16t + c, matching its four P / dS values.
-#pragma unroll
-    for (int t = 0; t < Gm::kDimTiles; ++t) {
-      acc_v[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(gtr + 16 * t), pi, acc_v[t], 0, 0, 0);
-      acc_k[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(qtr + 16 * t), di, acc_k[t], 0, 0, 0);
-    }
+    if (more) stash(cur ^ 1);  // the other buffer was last read before the previous barrier
+    __syncthreads();
   }
 
   if (n_parts > 1) {
     // One part of a split tile: fp32 partial sums in the lane-native layout
-    // [slot][hk][dk tiles, dv tiles][lane][4], reduced in part order later.
-    float* dst = partial + ((static_cast<int64_t>(slot_start[unit]) + part) * Hkv + hk) * (2 * Gm::kDimTiles * 256);
+    // [slot][hk][wave][dk tiles, dv tiles][lane][4], reduced in part order later.
+    float* dst = partial + (((static_cast<int64_t>(slot_start[unit]) + part) * Hkv + hk) * kWaves + wave) *
+                               (2 * Gm::kDimTiles * 256);
 #pragma unroll
     for (int t = 0; t < Gm::kDimTiles; ++t) {
       *reinterpret_cast<f32x4*>(dst + (t * 64 + lane) * 4) = acc_k[t];
@@ -380,8 +425,9 @@ __global__ void __launch_bounds__(64 * kWaves)
 }
 
 // Split tiles: sum the parts' partial sums in part order (a fixed order, so
-// the result is deterministic) and write dk and dv.  One wavefront per
-// (b, tile, hk); tiles that were not split were written by dkdv_kernel.
+// the result is deterministic) and write dk and dv.  One workgroup per
+// (b, 64-key tile, hk), wave w for keys 16w .. 16w+15; tiles that were not
+// split were written by dkdv_kernel.
 template <int D>
 __global__ void __launch_bounds__(64 * kWaves)
     dkdv_reduce_kernel(const int32_t* __restrict__ part_start, const int32_t* __restrict__ slot_start,
@@ -392,19 +438,20 @@ __global__ void __launch_bounds__(64 * kWaves)
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t x = blockIdx.x;
   const int64_t hk = x % Hkv;
-  const int64_t unit = (x / Hkv) * kWaves + wave;
+  const int64_t unit = x / Hkv;
   if (unit >= n_tiles) return;
   const int32_t n_parts = part_start[unit + 1] - part_start[unit];
   if (n_parts <= 1) return;
   const int64_t b = unit / n_kt;
-  const int64_t key0 = (unit % n_kt) * kChunk;
+  const int64_t key0 = (unit % n_kt) * 64 + 16 * wave;
   const int c = lane & 15;
   const int g = lane >> 4;
   f32x4 acc_k[Gm::kDimTiles], acc_v[Gm::kDimTiles];
 #pragma unroll
   for (int t = 0; t < Gm::kDimTiles; ++t) acc_k[t] = acc_v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int32_t p = 0; p < n_parts; ++p) {
-    const float* src = partial + ((static_cast<int64_t>(slot_start[unit]) + p) * Hkv + hk) * (2 * Gm::kDimTiles * 256);
+    const float* src = partial + (((static_cast<int64_t>(slot_start[unit]) + p) * Hkv + hk) * kWaves + wave) *
+                                     (2 * Gm::kDimTiles * 256);
 #pragma unroll
     for (int t = 0; t < Gm::kDimTiles; ++t) {
       acc_k[t] += *reinterpret_cast<const f32x4*>(src + (t * 64 + lane) * 4);
@@ -447,10 +494,10 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t stream) {
-  const int64_t n_kt = (a.S_kv + kChunk - 1) / kChunk;
+  const int64_t n_kt = (a.S_kv + 63) / 64;
   const int64_t n_tiles = a.B * n_kt;
-  // Parts never exceed n_tiles + max_parts; waves past the planned count exit.
-  const int64_t blocks = (n_tiles + a.max_parts + kWaves - 1) / kWaves * a.Hkv;
+  // Parts never exceed n_tiles + max_parts; workgroups past the planned count exit.
+  const int64_t blocks = (n_tiles + a.max_parts) * a.Hkv;
   const int G = static_cast<int>(a.Hq / a.Hkv);
   hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0, stream, a.q, a.k,
                      a.v, a.dout, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0], a.vs[1], a.vs[2],
@@ -459,9 +506,8 @@ hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t stream) {
                      a.partial, a.dk, a.dv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t rblocks = (n_tiles + kWaves - 1) / kWaves * a.Hkv;
-  hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3(static_cast<uint32_t>(rblocks)), dim3(64 * kWaves), 0, stream,
-                     a.part_start, a.slot_start, a.partial, a.S_kv, a.Hkv, n_kt, n_tiles, a.scale, a.dk, a.dv);
+  hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3(static_cast<uint32_t>(n_tiles * a.Hkv)), dim3(64 * kWaves), 0,
+                     stream, a.part_start, a.slot_start, a.partial, a.S_kv, a.Hkv, n_kt, n_tiles, a.scale, a.dk, a.dv);
   return hipGetLastError();
 }
 

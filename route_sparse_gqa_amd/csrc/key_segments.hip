@@ -1,12 +1,12 @@
-// Key segments: the compacted route lists regrouped by 16-key tile, for the
+// Key segments: the compacted route lists regrouped by 64-key tile, for the
 // key-side backward kernel, and the split of each tile's segments into
 // bounded parts.
 //
 // The backward's dk and dv sums run over every query row that routes a key
 // (fa4_qsa page: first-order autograd of the routed attention).  A segment
-// is one (query row, 16-key tile) pair in which the row routes at least one
-// key of the tile; it is stored as {row, mask}, bit c of the mask set iff the
-// row routes key 16 * tile + c.  The segments of a (batch, tile) are
+// is one (query row, 64-key tile) pair in which the row routes at least one
+// key of the tile; it is stored as {row, mask lo, mask hi, 0}, bit c of the
+// 64-bit mask set iff the row routes key 64 * tile + c.  The segments of a (batch, tile) are
 // contiguous and in ascending row order, so the key-side sums have a fixed
 // order and the backward is deterministic.
 //
@@ -24,7 +24,9 @@
 //      segment, the grand total at the end;
 //   6. one wavefront per row places each of its segments at
 //      tile start + chunk prefix + popcounts of the earlier rows of its chunk,
-//      i.e. at its rank among the rows that touch the tile;
+//      i.e. at its rank among the rows that touch the tile; the key mask of a
+//      run of list entries in one tile is a segmented OR-scan across the
+//      wavefront's lanes, carried from one 64-entry chunk to the next;
 //   7. parts: each tile's segment list is cut into parts of at most L
 //      segments, L = max(64, ceil(total / max_parts)), so that no wavefront
 //      of the key-side kernel carries a popular tile alone; tiles cut into
@@ -50,6 +52,18 @@ __global__ void __launch_bounds__(256) zero_kernel(uint32_t* __restrict__ p, int
     p[idx] = 0u;
 }
 
+__device__ __forceinline__ uint64_t shfl_up64(uint64_t x, int d) {
+  const uint32_t lo = __shfl_up(static_cast<uint32_t>(x), d);
+  const uint32_t hi = __shfl_up(static_cast<uint32_t>(x >> 32), d);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shfl64(uint64_t x, int src) {
+  const uint32_t lo = __shfl(static_cast<uint32_t>(x), src);
+  const uint32_t hi = __shfl(static_cast<uint32_t>(x >> 32), src);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // One wavefront per query row.  At the last list entry of each tile run it
 // marks the (row, tile) bit (kFill false) or writes the segment at its rank
 // (kFill true).
@@ -58,7 +72,7 @@ __global__ void __launch_bounds__(64 * kWaves)
     row_segments_kernel(const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count,
                         int64_t S_q, int64_t K, int64_t S_kv, int64_t n_kt, int64_t W, int64_t C, int64_t rows,
                         uint32_t* __restrict__ bits, const int32_t* __restrict__ chunk_prefix,
-                        const int32_t* __restrict__ tile_start, int2* __restrict__ segs, int64_t capacity) {
+                        const int32_t* __restrict__ tile_start, int4* __restrict__ segs, int64_t capacity) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -70,30 +84,42 @@ __global__ void __launch_bounds__(64 * kWaves)
   const int64_t w = i / 32;
   const uint32_t bit = 1u << (i % 32);
   uint32_t* words = bits + b * W * n_kt;  // word (w', t) at words[w' * n_kt + t]
-  for (int j = lane; j < n; j += 64) {
-    const int32_t id = min(max(lst[j], 0), id_max);
-    const int32_t tile = id / kKeyTile;
-    const bool last = j + 1 >= n || min(max(lst[j + 1], 0), id_max) / kKeyTile != tile;
-    if (!last) continue;
+  int32_t carry_tile = -1;                // tile of the run still open at the end of the previous chunk
+  uint64_t carry_mask = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int j = base + lane;
+    const bool valid = j < n;
+    const int32_t id = valid ? min(max(lst[j], 0), id_max) : 0;
+    const int32_t tile = valid ? id / kKeyTile : -2 - lane;  // lanes past the list never join a run
+    const int32_t next = j + 1 < n ? min(max(lst[j + 1], 0), id_max) / kKeyTile : -1;
+    const bool last = valid && next != tile;
     if (!kFill) {
-      atomicOr(&words[w * n_kt + tile], bit);
+      if (last) atomicOr(&words[w * n_kt + tile], bit);
       continue;
     }
-    // Keys of this segment: the entries back from j in the same tile (at
-    // most 16 in an ascending list).
-    uint32_t mask = 0;
-    for (int e = 0; e < kKeyTile && j - e >= 0; ++e) {
-      const int32_t idd = min(max(lst[j - e], 0), id_max);
-      if (idd / kKeyTile != tile) break;
-      mask |= 1u << (idd % kKeyTile);
+    // Keys of each run: inclusive OR over the lanes of the same tile (a run
+    // is contiguous in an ascending list, so equal tiles d lanes apart bound
+    // a run), plus the part of the run carried from the previous chunk.
+    uint64_t m = valid ? uint64_t{1} << (id % kKeyTile) : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint64_t y = shfl_up64(m, d);
+      const int32_t ty = __shfl_up(tile, d);
+      if (lane >= d && ty == tile) m |= y;
     }
+    if (tile == carry_tile) m |= carry_mask;
+    carry_tile = __shfl(tile, 63);
+    carry_mask = shfl64(m, 63);
+    if (!last) continue;
     // Rank among the rows touching this tile: rows of earlier chunks, then
     // earlier words of this chunk, then earlier rows of this word.
     const int64_t c = w / kChunkWords;
     int64_t pos = static_cast<int64_t>(tile_start[b * n_kt + tile]) + chunk_prefix[(b * C + c) * n_kt + tile];
     for (int64_t w2 = c * kChunkWords; w2 < w; ++w2) pos += __popc(words[w2 * n_kt + tile]);
     pos += __popc(words[w * n_kt + tile] & (bit - 1u));
-    if (pos < capacity) segs[pos] = int2{static_cast<int32_t>(i), static_cast<int32_t>(mask)};
+    if (pos < capacity)
+      segs[pos] = int4{static_cast<int32_t>(i), static_cast<int32_t>(static_cast<uint32_t>(m)),
+                       static_cast<int32_t>(static_cast<uint32_t>(m >> 32)), 0};
   }
 }
 

@@ -306,7 +306,7 @@ bool bwd_layout(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, i
   l->capacity = cap;
   l->max_parts = qsa::kSegPartsTotal / Hkv > 1 ? qsa::kSegPartsTotal / Hkv : 1;
   const int64_t slots = qsa::seg_max_slots(l->max_parts, cap);
-  if (!mul_ok(slots * Hkv, 128 * D, &partial)) return false;
+  if (!mul_ok(slots * Hkv, 512 * D, &partial)) return false;
   size_t off = 0;
   auto take = [&](size_t* at, int64_t bytes) {
     *at = off;
@@ -317,7 +317,7 @@ bool bwd_layout(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, i
   take(&l->chunk_prefix, 4 * chunks);
   take(&l->totals, 4 * tiles);
   take(&l->tile_start, 4 * (tiles + 1));
-  take(&l->segs, 8 * cap);
+  take(&l->segs, 16 * cap);
   take(&l->part_start, 4 * (tiles + 1));
   take(&l->slot_start, 4 * tiles);
   take(&l->plan, 8);
@@ -356,7 +356,7 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
   if (!bwd_layout(B, S_q, S_kv, Hq, Hkv, D, K, &l)) return QSA_ERR_LIMIT;
   int64_t kv_elems = 0;
   if (!mul_ok(B * S_kv, Hkv * D, &kv_elems) || kv_elems > (INT64_MAX >> 2)) return QSA_ERR_LIMIT;
-  if ((l.n_kt * B + l.max_parts + 3) / 4 * Hkv > kMaxGrid || (s.rows + 3) / 4 > kMaxGrid ||
+  if ((l.n_kt * B + l.max_parts) * Hkv > kMaxGrid || (s.rows + 3) / 4 > kMaxGrid ||
       (B * ((S_q + qsa::kSegChunkRows - 1) / qsa::kSegChunkRows) * l.n_kt + 255) / 256 > kMaxGrid)
     return QSA_ERR_LIMIT;
   if (workspace == nullptr || workspace_bytes < l.total || !aligned(workspace, kWorkspaceAlign))
@@ -384,7 +384,7 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
   w.chunk_prefix = reinterpret_cast<int32_t*>(ws + l.chunk_prefix);
   w.totals = reinterpret_cast<int32_t*>(ws + l.totals);
   w.tile_start = reinterpret_cast<int32_t*>(ws + l.tile_start);
-  w.segs = reinterpret_cast<int2*>(ws + l.segs);
+  w.segs = reinterpret_cast<int4*>(ws + l.segs);
   w.capacity = l.capacity;
   w.part_start = reinterpret_cast<int32_t*>(ws + l.part_start);
   w.slot_start = reinterpret_cast<int32_t*>(ws + l.slot_start);

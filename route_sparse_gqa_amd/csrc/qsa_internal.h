@@ -36,19 +36,19 @@ struct AttnArgs {
 // Fused gather-attention over compacted lists.
 hipError_t launch_gather_attention(const AttnArgs& a, hipStream_t stream);
 
-// Key segments (route lists regrouped by 16-key tile, rows ascending) and
+// Key segments (route lists regrouped by 64-key tile, rows ascending) and
 // their split into parts for the key-side backward kernel.
-constexpr int64_t kSegKeyTile = 16;     // keys per tile of the key-side backward
+constexpr int64_t kSegKeyTile = 64;     // keys per tile of the key-side backward (one workgroup)
 constexpr int64_t kSegChunkRows = 256;  // query rows per popcount-prefix chunk
 constexpr int64_t kSegMinPart = 64;     // smallest part length (segments)
-constexpr int64_t kSegPartsTotal = 16384;  // target parts over all KV heads
+constexpr int64_t kSegPartsTotal = 4096;  // target parts (workgroups) over all KV heads
 
 struct SegmentBuffers {
   uint32_t* bits;         // [B][ceil(S_q/32)][n_kt] one bit per (query row, tile)
   int32_t* chunk_prefix;  // [B][ceil(S_q/256)][n_kt]
   int32_t* totals;        // [B * n_kt]
   int32_t* tile_start;    // [B * n_kt + 1]: segments of (b, t) are [start[b*n_kt+t], start[b*n_kt+t+1])
-  int2* segs;             // [capacity] {query row within the batch, key mask}
+  int4* segs;             // [capacity] {query row within the batch, key mask lo, key mask hi, 0}
   int64_t capacity;
   int32_t* part_start;    // [B * n_kt + 1]
   int32_t* slot_start;    // [B * n_kt]
@@ -71,11 +71,11 @@ struct BwdArgs {
   const int32_t* route_list;
   const int32_t* route_count;
   const int32_t* seg_start;   // tile_start of the key segments
-  const int2* segs;
+  const int4* segs;
   const int32_t* part_start;
   const int32_t* slot_start;
   const int32_t* plan;
-  float* partial;             // [slots][Hkv][2][D/16][64][4] fp32 partial sums of split tiles
+  float* partial;             // [slots][Hkv][4 waves][2][D/16][64][4] fp32 partial sums of split tiles
   int64_t max_parts;
   int64_t B, S_q, S_kv, Hq, Hkv, D, K;
   float scale;
@@ -85,7 +85,7 @@ struct BwdArgs {
 };
 
 // dq and delta (one wavefront per (b, i, hk)); then dk and dv (one wavefront
-// per (b, 16-key tile, hk)) over the key segments.
+// workgroup per (part of a 64-key tile, hk)) over the key segments.
 hipError_t launch_attention_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_attention_dkdv(const BwdArgs& a, hipStream_t stream);
 

@@ -96,12 +96,12 @@ def test_other_host_checks():
 def _bwd_ws(B, S_q, S_kv, Hq, Hkv, D, K):
     """The layout the header documents, from its formula."""
     r = lambda x: -(-x // 256) * 256
-    T, n_w, n_c = -(-S_kv // 16), -(-S_q // 32), -(-S_q // 256)
+    T, n_w, n_c = -(-S_kv // 64), -(-S_q // 32), -(-S_q // 256)
     cap = B * S_q * min(K, T)
-    P = max(1, 16384 // Hkv)
+    P = max(1, 4096 // Hkv)
     slots = 2 * min(P, -(-cap // 64))
     return (r(4 * B * S_q * Hq) + r(4 * B * n_w * T) + r(4 * B * n_c * T) + r(4 * B * T) + r(4 * (B * T + 1)) +
-            r(8 * cap) + r(4 * (B * T + 1)) + r(4 * B * T) + r(8) + r(128 * D * Hkv * slots))
+            r(16 * cap) + r(4 * (B * T + 1)) + r(4 * B * T) + r(8) + r(512 * D * Hkv * slots))
 
 
 def test_backward_workspace_size():
@@ -111,7 +111,7 @@ def test_backward_workspace_size():
         assert ws(*args) == _bwd_ws(*args), args
     assert ws(1, 65536, 65536, 16, 2, 256, 2048) < 3 << 30  # long sequences fit in a few GiB
     assert ws(0, 1, 1, 1, 1, 64, 1) == 0 and ws(1, 1, 1, 1, 1, 64, 0) == 0
-    assert ws(1, 1 << 20, 1 << 24, 16, 2, 256, 2048) == 0  # more than 2^31 - 1 segments
+    assert ws(1, 1 << 21, 1 << 24, 16, 2, 256, 2048) == 0  # more than 2^31 - 1 segments
 
 
 def _call_backward(B=1, S_q=4, S_kv=32, Hq=2, Hkv=1, D=64, K=2, scale=0.1, ws_bytes=1 << 30, alias_dq_q=False,

@@ -14,7 +14,7 @@
   and dv exactly +0.0;
 * the backward is deterministic: a second call gives the same bits;
 * the key segments it builds (read back from the workspace) are exactly the
-  (row, 16-key tile, key mask) triples of the route lists, rows ascending
+  (row, 64-key tile, key mask) triples of the route lists, rows ascending
   within each tile.
 """
 
@@ -91,14 +91,16 @@ def _r256(x):
 
 def read_segments(ws: torch.Tensor, B, S_q, S_kv, Hq):
     """tile_start and segments from the documented workspace layout."""
-    n_kt, n_w, n_c = -(-S_kv // 16), -(-S_q // 32), -(-S_q // 256)
+    n_kt, n_w, n_c = -(-S_kv // 64), -(-S_q // 32), -(-S_q // 256)
     # delta, bit matrix, chunk prefixes, tile totals, then tile starts and segments
     off = _r256(4 * B * S_q * Hq) + _r256(4 * B * n_w * n_kt) + _r256(4 * B * n_c * n_kt) + _r256(4 * B * n_kt)
     w = ws.cpu().numpy()
     start = w[off:off + 4 * (B * n_kt + 1)].view(np.int32)
     off += _r256(4 * (B * n_kt + 1))
     total = int(start[-1])
-    segs = w[off:off + 8 * total].view(np.int32).reshape(total, 2)
+    rec = w[off:off + 16 * total].view(np.int32).reshape(total, 4)
+    segs = [(int(e[0]), int(np.uint32(e[1])) | (int(np.uint32(e[2])) << 32)) for e in rec]
+    assert not rec[:, 3].any(), "segment padding must be zero"
     return n_kt, start, segs
 
 
@@ -109,12 +111,12 @@ def expected_segments(lst: np.ndarray, cnt: np.ndarray, n_kt: int):
     for b in range(B):
         for i in range(S_q):
             for key in lst[b, i, :cnt[b, i]]:
-                t = int(key) // 16
+                t = int(key) // 64
                 e = out.setdefault((b, t), [])
                 if e and e[-1][0] == i:
-                    e[-1] = (i, e[-1][1] | (1 << (int(key) % 16)))
+                    e[-1] = (i, e[-1][1] | (1 << (int(key) % 64)))
                 else:
-                    e.append((i, 1 << (int(key) % 16)))
+                    e.append((i, 1 << (int(key) % 64)))
     return out
 
 
@@ -151,7 +153,7 @@ def test_backward_matches_oracle(case):
     assert int(start[-1]) == sum(len(x) for x in want.values())
     for b in range(B):
         for t in range(n_kt):
-            got = [tuple(x) for x in segs[start[b * n_kt + t]:start[b * n_kt + t + 1]].tolist()]
+            got = segs[start[b * n_kt + t]:start[b * n_kt + t + 1]]
             assert got == want.get((b, t), []), f"segments of (b={b}, tile={t}) differ"
 
     # determinism: a second backward gives the same bits

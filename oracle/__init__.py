@@ -12,6 +12,10 @@ their ``uint16`` bit patterns):
 * ``membership(routes, kv_length)``       -> uint8 [B,S_q,round_up(kv_length,128)]
 * ``tile_class(routes, kv_length)``       -> int32 [B,ceil(S_q/128),ceil(kv_length/128)]
 * ``forward(q, k, v, routes, scale, rows=None)`` -> float64 [B,rows,Hq,D]
+* ``tile_lists(kinds)`` -> dict of int32 arrays: ``partial_count`` [B,1,R],
+  ``partial_idx`` [B,1,R,C], ``full_count``, ``full_idx``, and the reverse
+  ``rev_partial_count`` [B,1,C], ``rev_partial_idx`` [B,1,C,R], ``rev_full_count``,
+  ``rev_full_idx`` (R, C = block rows and columns of ``kinds`` [B,R,C])
 * ``lse(q, k, routes, scale, rows=None)`` -> float64 [B,rows,Hq] (natural log; -inf for empty rows)
 * ``backward(q, k, v, dout, routes, scale, rows=None, keys=None)``
   -> (dq [B,rows,Hq,D], dk [B,keys,Hkv,D], dv [B,keys,Hkv,D]) float64
@@ -33,6 +37,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 TILE = 128
+TILE_LIST_KEYS = ("partial_count", "partial_idx", "full_count", "full_idx", "rev_partial_count", "rev_partial_idx",
+                  "rev_full_count", "rev_full_idx")
 
 
 def build(force: bool = True) -> str:
@@ -58,6 +64,8 @@ class Oracle:
         lib.oracle_tile_class.argtypes = [p, i64, i64, i64, i64, p]
         lib.oracle_forward.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, i64,
                                        ctypes.c_double, i64, i64, p]
+        lib.oracle_tile_lists.argtypes = [p, i64, i64, i64, p, p, p, p, p, p, p, p]
+        lib.oracle_tile_lists.restype = None
         lib.oracle_lse.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double, i64, i64, p]
         lib.oracle_backward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64,
                                         ctypes.c_double, i64, i64, i64, i64, p, p, p]
@@ -108,6 +116,18 @@ class Oracle:
         out = np.empty((B, r1 - r0, Hq, D), dtype=np.float64)
         self.lib.oracle_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(r), B, S_q, S_kv, Hq, Hkv, D, K,
                                 float(scale), r0, r1, _ptr(out))
+        return out
+
+    def tile_lists(self, kinds):
+        kinds = np.ascontiguousarray(kinds, dtype=np.int32)
+        B, R, C = kinds.shape
+        out = {
+            "partial_count": np.empty((B, 1, R), np.int32), "partial_idx": np.empty((B, 1, R, C), np.int32),
+            "full_count": np.empty((B, 1, R), np.int32), "full_idx": np.empty((B, 1, R, C), np.int32),
+            "rev_partial_count": np.empty((B, 1, C), np.int32), "rev_partial_idx": np.empty((B, 1, C, R), np.int32),
+            "rev_full_count": np.empty((B, 1, C), np.int32), "rev_full_idx": np.empty((B, 1, C, R), np.int32),
+        }
+        self.lib.oracle_tile_lists(_ptr(kinds), B, R, C, *(_ptr(out[k]) for k in TILE_LIST_KEYS))
         return out
 
     def lse(self, q, k, routes, scale, rows=None):
@@ -207,3 +227,8 @@ def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, rout
              rows: tuple[int, int] | None = None, keys: tuple[int, int] | None = None):
     """fp64 (dq [B,rows,Hq,D], dk [B,keys,Hkv,D], dv [B,keys,Hkv,D]) for upstream gradient ``dout``."""
     return _load().backward(q, k, v, dout, routes, scale, rows, keys)
+
+
+def tile_lists(kinds: np.ndarray) -> dict:
+    """Forward and reverse partial/full block lists of a tile-class table [B, R, C]."""
+    return _load().tile_lists(kinds)

@@ -30,6 +30,10 @@
  *    s_j = scale * <q[b,i,h,:], k[b,j,hk,:]>, o = sum_j softmax(s)_j v[b,j,hk,:];
  *    an empty R gives exactly zero; no causal or other mask is added.
  *    All arithmetic is fp64 on the exact bfloat16 input values.
+ *  - Block lists of a tile-class table (fa4_qsa page, `_compact_blocks` and
+ *    `_preprocess`): per block row (forward) and per block column (reverse),
+ *    the count and ascending indices of partial and of full tiles, see
+ *    `oracle_tile_lists`.
  *  - Log-sum-exp of each row's scaled scores and the first-order gradients
  *    dq, dk, dv of that attention (fa4_qsa page: FA4 owns first-order
  *    autograd; empty rows have zero output and zero gradients): the softmax
@@ -325,5 +329,58 @@ void oracle_backward(const uint16_t *q, const uint16_t *k, const uint16_t *v, co
         free(set);
         free(p);
         free(dp);
+    }
+}
+
+/*
+ * Block lists of a tile-class table (fa4_qsa page, `_compact_blocks`: partial
+ * and full block columns of each block row, int32 counts [batch, 1, rows];
+ * `_preprocess`: forward and reverse block lists).  kinds is int32
+ * [B, n_rows, n_cols] with 0 absent, 1 partial, 2 full.
+ *
+ * Forward, per (b, row) and per kind k in {1, 2}:
+ *   count[b][row]    = number of columns whose class is k;
+ *   idx[b][row][:]   = those columns in ascending order, followed by every
+ *                      other column in ascending order (each index row is a
+ *                      permutation of 0 .. n_cols - 1; only the first count
+ *                      entries are meaningful).
+ * Reverse, per (b, col): the same over rows of that column.
+ * Any output pointer may be NULL (that list is not produced).
+ */
+static void compact_line(const int32_t *kinds, int64_t n, int64_t stride, int32_t want, int32_t *count,
+                         int32_t *idx) {
+    int64_t m = 0;
+    for (int64_t x = 0; x < n; ++x)
+        if (kinds[x * stride] == want) {
+            if (idx) idx[m] = (int32_t)x;
+            ++m;
+        }
+    if (count) *count = (int32_t)m;
+    if (idx) {
+        int64_t r = m;
+        for (int64_t x = 0; x < n; ++x)
+            if (kinds[x * stride] != want) idx[r++] = (int32_t)x;
+    }
+}
+
+void oracle_tile_lists(const int32_t *kinds, int64_t B, int64_t n_rows, int64_t n_cols, int32_t *partial_count,
+                       int32_t *partial_idx, int32_t *full_count, int32_t *full_idx, int32_t *rev_partial_count,
+                       int32_t *rev_partial_idx, int32_t *rev_full_count, int32_t *rev_full_idx) {
+    for (int64_t b = 0; b < B; ++b) {
+        const int32_t *kb = kinds + b * n_rows * n_cols;
+        for (int64_t r = 0; r < n_rows; ++r) {
+            const int64_t o = b * n_rows + r;
+            compact_line(kb + r * n_cols, n_cols, 1, 1, partial_count ? partial_count + o : NULL,
+                         partial_idx ? partial_idx + o * n_cols : NULL);
+            compact_line(kb + r * n_cols, n_cols, 1, 2, full_count ? full_count + o : NULL,
+                         full_idx ? full_idx + o * n_cols : NULL);
+        }
+        for (int64_t c = 0; c < n_cols; ++c) {
+            const int64_t o = b * n_cols + c;
+            compact_line(kb + c, n_rows, n_cols, 1, rev_partial_count ? rev_partial_count + o : NULL,
+                         rev_partial_idx ? rev_partial_idx + o * n_rows : NULL);
+            compact_line(kb + c, n_rows, n_cols, 2, rev_full_count ? rev_full_count + o : NULL,
+                         rev_full_idx ? rev_full_idx + o * n_rows : NULL);
+        }
     }
 }

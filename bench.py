@@ -21,7 +21,10 @@ kernel, on the forward's output and log-sum-exp), reporting routed TFLOP/s
 with F = 10*D*Hq*N (scores, dP, dQ, dK, dV on routed pairs) and the
 algorithmic bytes of the whole call against the HBM roofline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass forward|backward]
+With ``--pass tile_lists`` it times qsa_tile_lists (forward and reverse
+partial/full block lists) on the workload's tile classes.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass forward|backward|tile_lists]
 """
 
 from __future__ import annotations
@@ -51,7 +54,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "tile_lists"], default="forward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -250,6 +253,9 @@ def main():
     if args.which == "backward":
         run_backward(args, w, plan, dev, N)
         return
+    if args.which == "tile_lists":
+        run_tile_lists(args, w, plan, dev)
+        return
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -375,6 +381,50 @@ def run_backward(args, w, plan, dev, N):
         "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)
+
+
+def run_tile_lists(args, w, plan, dev):
+    import torch
+
+    import route_sparse_gqa_amd as qsa
+
+    B, R, C = plan.tc.shape
+    outs = {"partial_count": (B, R), "partial_idx": (B, R, C), "full_count": (B, R), "full_idx": (B, R, C),
+            "rev_partial_count": (B, C), "rev_partial_idx": (B, C, R), "rev_full_count": (B, C),
+            "rev_full_idx": (B, C, R)}
+    bufs = [torch.empty(outs[k], dtype=torch.int32, device=dev) for k in qsa.TILE_LIST_KEYS]
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in bufs]
+    args_c = (ctypes.c_void_p(plan.tc.data_ptr()), B, R, C, *ptrs, plan.stream)
+
+    def call():
+        rc = plan.L.qsa_tile_lists(*args_c)
+        if rc != 0:
+            raise RuntimeError(f"qsa_tile_lists failed with status {rc}")
+
+    for _ in range(max(args.warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        call()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    tiles = B * R * C
+    alg_bytes = 2 * 4 * tiles + 4 * 4 * tiles + 2 * 4 * (B * R + B * C)  # table read per direction, lists written
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "block-list compaction time (forward + reverse, partial + full) on 1 MI355X",
+        "value": ms * 1e3, "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "block_rows": R, "block_cols": C},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "tile_lists_kernel",
+                     "ms_per_launch": ms, "alg_bytes_per_launch": alg_bytes},
+        "cpu_baseline": None,
+    }), flush=True)
 
 
 def _kernel_sha() -> str:

@@ -94,6 +94,36 @@ int qsa_preprocess(const void *routes, int routes_dtype, int64_t B, int64_t S_q,
                    int32_t *route_count, uint8_t *membership, int32_t *tile_class, void *stream);
 
 /*
+ * qsa_tile_lists -- forward and reverse partial/full block lists of a
+ * tile-class table (the block-sparse format of FlexAttention's BlockMask and
+ * the pages' FA4 path).
+ *
+ * Definition (fa4_qsa page, `_compact_blocks`: partial and full block
+ * columns of each block row, int32 counts [batch, 1, block_rows];
+ * `_preprocess`: forward and reverse block lists).  For each line -- a block
+ * row for the forward lists, a block column for the reverse ones -- and each
+ * kind (1 partial, 2 full): the number of tiles of that kind, and an index
+ * row with their positions in ascending order followed by every other
+ * position in ascending order (a permutation; only the first count entries
+ * are meaningful).
+ *
+ *   tile_class        [B, n_rows, n_cols] int32 (0/1/2), contiguous, as
+ *                     qsa_preprocess writes it.  Other values count as
+ *                     neither kind.
+ *   partial_count     OUT, nullable: [B, 1, n_rows] int32
+ *   partial_idx       OUT, nullable: [B, 1, n_rows, n_cols] int32
+ *   full_count, full_idx                 OUT, nullable: same shapes, full tiles
+ *   rev_partial_count OUT, nullable: [B, 1, n_cols] int32
+ *   rev_partial_idx   OUT, nullable: [B, 1, n_cols, n_rows] int32
+ *   rev_full_count, rev_full_idx         OUT, nullable: same shapes, full tiles
+ * All contiguous, 4-B aligned, not overlapping each other or tile_class.
+ * Errors: NULL_POINTER (tile_class), EMPTY_DIM, LAYOUT, ALIAS, LIMIT, HIP.
+ */
+int qsa_tile_lists(const int32_t *tile_class, int64_t B, int64_t n_rows, int64_t n_cols, int32_t *partial_count,
+                   int32_t *partial_idx, int32_t *full_count, int32_t *full_idx, int32_t *rev_partial_count,
+                   int32_t *rev_partial_idx, int32_t *rev_full_count, int32_t *rev_full_idx, void *stream);
+
+/*
  * qsa_forward_workspace_size -- bytes of device workspace qsa_forward needs:
  * the compacted lists and counts (4*B*S_q*K + 4*B*S_q) plus alignment.
  * Returns 0 when a size is < 1 or the product overflows.

@@ -9,6 +9,7 @@ torch's current HIP stream to the library.  Every step of the computation
 runs in the library's HIP kernels; there is no other code path.
 
 * ``qsa_preprocess(routes, kv_length, membership=False, tile_class=False)``
+* ``qsa_tile_lists(tile_class)``
 * ``qsa_forward(q, k, v, routes, scale=None)``
 * ``qsa_forward_preprocessed(q, k, v, route_list, route_count, scale=None, return_lse=False)``
 * ``qsa_backward(q, k, v, out, dout, lse, route_list, route_count, scale=None)``
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_forward_preprocessed.argtypes = [p, P64, p, P64, p, P64, p, p, i64, i64, i64, i64, i64, i64, i64,
                                                ctypes.c_float, p, p, p]
         L.qsa_forward_preprocessed.restype = i32
+        L.qsa_tile_lists.argtypes = [p, i64, i64, i64, p, p, p, p, p, p, p, p, p]
+        L.qsa_tile_lists.restype = i32
         L.qsa_backward_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64]
         L.qsa_backward_workspace_size.restype = ctypes.c_size_t
         L.qsa_backward.argtypes = [p, P64, p, P64, p, P64, p, p, P64, p, p, p, i64, i64, i64, i64, i64, i64, i64,
@@ -164,6 +167,34 @@ def qsa_preprocess(routes: torch.Tensor, kv_length: int, membership: bool = Fals
                               _ptr(mem), _ptr(tc), _stream(dev))
     _check(st, "qsa_preprocess")
     return lst, cnt, mem, tc
+
+
+TILE_LIST_KEYS = ("partial_count", "partial_idx", "full_count", "full_idx", "rev_partial_count", "rev_partial_idx",
+                  "rev_full_count", "rev_full_idx")
+
+
+def qsa_tile_lists(tile_class: torch.Tensor, which=TILE_LIST_KEYS) -> dict:
+    """Forward and reverse partial/full block lists of a tile-class table [B, R, C] (int32 0/1/2).
+
+    Returns a dict with the requested keys of ``TILE_LIST_KEYS``: counts [B,1,R] and
+    indices [B,1,R,C] per block row, and the reverse counts [B,1,C] and indices
+    [B,1,C,R] per block column (listed tiles ascending, then the other positions).
+    """
+    dev = _require_gpu(tile_class)
+    if tile_class.dtype != torch.int32 or tile_class.dim() != 3:
+        raise ValueError("tile_class must be an int32 [B, rows, cols] tensor")
+    tile_class = tile_class.contiguous()
+    B, R, C = tile_class.shape
+    shapes = {"partial_count": (B, 1, R), "partial_idx": (B, 1, R, C), "full_count": (B, 1, R),
+              "full_idx": (B, 1, R, C), "rev_partial_count": (B, 1, C), "rev_partial_idx": (B, 1, C, R),
+              "rev_full_count": (B, 1, C), "rev_full_idx": (B, 1, C, R)}
+    unknown = set(which) - set(TILE_LIST_KEYS)
+    if unknown:
+        raise ValueError(f"unknown block lists: {sorted(unknown)}")
+    out = {k: torch.empty(shapes[k], dtype=torch.int32, device=dev) for k in TILE_LIST_KEYS if k in which}
+    st = lib().qsa_tile_lists(_ptr(tile_class), B, R, C, *(_ptr(out.get(k)) for k in TILE_LIST_KEYS), _stream(dev))
+    _check(st, "qsa_tile_lists")
+    return out
 
 
 def _attention_shapes(q, k, v):
@@ -280,6 +311,7 @@ def qsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
 
 __all__ = [
     "qsa_preprocess",
+    "qsa_tile_lists",
     "qsa_forward",
     "qsa_forward_preprocessed",
     "qsa_backward",

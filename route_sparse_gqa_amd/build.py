@@ -28,6 +28,7 @@ SOURCES = [
     "gather_attention.hip",
     "attention_backward.hip",
     "key_segments.hip",
+    "tile_lists.hip",
     "qsa_api.cpp",
 ]
 

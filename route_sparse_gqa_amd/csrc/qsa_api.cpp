@@ -161,6 +161,33 @@ QSA_EXPORT int qsa_preprocess(const void* routes, int routes_dtype, int64_t B, i
       qsa::launch_membership_tiles(route_list, route_count, B, S_q, K, kv_length, membership, tile_class, st));
 }
 
+QSA_EXPORT int qsa_tile_lists(const int32_t* tile_class, int64_t B, int64_t n_rows, int64_t n_cols,
+                              int32_t* partial_count, int32_t* partial_idx, int32_t* full_count, int32_t* full_idx,
+                              int32_t* rev_partial_count, int32_t* rev_partial_idx, int32_t* rev_full_count,
+                              int32_t* rev_full_idx, void* stream) {
+  if (B < 1 || n_rows < 1 || n_cols < 1) return QSA_ERR_EMPTY_DIM;
+  if (tile_class == nullptr) return QSA_ERR_NULL_POINTER;
+  int64_t tiles = 0, rows = 0, cols = 0;
+  if (n_rows > kMaxGrid || n_cols > kMaxGrid || !mul_ok(B, n_rows, &rows) || !mul_ok(B, n_cols, &cols) ||
+      !mul_ok(rows, n_cols, &tiles) || tiles > (INT64_MAX >> 3) || (rows + cols + 3) / 4 > kMaxGrid)
+    return QSA_ERR_LIMIT;
+  int32_t* const out[8] = {partial_count, partial_idx, full_count, full_idx,
+                           rev_partial_count, rev_partial_idx, rev_full_count, rev_full_idx};
+  const int64_t elems[8] = {rows, tiles, rows, tiles, cols, tiles, cols, tiles};
+  if (!aligned(tile_class, 4)) return QSA_ERR_LAYOUT;
+  for (int a = 0; a < 8; ++a)
+    if (out[a] != nullptr && !aligned(out[a], 4)) return QSA_ERR_LAYOUT;
+  const Range in = dense(tile_class, 4 * tiles);
+  for (int a = 0; a < 8; ++a) {
+    const Range ra = out[a] ? dense(out[a], 4 * elems[a]) : Range{};
+    if (overlap(ra, in)) return QSA_ERR_ALIAS;
+    for (int b = a + 1; b < 8; ++b)
+      if (overlap(ra, out[b] ? dense(out[b], 4 * elems[b]) : Range{})) return QSA_ERR_ALIAS;
+  }
+  (void)hipGetLastError();
+  return hip_status(qsa::launch_tile_lists(tile_class, B, n_rows, n_cols, out, as_stream(stream)));
+}
+
 namespace {
 
 int check_attention(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],

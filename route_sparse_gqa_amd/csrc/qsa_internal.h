@@ -20,6 +20,12 @@ hipError_t launch_membership_tiles(const int32_t* route_list, const int32_t* rou
                                    int64_t S_q, int64_t K, int64_t kv_length, uint8_t* membership,
                                    int32_t* tile_class, hipStream_t stream);
 
+// Forward and reverse partial/full block lists of a tile-class table; out =
+// {partial_count, partial_idx, full_count, full_idx, rev_partial_count,
+// rev_partial_idx, rev_full_count, rev_full_idx}, each nullable.
+hipError_t launch_tile_lists(const int32_t* kinds, int64_t B, int64_t n_rows, int64_t n_cols, int32_t* const out[8],
+                             hipStream_t stream);
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;

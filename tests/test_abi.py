@@ -29,7 +29,7 @@ def _declared_constants():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "qsa_preprocess", "qsa_forward", "qsa_forward_preprocessed", "qsa_forward_workspace_size",
-        "qsa_backward", "qsa_backward_workspace_size", "qsa_status_string"])
+        "qsa_backward", "qsa_backward_workspace_size", "qsa_tile_lists", "qsa_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -136,3 +136,13 @@ def test_backward_host_checks():
     assert _call_backward(null_lse=True) == -1
     assert _call_backward(alias_dq_q=True) == -9
     assert _call_backward(ws_bytes=16) == -10
+
+
+def test_tile_lists_host_checks():
+    L = qsa.lib()
+    f = [ctypes.c_void_p(n << 32) for n in range(1, 10)]  # distinct, never dereferenced
+    assert L.qsa_tile_lists(f[0], 0, 2, 2, *f[1:9], None) == -2
+    assert L.qsa_tile_lists(None, 1, 2, 2, *f[1:9], None) == -1
+    assert L.qsa_tile_lists(f[0], 1, 2, 2, f[1], f[1], *f[3:9], None) == -9  # two outputs alias
+    assert L.qsa_tile_lists(f[0], 1, 2, 2, f[0], *f[2:9], None) == -9        # output aliases the input
+    assert L.qsa_tile_lists(ctypes.c_void_p((1 << 32) + 2), 1, 2, 2, *f[1:9], None) == -8

@@ -16,6 +16,9 @@ their ``uint16`` bit patterns):
   ``partial_idx`` [B,1,R,C], ``full_count``, ``full_idx``, and the reverse
   ``rev_partial_count`` [B,1,C], ``rev_partial_idx`` [B,1,C,R], ``rev_full_count``,
   ``rev_full_idx`` (R, C = block rows and columns of ``kinds`` [B,R,C])
+* ``select_token_ids(iq, ck, seq_lens, token_budget, compress_ratio, q_offset=0, rows=None)``
+  -> int32 [B,rows,token_budget+compress_ratio-1] (iq [B,S_q,H,D], ck [B,n_blocks,D] bf16 bits)
+* ``block_scores(iq, ck, rows=None)`` -> float64 [B,rows,n_blocks]: every block's score, visible or not
 * ``lse(q, k, routes, scale, rows=None)`` -> float64 [B,rows,Hq] (natural log; -inf for empty rows)
 * ``backward(q, k, v, dout, routes, scale, rows=None, keys=None)``
   -> (dq [B,rows,Hq,D], dk [B,keys,Hkv,D], dv [B,keys,Hkv,D]) float64
@@ -69,8 +72,10 @@ class Oracle:
         lib.oracle_lse.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double, i64, i64, p]
         lib.oracle_backward.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64,
                                         ctypes.c_double, i64, i64, i64, i64, p, p, p]
+        lib.oracle_select_token_ids.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, p]
+        lib.oracle_block_scores.argtypes = [p, p, i64, i64, i64, i64, i64, i64, i64, p]
         for f in (lib.oracle_route_lists, lib.oracle_membership, lib.oracle_tile_class, lib.oracle_forward,
-                  lib.oracle_lse, lib.oracle_backward):
+                  lib.oracle_lse, lib.oracle_backward, lib.oracle_select_token_ids, lib.oracle_block_scores):
             f.restype = None
         self.lib = lib
 
@@ -162,6 +167,38 @@ class Oracle:
         return dq, dk, dv
 
 
+    def select_token_ids(self, iq, ck, seq_lens, token_budget, compress_ratio, q_offset=0, rows=None):
+        iq, ck = _bf16_bits(iq=iq, ck=ck)
+        lens = np.ascontiguousarray(seq_lens, dtype=np.int64)
+        B, S_q, H, D = iq.shape
+        if ck.ndim == 4:  # [B, n_blocks, 1, D]
+            ck = np.ascontiguousarray(ck[:, :, 0, :])
+        n_blocks = ck.shape[1]
+        c, budget, q_offset = int(compress_ratio), int(token_budget), int(q_offset)
+        if ck.shape[0] != B or ck.shape[2] != D or lens.shape != (B,):
+            raise ValueError("shape mismatch among index queries, block keys and lengths")
+        if c < 1 or budget < 1 or q_offset < 0:
+            raise ValueError("compress_ratio and token_budget must be >= 1, q_offset >= 0")
+        if (q_offset + S_q) // c > n_blocks:
+            raise ValueError("fewer block keys than the last query row can see")
+        r0, r1 = (0, S_q) if rows is None else (int(rows[0]), int(rows[1]))
+        out = np.empty((B, r1 - r0, budget + c - 1), dtype=np.int32)
+        self.lib.oracle_select_token_ids(_ptr(iq), _ptr(ck), _ptr(lens), B, S_q, H, D, n_blocks, q_offset,
+                                         budget, c, r0, r1, _ptr(out))
+        return out
+
+    def block_scores(self, iq, ck, rows=None):
+        iq, ck = _bf16_bits(iq=iq, ck=ck)
+        if ck.ndim == 4:
+            ck = np.ascontiguousarray(ck[:, :, 0, :])
+        B, S_q, H, D = iq.shape
+        n_blocks = ck.shape[1]
+        r0, r1 = (0, S_q) if rows is None else (int(rows[0]), int(rows[1]))
+        out = np.empty((B, r1 - r0, n_blocks), dtype=np.float64)
+        self.lib.oracle_block_scores(_ptr(iq), _ptr(ck), B, S_q, H, D, n_blocks, r0, r1, _ptr(out))
+        return out
+
+
 def _bf16_bits(**tensors):
     out = []
     for name, t in tensors.items():
@@ -232,3 +269,14 @@ def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, rout
 def tile_lists(kinds: np.ndarray) -> dict:
     """Forward and reverse partial/full block lists of a tile-class table [B, R, C]."""
     return _load().tile_lists(kinds)
+
+
+def select_token_ids(iq: np.ndarray, ck: np.ndarray, seq_lens: np.ndarray, token_budget: int, compress_ratio: int,
+                     q_offset: int = 0, rows: tuple[int, int] | None = None) -> np.ndarray:
+    """Selected token IDs int32 [B, rows, token_budget + compress_ratio - 1] (-1 = empty slot)."""
+    return _load().select_token_ids(iq, ck, seq_lens, token_budget, compress_ratio, q_offset, rows)
+
+
+def block_scores(iq: np.ndarray, ck: np.ndarray, rows: tuple[int, int] | None = None) -> np.ndarray:
+    """fp64 block scores sum_h relu(<iq[b,i,h], ck[b,j]>) / sqrt(D), [B, rows, n_blocks]."""
+    return _load().block_scores(iq, ck, rows)

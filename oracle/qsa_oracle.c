@@ -34,6 +34,10 @@
  *    `_preprocess`): per block row (forward) and per block column (reverse),
  *    the count and ascending indices of partial and of full tiles, see
  *    `oracle_tile_lists`.
+ *  - Route selection (qsa page, `select_qsa_token_ids`): per query row the
+ *    best compressed blocks by sum over index heads of relu(q . k) / sqrt(D),
+ *    expanded to token IDs, plus the incomplete causal tail, see
+ *    `oracle_select_token_ids`.
  *  - Log-sum-exp of each row's scaled scores and the first-order gradients
  *    dq, dk, dv of that attention (fa4_qsa page: FA4 owns first-order
  *    autograd; empty rows have zero output and zero gradients): the softmax
@@ -382,5 +386,104 @@ void oracle_tile_lists(const int32_t *kinds, int64_t B, int64_t n_rows, int64_t 
             compact_line(kb + c, n_rows, n_cols, 2, rev_full_count ? rev_full_count + o : NULL,
                          rev_full_idx ? rev_full_idx + o * n_rows : NULL);
         }
+    }
+}
+
+/*
+ * Route selection by compressed-block scores (qsa page,
+ * `select_qsa_token_ids`; `Qwen3_8_FlashNextQSAIndexer` for the output
+ * width).
+ *
+ * Inputs: index queries iq [B, S_q, H, D] and compressed block keys
+ * ck [B, n_blocks, D] (one key head), contiguous bfloat16 bit patterns;
+ * seq_lens [B] right-padded logical lengths in global positions.  Local
+ * query row i stands at global position t = q_offset + i.  With
+ * c = compress_ratio, kb = token_budget / c (integer division) and
+ * W = token_budget + c - 1 slots per row:
+ *
+ *   - a row with t >= seq_lens[b] is a padding query: every slot is -1;
+ *   - otherwise nv = floor((t + 1) / c) complete blocks are visible, and
+ *     block j scores  s_j = sum_h max(0, <iq[b,i,h,:], ck[b,j,:]>) / sqrt(D);
+ *   - the m = min(kb, nv) best blocks are kept, best meaning the larger
+ *     score and, between equal scores, the smaller block index;
+ *   - slots [0, m*c) hold the kept blocks in ascending block order, each
+ *     expanded to its c token IDs j*c .. j*c + c - 1; slots [m*c, token_budget)
+ *     are -1;
+ *   - slots [token_budget, token_budget + (t + 1) - nv*c) hold the tokens of
+ *     the incomplete causal tail, nv*c .. t; the remaining slots are -1.
+ *
+ * Scores are fp64 on the exact bfloat16 values; the order of the kept
+ * blocks, the tie rule and the fixed slot layout are readings of the page
+ * (it orders none of them).  out is [B, row_end - row_begin, W] int32.
+ */
+typedef struct {
+    double score;
+    int64_t block;
+} scored_block;
+
+static int cmp_best_first(const void *a, const void *b) {
+    const scored_block *x = (const scored_block *)a, *y = (const scored_block *)b;
+    if (x->score != y->score) return x->score > y->score ? -1 : 1;
+    return (x->block > y->block) - (x->block < y->block);
+}
+
+/* s_j of one query row against one block key, fp64. */
+static double block_score(const uint16_t *qrow, const uint16_t *key, int64_t H, int64_t D) {
+    double total = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += bf16_to_double(qrow[h * D + d]) * bf16_to_double(key[d]);
+        total += dot > 0.0 ? dot : 0.0;
+    }
+    return total / sqrt((double)D);
+}
+
+/* scores [B, row_end - row_begin, n_blocks] fp64: s_j for every block, visible or not. */
+void oracle_block_scores(const uint16_t *iq, const uint16_t *ck, int64_t B, int64_t S_q, int64_t H, int64_t D,
+                         int64_t n_blocks, int64_t row_begin, int64_t row_end, double *scores) {
+    const int64_t n_rows = row_end - row_begin;
+#pragma omp parallel for schedule(dynamic, 4) collapse(2)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t i = row_begin; i < row_end; ++i)
+            for (int64_t j = 0; j < n_blocks; ++j)
+                scores[(b * n_rows + (i - row_begin)) * n_blocks + j] =
+                    block_score(iq + (b * S_q + i) * H * D, ck + (b * n_blocks + j) * D, H, D);
+}
+
+void oracle_select_token_ids(const uint16_t *iq, const uint16_t *ck, const int64_t *seq_lens, int64_t B,
+                             int64_t S_q, int64_t H, int64_t D, int64_t n_blocks, int64_t q_offset,
+                             int64_t token_budget, int64_t compress_ratio, int64_t row_begin, int64_t row_end,
+                             int32_t *out) {
+    const int64_t c = compress_ratio;
+    const int64_t kb = token_budget / c;
+    const int64_t W = token_budget + c - 1;
+    const int64_t n_rows = row_end - row_begin;
+#pragma omp parallel
+    {
+        scored_block *cand = (scored_block *)malloc((size_t)(n_blocks > 0 ? n_blocks : 1) * sizeof(scored_block));
+        int64_t *kept = (int64_t *)malloc((size_t)(n_blocks > 0 ? n_blocks : 1) * sizeof(int64_t));
+#pragma omp for schedule(dynamic, 4) collapse(2)
+        for (int64_t b = 0; b < B; ++b) {
+            for (int64_t i = row_begin; i < row_end; ++i) {
+                int32_t *o = out + (b * n_rows + (i - row_begin)) * W;
+                for (int64_t s = 0; s < W; ++s) o[s] = -1;
+                const int64_t t = q_offset + i;
+                if (t >= seq_lens[b]) continue; /* padding query */
+                const int64_t nv = (t + 1) / c; /* <= n_blocks: the caller checks it */
+                for (int64_t j = 0; j < nv; ++j) {
+                    cand[j].score = block_score(iq + (b * S_q + i) * H * D, ck + (b * n_blocks + j) * D, H, D);
+                    cand[j].block = j;
+                }
+                qsort(cand, (size_t)nv, sizeof(scored_block), cmp_best_first);
+                const int64_t m = kb < nv ? kb : nv;
+                for (int64_t r = 0; r < m; ++r) kept[r] = cand[r].block;
+                qsort(kept, (size_t)m, sizeof(int64_t), cmp_int64);
+                for (int64_t r = 0; r < m; ++r)
+                    for (int64_t u = 0; u < c; ++u) o[r * c + u] = (int32_t)(kept[r] * c + u);
+                for (int64_t u = 0; nv * c + u <= t; ++u) o[token_budget + u] = (int32_t)(nv * c + u);
+            }
+        }
+        free(cand);
+        free(kept);
     }
 }

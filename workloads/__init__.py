@@ -10,7 +10,9 @@ oracle and the HIP path consume exactly the same arrays.
 """
 
 from .generators import (  # noqa: F401
+    SELECT_WORKLOADS,
     WORKLOADS,
+    SelectWorkload,
     Workload,
     bf16_bits_to_float32,
     float32_to_bf16_bits,
@@ -18,5 +20,7 @@ from .generators import (  # noqa: F401
     make_inputs,
     make_qkv,
     make_routes,
+    make_select_inputs,
     random_dout,
+    random_select_case,
 )

@@ -309,3 +309,99 @@ def random_small_case(seed: int, B: int, S_q: int, S_kv: int, Hq: int, Hkv: int,
     empty = rng.random((B, S_q)) < p_empty
     routes[empty] = -1
     return q, k, v, routes.astype(route_dtype)
+
+
+# --------------------------------------------------------------------------
+# route-selection inputs: index queries and compressed block keys
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class SelectWorkload:
+    """Shapes of one route-selection case (index heads H, index head dim D)."""
+
+    name: str
+    number: int  # 1-based, fixes the seed
+    B: int
+    S_q: int
+    S_global: int
+    H: int
+    D: int
+    compress_ratio: int
+    token_budget: int
+    lengths: tuple
+    q_offset: int = 0
+    description: str = ""
+
+    @property
+    def n_blocks(self) -> int:
+        return self.S_global // self.compress_ratio
+
+    @property
+    def width(self) -> int:
+        return self.token_budget + self.compress_ratio - 1
+
+    @property
+    def seed(self) -> int:
+        return 2000 + self.number
+
+
+SELECT_WORKLOADS = {
+    w.name: w
+    for w in [
+        SelectWorkload("sel_tiny", 1, B=2, S_q=256, S_global=256, H=4, D=64, compress_ratio=4, token_budget=32,
+                       lengths=(256, 197), description="B=2 S=256 H=4 D=64 c=4 budget=32, lengths 256/197"),
+        SelectWorkload("sel_right_padded", 2, B=2, S_q=4096, S_global=4096, H=16, D=128, compress_ratio=4,
+                       token_budget=512, lengths=(4096, 3000),
+                       description="B=2 S=4096 H=16 D=128 c=4 budget=512, lengths 4096/3000"),
+        SelectWorkload("sel_cp_slice", 3, B=1, S_q=8192, S_global=32768, H=16, D=128, compress_ratio=4,
+                       token_budget=2048, lengths=(32768,), q_offset=24576,
+                       description="B=1 S_q=8192 at offset 24576 of 32768, H=16 D=128 c=4 budget=2048"),
+        SelectWorkload("sel_long", 4, B=1, S_q=65536, S_global=65536, H=16, D=128, compress_ratio=4,
+                       token_budget=2048, lengths=(65536,),
+                       description="B=1 S=65536 H=16 D=128 c=4 budget=2048 (16384 blocks)"),
+    ]
+}
+
+
+def _unit_rms_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) vectors along the last axis scaled to unit RMS in float32, rounded to bfloat16 bits."""
+    out = np.empty(shape, dtype=np.uint16)
+    D = shape[-1]
+    flat = out.reshape(-1, D)
+    step = max(1, (1 << 22) // D)
+    for s in range(0, flat.shape[0], step):
+        n = min(step, flat.shape[0] - s)
+        x = rng.standard_normal((n, D), dtype=np.float32)
+        x /= np.sqrt(np.mean(x * x, axis=1, keepdims=True, dtype=np.float32))
+        flat[s:s + n] = float32_to_bf16_bits(x)
+    return out
+
+
+def make_select_inputs(name: str):
+    """Return ``(workload, iq [B,S_q,H,D], ck [B,n_blocks,1,D], seq_lens int64 [B])``.
+
+    Index queries and block keys are unit-RMS random vectors (the pages feed
+    RMS-normalised, rotated projections; their weights are not available, so
+    random directions stand in), as bfloat16 bits.
+    """
+    w = SELECT_WORKLOADS[name]
+    rq, rk = [np.random.Generator(np.random.PCG64(c)) for c in np.random.SeedSequence(w.seed).spawn(2)]
+    iq = _unit_rms_bf16(rq, (w.B, w.S_q, w.H, w.D))
+    ck = _unit_rms_bf16(rk, (w.B, w.n_blocks, 1, w.D))
+    return w, iq, ck, np.array(w.lengths, dtype=np.int64)
+
+
+def random_select_case(seed: int, B: int, S_q: int, H: int, D: int, n_blocks: int, integer: bool = False):
+    """Index queries [B,S_q,H,D] and block keys [B,n_blocks,1,D] as bfloat16 bits.
+
+    ``integer=True`` draws small integers in [-3, 3]: every product and sum is
+    then exact in float32, and equal scores (ties) are frequent.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if integer:
+        iq = rng.integers(-3, 4, size=(B, S_q, H, D)).astype(np.float32)
+        ck = rng.integers(-3, 4, size=(B, n_blocks, 1, D)).astype(np.float32)
+    else:
+        iq = rng.standard_normal((B, S_q, H, D), dtype=np.float32)
+        ck = rng.standard_normal((B, n_blocks, 1, D), dtype=np.float32)
+    return float32_to_bf16_bits(iq), float32_to_bf16_bits(ck)

@@ -52,6 +52,8 @@ extern "C" {
 #define QSA_ERR_WORKSPACE -10   /* workspace NULL or smaller than required             */
 #define QSA_ERR_LIMIT -11       /* K > QSA_MAX_ROUTES or G > QSA_MAX_GROUP             */
 #define QSA_ERR_HIP -12         /* a HIP launch reported an error                      */
+#define QSA_ERR_SELECTION -13   /* token_budget or compress_ratio < 1, or query rows   */
+                                /* outside [0, S_global) (route selection)             */
 
 /* ---- constants --------------------------------------------------------- */
 #define QSA_INT32 0          /* routes are int32_t (sign-extended before the checks) */
@@ -59,6 +61,9 @@ extern "C" {
 #define QSA_TILE 128         /* rows and columns of one membership tile              */
 #define QSA_MAX_ROUTES 16384 /* largest K (route slots per query row)               */
 #define QSA_MAX_GROUP 16     /* largest G = Hq / Hkv                                */
+#define QSA_MAX_SELECT_BLOCKS 4096   /* largest token_budget / compress_ratio          */
+#define QSA_MAX_VISIBLE_BLOCKS 65536 /* largest floor(S_global / compress_ratio)       */
+#define QSA_MAX_INDEX_HEADS 64       /* largest H (index heads) of route selection     */
 
 /*
  * qsa_preprocess -- validate, deduplicate and compact the routes; optionally
@@ -242,6 +247,62 @@ int qsa_backward(const void *q, const int64_t q_strides[4], const void *k, const
                  size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
+/*
+ * qsa_select_workspace_size -- bytes of fp32 score workspace with which
+ * qsa_select_token_ids scores every query row in one pass:
+ * rows_rounded * ld * 4, ld = round_up(floor((q_offset + S_q) / c), 64),
+ * rows_rounded = B * S_q rounded up to whole row tiles (16 rows for H <= 16,
+ * 8 for H <= 32, 4 for H <= 64).  Any workspace of at least one row tile
+ * (tile_rows * ld * 4 bytes) also works: the rows are then processed in
+ * passes of as many whole tiles as fit, in order, on the same stream.
+ * Returns 0 when an argument is out of range.
+ */
+size_t qsa_select_workspace_size(int64_t B, int64_t S_q, int64_t H, int64_t q_offset, int64_t compress_ratio);
+
+/*
+ * qsa_select_token_ids -- route selection by compressed-block scores: the
+ * producer of the routes the attention entry points consume.
+ *
+ * Definition (qsa page, `select_qsa_token_ids`; `Qwen3_8_FlashNextQSAIndexer`
+ * for the output width token_budget + compress_ratio - 1): local query row i
+ * stands at global position t = q_offset + i (q_offset = cp_rank * S_q under
+ * contiguous context parallelism, 0 otherwise).  With c = compress_ratio and
+ * kb = token_budget / c (integer division):
+ *   - t >= seq_lens[b] (a right-padding query): every slot is -1;
+ *   - otherwise the nv = floor((t+1)/c) complete blocks are visible and block
+ *     j scores sum_h relu(<index_q[b,i,h,:], block_k[b,j,0,:]>) / sqrt(D);
+ *     the m = min(kb, nv) best blocks are kept, equal scores going to the
+ *     smaller block index (a reading; the page fixes no tie rule);
+ *   - slots [0, m*c): the kept blocks in ascending order (a reading), each as
+ *     its c token IDs j*c .. j*c+c-1; slots [m*c, token_budget): -1;
+ *   - slots [token_budget, token_budget + c - 1): the tokens nv*c .. t of the
+ *     incomplete causal tail (0 to c-1 of them), then -1.
+ * Scores are computed with bf16 products and fp32 sums and compared in fp32
+ * (the page scores in an fp32 tensor).  IDs are global token positions.
+ *
+ *   index_q     [B, S_q, H, D] bf16 (normalised, rotated index queries),
+ *               last stride 1, rows 16-B aligned, other strides multiples of 8.
+ *   block_k     [B, n_blocks, 1, D] bf16 (pooled, normalised, rotated block
+ *               keys), same layout rules; n_blocks >= floor(S_global / c);
+ *               the size-1 head dimension's stride is ignored.
+ *   seq_lens    [B] int64 right-padded logical lengths in global positions,
+ *               read on the device (values outside [0, S_global] behave as
+ *               clamped to it).
+ *   S_global    padded global sequence length: q_offset + S_q <= S_global.
+ *   D in {64, 128, 256}; 1 <= H <= QSA_MAX_INDEX_HEADS;
+ *   kb <= QSA_MAX_SELECT_BLOCKS; floor(S_global / c) <= QSA_MAX_VISIBLE_BLOCKS.
+ *   out         OUT [B, S_q, token_budget + c - 1] int32, contiguous.
+ *   workspace   device memory of at least one row tile (see
+ *               qsa_select_workspace_size), 256-B aligned; may be NULL when
+ *               no row sees more than kb blocks.
+ * Errors: NULL_POINTER, EMPTY_DIM, SELECTION, HEAD_DIM, LAYOUT, ALIAS,
+ * WORKSPACE, LIMIT, HIP.
+ */
+int qsa_select_token_ids(const void *index_q, const int64_t q_strides[4], const void *block_k,
+                         const int64_t k_strides[4], const int64_t *seq_lens, int64_t B, int64_t S_q, int64_t H,
+                         int64_t D, int64_t S_global, int64_t q_offset, int64_t token_budget, int64_t compress_ratio,
+                         int32_t *out, void *workspace, size_t workspace_bytes, void *stream);
+
 const char *qsa_status_string(int status);
 
 #ifdef __cplusplus

@@ -13,7 +13,10 @@ runs in the library's HIP kernels; there is no other code path.
 * ``qsa_forward(q, k, v, routes, scale=None)``
 * ``qsa_forward_preprocessed(q, k, v, route_list, route_count, scale=None, return_lse=False)``
 * ``qsa_backward(q, k, v, out, dout, lse, route_list, route_count, scale=None)``
-* ``qsa_forward_workspace_size(B, S_q, K)``, ``qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)``
+* ``qsa_select_token_ids(index_queries, compressed_keys, sequence_lengths, token_budget, compress_ratio,
+  query_position_offset=0, global_sequence_length=None, query_chunk_size=None)``
+* ``qsa_forward_workspace_size(B, S_q, K)``, ``qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)``,
+  ``qsa_select_workspace_size(B, S_q, H, q_offset, compress_ratio)``
 * ``qsa_status_string(status)``
 """
 
@@ -80,6 +83,11 @@ def lib() -> ctypes.CDLL:
         L.qsa_backward.argtypes = [p, P64, p, P64, p, P64, p, p, P64, p, p, p, i64, i64, i64, i64, i64, i64, i64,
                                    ctypes.c_float, p, p, p, p, ctypes.c_size_t, p]
         L.qsa_backward.restype = i32
+        L.qsa_select_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+        L.qsa_select_workspace_size.restype = ctypes.c_size_t
+        L.qsa_select_token_ids.argtypes = [p, P64, p, P64, p, i64, i64, i64, i64, i64, i64, i64, i64, p, p,
+                                           ctypes.c_size_t, p]
+        L.qsa_select_token_ids.restype = i32
         _lib = L
     return _lib
 
@@ -94,6 +102,10 @@ def qsa_forward_workspace_size(B: int, S_q: int, K: int) -> int:
 
 def qsa_backward_workspace_size(B: int, S_q: int, S_kv: int, Hq: int, Hkv: int, D: int, K: int) -> int:
     return int(lib().qsa_backward_workspace_size(int(B), int(S_q), int(S_kv), int(Hq), int(Hkv), int(D), int(K)))
+
+
+def qsa_select_workspace_size(B: int, S_q: int, H: int, q_offset: int, compress_ratio: int) -> int:
+    return int(lib().qsa_select_workspace_size(int(B), int(S_q), int(H), int(q_offset), int(compress_ratio)))
 
 
 def _check(status: int, where: str) -> None:
@@ -309,7 +321,56 @@ def qsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
     return dq, dk, dv
 
 
+def qsa_select_token_ids(index_queries: torch.Tensor, compressed_keys: torch.Tensor, sequence_lengths: torch.Tensor,
+                         token_budget: int, compress_ratio: int, query_position_offset: int = 0,
+                         global_sequence_length: Optional[int] = None, query_chunk_size: Optional[int] = None,
+                         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Route selection: int32 token IDs [B, S_q, token_budget + compress_ratio - 1] (-1 = empty slot).
+
+    ``index_queries`` bf16 [B,S_q,H,D], ``compressed_keys`` bf16 [B,n_blocks,1,D] with
+    ``n_blocks >= global_sequence_length // compress_ratio``, ``sequence_lengths`` int [B]
+    (right-padded logical lengths, global positions; read on the device, no host sync).
+    ``global_sequence_length`` defaults to the local query length.  ``query_chunk_size``
+    bounds the rows scored per pass (fp32 scores [rows, visible blocks]); ``None`` scores
+    every row in one pass.  Chunking changes no result.
+    """
+    dev = _require_gpu(index_queries, compressed_keys, sequence_lengths)
+    iq = _bf16_operand(index_queries, "index_queries")
+    ck = _bf16_operand(compressed_keys, "compressed_keys")
+    B, S_q, H, D = iq.shape
+    c, budget, q_off = int(compress_ratio), int(token_budget), int(query_position_offset)
+    S_global = S_q if global_sequence_length is None else int(global_sequence_length)
+    if ck.shape[0] != B or ck.shape[2] != 1 or ck.shape[3] != D:
+        raise ValueError(f"compressed_keys must be [B, n_blocks, 1, D] = [{B}, n, 1, {D}], got {tuple(ck.shape)}")
+    if c >= 1 and ck.shape[1] < S_global // c:
+        raise ValueError(f"compressed_keys holds {ck.shape[1]} blocks, fewer than {S_global} // {c}")
+    if tuple(sequence_lengths.shape) != (B,):
+        raise ValueError(f"sequence_lengths must be [B] = [{B}]")
+    lens = sequence_lengths.to(torch.int64).contiguous()
+    width = budget + c - 1
+    if out is None:
+        out = torch.empty((B, S_q, max(width, 0)), dtype=torch.int32, device=dev)
+    elif out.dtype != torch.int32 or tuple(out.shape) != (B, S_q, width) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous int32 tensor of shape {(B, S_q, width)}")
+    if workspace is None:
+        full = qsa_select_workspace_size(B, S_q, H, q_off, c)
+        ws_bytes = full
+        if query_chunk_size is not None and full > 0:
+            tile_rows = 16 if H <= 16 else (8 if H <= 32 else 4)
+            tiles = -(-B * S_q // tile_rows)
+            per_tile = full // tiles
+            ws_bytes = min(full, max(1, -(-int(query_chunk_size) // tile_rows)) * per_tile)
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().qsa_select_token_ids(_ptr(iq), _strides(iq), _ptr(ck), _strides(ck), _ptr(lens), B, S_q, H, D,
+                                    S_global, q_off, budget, c, _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st, "qsa_select_token_ids")
+    return out
+
+
 __all__ = [
+    "qsa_select_token_ids",
+    "qsa_select_workspace_size",
     "qsa_preprocess",
     "qsa_tile_lists",
     "qsa_forward",

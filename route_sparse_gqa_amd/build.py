@@ -29,6 +29,7 @@ SOURCES = [
     "attention_backward.hip",
     "key_segments.hip",
     "tile_lists.hip",
+    "route_select.hip",
     "qsa_api.cpp",
 ]
 

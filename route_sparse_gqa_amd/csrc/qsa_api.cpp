@@ -9,6 +9,7 @@
 // silent fallback to another path (qsa page, `qsa_gqa_attention`).
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 
 #include "../../include/qsa.h"
@@ -103,8 +104,13 @@ QSA_EXPORT const char* qsa_status_string(int status) {
     case QSA_ERR_LAYOUT: return "tensor layout unsupported (last stride 1, 16-byte aligned rows required)";
     case QSA_ERR_ALIAS: return "an output overlaps an input or another output";
     case QSA_ERR_WORKSPACE: return "workspace missing or too small";
-    case QSA_ERR_LIMIT: return "size beyond a library limit (K <= 16384, G <= 16, grid size)";
+    case QSA_ERR_LIMIT:
+      return "size beyond a library limit (K <= 16384, G <= 16, index heads <= 64, kept blocks <= 4096, "
+             "visible blocks <= 65536, grid size)";
     case QSA_ERR_HIP: return "HIP launch error";
+    case QSA_ERR_SELECTION:
+      return "selection arguments out of range (token_budget >= 1, compress_ratio >= 1, "
+             "0 <= q_offset, q_offset + S_q <= S_global)";
     default: return "unknown status";
   }
 }
@@ -452,4 +458,95 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
   rc = hip_status(qsa::launch_key_segments(route_list, route_count, B, S_q, K, S_kv, w, st));
   if (rc != QSA_OK) return rc;
   return hip_status(qsa::launch_attention_dkdv(a, st));
+}
+
+namespace {
+
+// Shape checks of route selection; fills the derived sizes.
+struct SelectSizes {
+  int64_t width = 0, rows = 0, tile_rows = 0, ld = 0, tiles = 0, full_bytes = 0, tile_bytes = 0;
+};
+
+int check_select_dims(int64_t B, int64_t S_q, int64_t H, int64_t D, int64_t S_global, int64_t q_offset,
+                      int64_t token_budget, int64_t c, SelectSizes* z) {
+  if (B < 1 || S_q < 1 || H < 1 || D < 1 || S_global < 1) return QSA_ERR_EMPTY_DIM;
+  if (token_budget < 1 || c < 1 || q_offset < 0 || q_offset > S_global || S_q > S_global - q_offset)
+    return QSA_ERR_SELECTION;
+  if (D != 64 && D != 128 && D != 256) return QSA_ERR_HEAD_DIM;
+  if (H > QSA_MAX_INDEX_HEADS || S_global > kMaxGrid || token_budget / c > QSA_MAX_SELECT_BLOCKS ||
+      S_global / c > QSA_MAX_VISIBLE_BLOCKS || token_budget > kMaxGrid - c)
+    return QSA_ERR_LIMIT;
+  z->width = token_budget + c - 1;
+  if (!mul_ok(B, S_q, &z->rows) || z->rows > kMaxGrid) return QSA_ERR_LIMIT;
+  int64_t outs = 0;
+  if (!mul_ok(z->rows, z->width, &outs) || outs > (INT64_MAX >> 3)) return QSA_ERR_LIMIT;
+  z->tile_rows = qsa::select_rows_per_tile(H);
+  z->ld = qsa::select_score_ld(S_q, q_offset, c);
+  z->tiles = B * ((S_q + z->tile_rows - 1) / z->tile_rows);
+  const int64_t n_chunks = (z->ld + 127) / 128;
+  if ((z->tiles + 7) / 8 * 8 > kMaxGrid / n_chunks) return QSA_ERR_LIMIT;
+  z->tile_bytes = 4 * z->tile_rows * z->ld;
+  if (!mul_ok(z->tiles, z->tile_bytes, &z->full_bytes) || z->full_bytes > (INT64_MAX >> 2)) return QSA_ERR_LIMIT;
+  return QSA_OK;
+}
+
+}  // namespace
+
+QSA_EXPORT size_t qsa_select_workspace_size(int64_t B, int64_t S_q, int64_t H, int64_t q_offset,
+                                            int64_t compress_ratio) {
+  SelectSizes z;
+  if (q_offset < 0 || compress_ratio < 1 || S_q < 1 || q_offset > INT64_MAX - S_q) return 0;
+  // the smallest S_global and budget these sizes allow: the workspace does not depend on them
+  if (check_select_dims(B, S_q, H, 64, q_offset + S_q, q_offset, 1, compress_ratio, &z) != QSA_OK &&
+      check_select_dims(B, S_q, H, 64, q_offset + S_q, q_offset, compress_ratio, compress_ratio, &z) != QSA_OK)
+    return 0;
+  return round_up(static_cast<size_t>(z.full_bytes), kWorkspaceAlign);
+}
+
+QSA_EXPORT int qsa_select_token_ids(const void* index_q, const int64_t q_strides[4], const void* block_k,
+                                    const int64_t k_strides[4], const int64_t* seq_lens, int64_t B, int64_t S_q,
+                                    int64_t H, int64_t D, int64_t S_global, int64_t q_offset, int64_t token_budget,
+                                    int64_t compress_ratio, int32_t* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  SelectSizes z;
+  if (int st = check_select_dims(B, S_q, H, D, S_global, q_offset, token_budget, compress_ratio, &z)) return st;
+  if (index_q == nullptr || q_strides == nullptr || block_k == nullptr || k_strides == nullptr ||
+      seq_lens == nullptr || out == nullptr)
+    return QSA_ERR_NULL_POINTER;
+  if (int st = check_bf16_tensor(index_q, q_strides)) return st;
+  const int64_t ks[4] = {k_strides[0], k_strides[1], 0, k_strides[3]};  // the size-1 head dim is not walked
+  if (int st = check_bf16_tensor(block_k, ks)) return st;
+  if (!aligned(seq_lens, 8) || !aligned(out, 4)) return QSA_ERR_LAYOUT;
+  const int64_t c = compress_ratio;
+  const int64_t nv_all = (q_offset + S_q) / c;
+  const bool scoring = token_budget / c > 0 && nv_all > token_budget / c;
+  if (scoring && (workspace == nullptr || workspace_bytes < static_cast<size_t>(z.tile_bytes) ||
+                  !aligned(workspace, kWorkspaceAlign)))
+    return QSA_ERR_WORKSPACE;
+
+  const int64_t n_blocks = S_global / c;
+  const int64_t qshape[4] = {B, S_q, H, D}, kshape[4] = {B, n_blocks > 0 ? n_blocks : 1, 1, D};
+  const Range r_q = extent(index_q, qshape, q_strides, 4, 2);
+  const Range r_k = extent(block_k, kshape, ks, 4, 2);
+  const Range r_len = dense(seq_lens, 8 * B);
+  const Range r_out = dense(out, 4 * z.rows * z.width);
+  const size_t used = std::min(workspace_bytes, static_cast<size_t>(z.full_bytes));
+  const Range r_ws = scoring ? dense(workspace, static_cast<int64_t>(used)) : Range{};
+  if (overlap(r_out, r_q) || overlap(r_out, r_k) || overlap(r_out, r_len) || overlap(r_out, r_ws) ||
+      overlap(r_ws, r_q) || overlap(r_ws, r_k) || overlap(r_ws, r_len))
+    return QSA_ERR_ALIAS;
+
+  qsa::SelectArgs a;
+  a.iq = static_cast<const uint16_t*>(index_q);
+  a.ck = static_cast<const uint16_t*>(block_k);
+  std::memcpy(a.qs, q_strides, sizeof a.qs);
+  std::memcpy(a.cs, ks, sizeof a.cs);
+  a.seq_lens = seq_lens;
+  a.B = B; a.S_q = S_q; a.H = H; a.D = D; a.q_offset = q_offset;
+  a.token_budget = token_budget; a.compress_ratio = c;
+  a.out = out;
+  a.scores = static_cast<float*>(workspace);
+  a.workspace_bytes = scoring ? used : 0;
+  (void)hipGetLastError();
+  return hip_status(qsa::launch_select(a, as_stream(stream)));
 }

@@ -95,6 +95,23 @@ struct BwdArgs {
 hipError_t launch_attention_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_attention_dkdv(const BwdArgs& a, hipStream_t stream);
 
+// Route selection by compressed-block scores (scores into `scores`, then a
+// per-row top-k), in passes of whole row tiles that fit workspace_bytes.
+struct SelectArgs {
+  const uint16_t* iq;  // [B, S_q, H, D] bf16
+  const uint16_t* ck;  // [B, n_blocks, 1, D] bf16
+  int64_t qs[4], cs[4];
+  const int64_t* seq_lens;  // [B]
+  int64_t B, S_q, H, D, q_offset, token_budget, compress_ratio;
+  int32_t* out;    // [B, S_q, token_budget + compress_ratio - 1]
+  float* scores;   // workspace
+  size_t workspace_bytes;
+};
+
+int64_t select_rows_per_tile(int64_t H);  // query rows per score workgroup (16, 8 or 4)
+int64_t select_score_ld(int64_t S_q, int64_t q_offset, int64_t c);  // floats per score row
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
 // Upper bound of the partial-sum slots the split can use, per KV head.
 inline int64_t seg_max_slots(int64_t max_parts, int64_t capacity) {
   const int64_t by_capacity = (capacity + kSegMinPart - 1) / kSegMinPart;

@@ -1,0 +1,390 @@
+// Route selection for gfx950: compressed-block scores on the matrix cores,
+// then a per-row top-k by radix select, expanded to token IDs with the
+// incomplete causal tail appended.
+//
+// Definition: qsa page, `select_qsa_token_ids`.  Query row i stands at
+// global position t = q_offset + i and sees nv = floor((t + 1) / c) complete
+// blocks; block j scores sum_h relu(<q[t,h], k[j]>) / sqrt(D) (the positive
+// 1/sqrt(D) factor orders nothing, so the kernels rank the unscaled sums);
+// the best kb = token_budget / c blocks are kept (equal scores: the smaller
+// block index), written in ascending block order as c token IDs each, then
+// the tokens nv*c .. t of the incomplete tail go to the last c - 1 slots.
+// Rows at or past their batch's logical length are all -1.
+//
+// Design:
+//  * select_scores_kernel -- a workgroup owns 16/HG query rows of one batch
+//    (HG = head groups of 16) and 128 consecutive blocks.  The 128 block
+//    keys are staged once in LDS (row stride 2D + 16 bytes, so the operand
+//    reads are conflict-free) and shared by the four waves.  Per 16 blocks a
+//    wave runs v_mfma_f32_16x16x32_bf16 with the 16 index heads of a row on
+//    M (A operand = the row's queries, held in registers for the whole
+//    workgroup) and the 16 blocks on N; lane (n, g) then holds heads
+//    4g .. 4g+3 of block n, so the relu and three adds give a partial sum and
+//    a two-step exchange across the lane groups (xor 32, then xor 16) both
+//    completes the sums of four rows and leaves row g's sum in lane group g,
+//    which stores it.  Workgroups are mapped so that every block chunk of a
+//    row tile runs on the same XCD (the tile's queries stay in that L2).
+//    fp32 scores go to a [rows, ld] workspace, only for rows that see more
+//    than kb blocks, only for visible blocks.
+//  * select_topk_kernel -- one workgroup per query row.  Scores sit in
+//    registers (E per thread, coalesced loads); three LDS-histogram passes
+//    over the float bit patterns (non-negative floats order like their bits;
+//    11, 11 and 10 bits) find the kb-th largest value tau and how many of
+//    the values equal to tau to keep.  Ballots build bitmaps of the values
+//    above tau and of those equal to it; a block prefix over the words keeps
+//    the lowest-index ties and places every kept block at its rank, in
+//    ascending block order.  The row is then written coalesced.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "qsa.h"
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kScoreThreads = 256;
+constexpr int kScoreBlocks = 128;  // blocks per score workgroup: 8 MFMA tiles of 16
+constexpr int kBins = 2048;        // histogram bins of one radix pass (11 bits)
+
+template <int D>
+struct SelGeo {
+  static constexpr int kSteps = D / 32;   // K-slices of one 16x16x32 product
+  static constexpr int kStride = D + 8;   // LDS row stride (bf16): 2D + 16 bytes
+  static constexpr int kPieces = D / 8;   // 16-byte pieces of one key row
+};
+
+__device__ __forceinline__ int64_t clamp_len(int64_t L, int64_t q_end) { return L < 0 ? 0 : (L > q_end ? q_end : L); }
+
+template <int D, int HG>
+__global__ void __launch_bounds__(kScoreThreads)
+    select_scores_kernel(const uint16_t* __restrict__ iq, int64_t qs0, int64_t qs1, int64_t qs2,
+                         const uint16_t* __restrict__ ck, int64_t cs0, int64_t cs1,
+                         const int64_t* __restrict__ seq_lens, int64_t S_q, int64_t H, int64_t q_offset,
+                         int64_t c, int64_t kb, int64_t tile0, int64_t n_tiles, int64_t tiles_per_batch,
+                         int64_t n_chunks, int64_t row_base, int64_t ld, float* __restrict__ scores) {
+  using Geo = SelGeo<D>;
+  constexpr int RW = 4 / HG;   // query rows per wave
+  constexpr int RPW = 4 * RW;  // query rows per workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t kslab[kScoreBlocks * Geo::kStride];
+
+  // Workgroup w -> (tile, chunk): tiles go in groups of 8, tile 8q + x to
+  // workgroups congruent to x mod 8, i.e. always to the same XCD.
+  const int64_t w = blockIdx.x;
+  const int64_t group = w / (8 * n_chunks), rem = w % (8 * n_chunks);
+  const int64_t local_tile = group * 8 + rem % 8;
+  const int64_t chunk = rem / 8;
+  if (local_tile >= n_tiles) return;  // every exit precedes the only barrier
+  const int64_t tile = tile0 + local_tile;
+  const int64_t b = tile / tiles_per_batch;
+  const int64_t i0 = (tile % tiles_per_batch) * RPW;
+  const int64_t q_end = q_offset + S_q;
+  const int64_t L = clamp_len(seq_lens[b], q_end);
+  // Non-padding rows are a prefix of the tile; the last one sees the most blocks.
+  const int64_t i_last = min(min(i0 + RPW - 1, S_q - 1), L - 1 - q_offset);
+  if (i_last < i0) return;
+  const int64_t nv_max = (q_offset + i_last + 1) / c;
+  const int64_t j0 = chunk * kScoreBlocks;
+  if (nv_max <= kb || j0 >= nv_max) return;
+  const int nblk = static_cast<int>(min(static_cast<int64_t>(kScoreBlocks), nv_max - j0));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int m = lane & 15;  // head row of the A operand; block column of B and of the result
+  const int g = lane >> 4;  // k-group of the operands; head quad of the result
+
+  // Block keys j0 .. j0 + nblk - 1 into LDS (zeros past them).
+  const uint16_t* kbase = ck + b * cs0;
+  for (int p = tid; p < kScoreBlocks * Geo::kPieces; p += kScoreThreads) {
+    const int blk = p / Geo::kPieces, piece = p % Geo::kPieces;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (blk < nblk) v = load16(kbase + (j0 + blk) * cs1 + 8 * piece);
+    *reinterpret_cast<u32x4*>(kslab + blk * Geo::kStride + 8 * piece) = v;
+  }
+
+  // Queries as the A operand: lane (m, g) holds head 16 hg + m, dims 32s + 8g .. +7.
+  bf16x8 qf[RW][HG][Geo::kSteps];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int64_t i = i0 + wave * RW + r;
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      const int head = 16 * hg + m;
+      const bool ok = i <= i_last && head < H;
+      const uint16_t* qp = iq + b * qs0 + (ok ? i : 0) * qs1 + (ok ? head : 0) * qs2 + 8 * g;
+#pragma unroll
+      for (int s = 0; s < Geo::kSteps; ++s)
+        qf[r][hg][s] = ok ? __builtin_bit_cast(bf16x8, load16(qp + 32 * s)) : bf16x8{};
+    }
+  }
+
+  // Row stored by this lane (lane group g owns row g of the wave) and its visible blocks.
+  const int64_t my_i = i0 + wave * RW + g;
+  const bool my_row = g < RW && my_i <= i_last;
+  const int64_t my_nv = my_row ? (q_offset + my_i + 1) / c : 0;
+  const bool my_store = my_row && my_nv > kb;
+  float* my_out = scores + (my_store ? (b * S_q + my_i - row_base) * ld : 0);
+
+  __syncthreads();
+
+  const int n_sub = (nblk + 15) / 16;
+  for (int sc = 0; sc < n_sub; ++sc) {
+    bf16x8 kf[Geo::kSteps];
+    const uint16_t* kp = kslab + (16 * sc + m) * Geo::kStride + 8 * g;
+#pragma unroll
+    for (int s = 0; s < Geo::kSteps; ++s) kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 32 * s));
+
+    float part[4] = {0.f, 0.f, 0.f, 0.f};  // rows past RW stay 0
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      float sum = 0.f;
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < Geo::kSteps; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[r][hg][s], kf[s], acc, 0, 0, 0);
+        sum += fmaxf(acc[0], 0.f) + fmaxf(acc[1], 0.f) + fmaxf(acc[2], 0.f) + fmaxf(acc[3], 0.f);
+      }
+      part[r] = sum;
+    }
+    // Lane groups g and g^2 swap halves: groups 0, 1 keep rows 0, 1; groups 2, 3 keep rows 2, 3.
+    const bool upper = g >= 2;
+    float keep0 = upper ? part[2] : part[0];
+    float keep1 = upper ? part[3] : part[1];
+    keep0 += __shfl_xor(upper ? part[0] : part[2], 32);
+    keep1 += __shfl_xor(upper ? part[1] : part[3], 32);
+    // Groups g and g^1: even groups finish their first kept row, odd ones the second.
+    const bool odd = (g & 1) != 0;
+    float total = (odd ? keep1 : keep0) + __shfl_xor(odd ? keep0 : keep1, 16);
+    total = total > 0.f ? total : 0.f;  // one zero: -0.0 would order below +0.0 by bits
+    const int64_t j = j0 + 16 * sc + m;
+    if (my_store && j < my_nv) my_out[j] = total;
+  }
+}
+
+// Exclusive prefix sum of x over the workgroup's threads (in thread order),
+// and the total.  Every thread must call it.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int q = 0; q < NT / 64; ++q) {
+    const int v = wave_tot[q];
+    before += q < wave ? v : 0;
+    sum += v;
+  }
+  __syncthreads();  // wave_tot is reused by the next call
+  *total = sum;
+  return before + incl - x;
+}
+
+template <int NT, int E>
+__global__ void __launch_bounds__(NT)
+    select_topk_kernel(const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ seq_lens,
+                       int64_t S_q, int64_t q_offset, int64_t c, int64_t kb, int64_t budget, int64_t W,
+                       int64_t row_base, int32_t* __restrict__ out) {
+  constexpr int kWaves = NT / 64;
+  constexpr int kWords = NT * E / 64;  // <= NT: one bitmap word per thread at most
+  constexpr int kBinsPerThread = kBins / NT;
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint64_t gt_words[kWords];
+  __shared__ uint64_t eq_words[kWords];
+  __shared__ int32_t kept[QSA_MAX_SELECT_BLOCKS];
+  __shared__ int wave_tot[kWaves];
+  __shared__ int found[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t row = row_base + blockIdx.x;  // b * S_q + i
+  const int64_t b = row / S_q, i = row % S_q;
+  const int64_t t = q_offset + i;
+  int32_t* orow = out + row * W;
+  if (t >= clamp_len(seq_lens[b], q_offset + S_q)) {  // padding query
+    for (int64_t s = tid; s < W; s += NT) orow[s] = -1;
+    return;
+  }
+  const int64_t nv = (t + 1) / c;
+  const int64_t tail0 = nv * c, tail_n = t + 1 - tail0;
+  const bool sparse = kb > 0 && nv > kb;
+  const int64_t mc = (kb < nv ? kb : nv) * c;  // slots holding kept-block tokens
+
+  if (sparse) {  // workgroup-uniform
+    const float* srow = scores + (row - row_base) * ld;
+    const int n = static_cast<int>(nv);
+    const int ne = (n + NT - 1) / NT;
+    uint32_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = e * NT + tid;
+      key[e] = (e < ne && idx < n) ? __float_as_uint(srow[idx]) : 0u;
+    }
+    uint32_t prefix = 0, hi_mask = 0;
+    int remaining = static_cast<int>(kb);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const int sh = p == 0 ? 21 : (p == 1 ? 10 : 0);
+      const uint32_t dmask = p == 2 ? 0x3FFu : 0x7FFu;
+      for (int q = tid; q < kBins; q += NT) hist[q] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int idx = e * NT + tid;
+        if (e < ne && idx < n && (key[e] & hi_mask) == prefix) atomicAdd(&hist[(key[e] >> sh) & dmask], 1u);
+      }
+      __syncthreads();
+      int local = 0;
+#pragma unroll
+      for (int q = 0; q < kBinsPerThread; ++q) local += static_cast<int>(hist[tid * kBinsPerThread + q]);
+      int total = 0;
+      const int before = block_exclusive_scan<NT>(local, wave_tot, &total);
+      const int above = total - before - local;  // candidates in higher bins than this thread's
+      if (above < remaining && above + local >= remaining) {
+        int acc = above;
+        for (int q = kBinsPerThread - 1; q >= 0; --q) {
+          const int h = static_cast<int>(hist[tid * kBinsPerThread + q]);
+          if (acc + h >= remaining) {
+            found[0] = tid * kBinsPerThread + q;
+            found[1] = remaining - acc;
+            break;
+          }
+          acc += h;
+        }
+      }
+      __syncthreads();
+      prefix |= static_cast<uint32_t>(found[0]) << sh;
+      hi_mask |= dmask << sh;
+      remaining = found[1];
+      __syncthreads();  // found and hist are rewritten by the next pass
+    }
+    const uint32_t tau = prefix;  // the kb-th largest value; keep `remaining` of the values equal to it
+
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = e * NT + tid;
+      const bool valid = e < ne && idx < n;
+      const uint64_t bg = __ballot(valid && key[e] > tau);
+      const uint64_t be = __ballot(valid && key[e] == tau);
+      if (lane == 0) {
+        gt_words[e * kWaves + wave] = bg;  // word e * kWaves + wave covers blocks 64 * word .. +63
+        eq_words[e * kWaves + wave] = be;
+      }
+    }
+    __syncthreads();
+    const uint64_t eqw = tid < kWords ? eq_words[tid] : 0ull;
+    const uint64_t gtw = tid < kWords ? gt_words[tid] : 0ull;
+    int total = 0;
+    const int eq_before = block_exclusive_scan<NT>(__popcll(eqw), wave_tot, &total);
+    const int take = min(max(remaining - eq_before, 0), __popcll(eqw));  // lowest-index ties first
+    uint64_t keep = gtw, rest = eqw;
+    for (int q = 0; q < take; ++q) {
+      const uint64_t low = rest & (~rest + 1ull);
+      keep |= low;
+      rest ^= low;
+    }
+    int rank = block_exclusive_scan<NT>(__popcll(keep), wave_tot, &total);
+    while (keep != 0ull) {
+      if (rank < kb) kept[rank] = 64 * tid + __builtin_ctzll(keep);  // rank < kb always; guards LDS
+      ++rank;
+      keep &= keep - 1ull;
+    }
+    __syncthreads();
+  }
+
+  for (int64_t s = tid; s < W; s += NT) {
+    int64_t v = -1;
+    if (s < mc) v = sparse ? static_cast<int64_t>(kept[s / c]) * c + s % c : s;
+    else if (s >= budget && s - budget < tail_n) v = tail0 + (s - budget);
+    orow[s] = static_cast<int32_t>(v);
+  }
+}
+
+template <int D>
+hipError_t launch_scores_d(const SelectArgs& a, int hg, int64_t tile0, int64_t n_tiles, int64_t tiles_per_batch,
+                           int64_t n_chunks, int64_t row_base, int64_t ld, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>((n_tiles + 7) / 8 * 8 * n_chunks));
+  const int64_t kb = a.token_budget / a.compress_ratio;
+#define QSA_SCORES(HG)                                                                                          \
+  hipLaunchKernelGGL((select_scores_kernel<D, HG>), grid, dim3(kScoreThreads), 0, stream, a.iq, a.qs[0],       \
+                     a.qs[1], a.qs[2], a.ck, a.cs[0], a.cs[1], a.seq_lens, a.S_q, a.H, a.q_offset,              \
+                     a.compress_ratio, kb, tile0, n_tiles, tiles_per_batch, n_chunks, row_base, ld, a.scores)
+  switch (hg) {
+    case 1: QSA_SCORES(1); break;
+    case 2: QSA_SCORES(2); break;
+    default: QSA_SCORES(4); break;
+  }
+#undef QSA_SCORES
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const SelectArgs& a, int64_t nv_all, int64_t row_base, int64_t rows, int64_t ld,
+                       hipStream_t stream) {
+  const int64_t c = a.compress_ratio, kb = a.token_budget / c, W = a.token_budget + c - 1;
+  const dim3 grid(static_cast<uint32_t>(rows));
+#define QSA_TOPK(NT, E)                                                                                          \
+  hipLaunchKernelGGL((select_topk_kernel<NT, E>), grid, dim3(NT), 0, stream, a.scores, ld, a.seq_lens, a.S_q, \
+                     a.q_offset, c, kb, a.token_budget, W, row_base, a.out)
+  if (nv_all <= 256 * 4) QSA_TOPK(256, 4);
+  else if (nv_all <= 256 * 8) QSA_TOPK(256, 8);
+  else if (nv_all <= 256 * 16) QSA_TOPK(256, 16);
+  else if (nv_all <= 256 * 32) QSA_TOPK(256, 32);
+  else if (nv_all <= 256 * 64) QSA_TOPK(256, 64);
+  else QSA_TOPK(1024, 64);
+#undef QSA_TOPK
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t select_rows_per_tile(int64_t H) { return H <= 16 ? 16 : (H <= 32 ? 8 : 4); }
+
+int64_t select_score_ld(int64_t S_q, int64_t q_offset, int64_t c) {
+  const int64_t nv_all = (q_offset + S_q) / c;
+  return (nv_all < 1 ? 1 : nv_all + 63) / 64 * 64;
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
+  const int64_t c = a.compress_ratio, kb = a.token_budget / c;
+  const int64_t nv_all = (a.q_offset + a.S_q) / c;  // blocks the last query row sees
+  const int64_t rpt = select_rows_per_tile(a.H);
+  const int hg = static_cast<int>(16 / rpt);
+  const int64_t tiles_per_batch = (a.S_q + rpt - 1) / rpt;
+  const int64_t n_tiles = a.B * tiles_per_batch;
+  const int64_t ld = select_score_ld(a.S_q, a.q_offset, c);
+  const bool scoring = kb > 0 && nv_all > kb;
+  const int64_t tiles_per_pass =
+      scoring ? static_cast<int64_t>(a.workspace_bytes / (static_cast<size_t>(rpt * ld) * sizeof(float))) : n_tiles;
+  if (tiles_per_pass < 1) return hipErrorInvalidValue;  // the entry point checks the size first
+  const int64_t n_chunks = (nv_all + kScoreBlocks - 1) / kScoreBlocks;
+  for (int64_t t0 = 0; t0 < n_tiles; t0 += tiles_per_pass) {
+    const int64_t t1 = std::min(n_tiles, t0 + tiles_per_pass);
+    const int64_t row_base = (t0 / tiles_per_batch) * a.S_q + (t0 % tiles_per_batch) * rpt;
+    const int64_t last = t1 - 1;
+    const int64_t row_end = (last / tiles_per_batch) * a.S_q + std::min((last % tiles_per_batch) * rpt + rpt, a.S_q);
+    if (scoring) {
+      hipError_t e;
+      switch (a.D) {
+        case 64: e = launch_scores_d<64>(a, hg, t0, t1 - t0, tiles_per_batch, n_chunks, row_base, ld, stream); break;
+        case 128: e = launch_scores_d<128>(a, hg, t0, t1 - t0, tiles_per_batch, n_chunks, row_base, ld, stream); break;
+        default: e = launch_scores_d<256>(a, hg, t0, t1 - t0, tiles_per_batch, n_chunks, row_base, ld, stream); break;
+      }
+      if (e != hipSuccess) return e;
+    }
+    const hipError_t e = launch_topk(a, nv_all, row_base, row_end - row_base, ld, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace qsa

@@ -29,7 +29,8 @@ def _declared_constants():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "qsa_preprocess", "qsa_forward", "qsa_forward_preprocessed", "qsa_forward_workspace_size",
-        "qsa_backward", "qsa_backward_workspace_size", "qsa_tile_lists", "qsa_status_string"])
+        "qsa_backward", "qsa_backward_workspace_size", "qsa_tile_lists", "qsa_status_string",
+        "qsa_select_token_ids", "qsa_select_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -146,3 +147,49 @@ def test_tile_lists_host_checks():
     assert L.qsa_tile_lists(f[0], 1, 2, 2, f[1], f[1], *f[3:9], None) == -9  # two outputs alias
     assert L.qsa_tile_lists(f[0], 1, 2, 2, f[0], *f[2:9], None) == -9        # output aliases the input
     assert L.qsa_tile_lists(ctypes.c_void_p((1 << 32) + 2), 1, 2, 2, *f[1:9], None) == -8
+
+
+def test_select_workspace_size():
+    ws = qsa.qsa_select_workspace_size
+    # 16-row tiles (H <= 16), rows of round_up(floor((q_offset + S_q) / c), 64) floats
+    assert ws(1, 65536, 16, 0, 4) == 65536 * 16384 * 4
+    assert ws(2, 4096, 16, 0, 4) == 2 * 4096 * 1024 * 4
+    assert ws(1, 8192, 16, 24576, 4) == 8192 * 8192 * 4
+    assert ws(1, 20, 16, 0, 4) == 32 * 64 * 4           # 20 rows -> two 16-row tiles, 5 blocks -> 64
+    assert ws(2, 20, 40, 0, 4) == 2 * 5 * 4 * 64 * 4    # H > 32: 4-row tiles per batch
+    assert ws(0, 10, 16, 0, 4) == 0 and ws(1, 10, 0, 0, 4) == 0 and ws(1, 10, 65, 0, 4) == 0
+    assert ws(1, 10, 16, -1, 4) == 0 and ws(1, 10, 16, 0, 0) == 0
+
+
+def _call_select(B=1, S_q=64, H=4, D=64, S_global=64, q_offset=0, budget=8, c=4, ws_bytes=1 << 20,
+                 null_lens=False, alias_out_q=False, k_last_stride=1, misaligned_ws=False):
+    """Every call made with this helper carries one invalid argument (fake pointers never reach a launch)."""
+    L = qsa.lib()
+    sq = (ctypes.c_int64 * 4)(S_q * H * D, H * D, D, 1)
+    nb = max(S_global // max(c, 1), 1)
+    sk = (ctypes.c_int64 * 4)(nb * D, D, D, k_last_stride)
+    fq, fk, fl, fo, fw = (ctypes.c_void_p(n << 32) for n in range(1, 6))
+    if alias_out_q:
+        fo = fq
+    if misaligned_ws:
+        fw = ctypes.c_void_p((5 << 32) + 64)
+    return L.qsa_select_token_ids(fq, sq, fk, sk, None if null_lens else fl, B, S_q, H, D, S_global, q_offset,
+                                  budget, c, fo, fw, ws_bytes, None)
+
+
+def test_select_host_checks():
+    assert _call_select(S_q=0) == -2
+    assert _call_select(H=0) == -2
+    assert _call_select(budget=0) == -13
+    assert _call_select(c=0) == -13
+    assert _call_select(q_offset=-1) == -13
+    assert _call_select(q_offset=8) == -13          # q_offset + S_q > S_global
+    assert _call_select(D=96) == -5
+    assert _call_select(H=65) == -11
+    assert _call_select(budget=4 * 4097) == -11      # more than 4096 kept blocks
+    assert _call_select(S_global=4 * 65537, S_q=64) == -11
+    assert _call_select(null_lens=True) == -1
+    assert _call_select(k_last_stride=2) == -8
+    assert _call_select(alias_out_q=True) == -9
+    assert _call_select(ws_bytes=16) == -10          # smaller than one 16-row tile of scores
+    assert _call_select(misaligned_ws=True) == -10

@@ -24,7 +24,14 @@ algorithmic bytes of the whole call against the HBM roofline.
 With ``--pass tile_lists`` it times qsa_tile_lists (forward and reverse
 partial/full block lists) on the workload's tile classes.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass forward|backward|tile_lists]
+With ``--pass select`` it times route selection (qsa_select_token_ids: MFMA
+block scores, per-row top-k, expansion) on a selection workload (default
+sel_long), reporting scoring TFLOP/s with F = 2*H*D*sum(nv) over the rows
+that see more than token_budget/c blocks (the only rows whose blocks are
+scored), against the bf16 matrix-core peak.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--pass forward|backward|tile_lists|select]
 """
 
 from __future__ import annotations
@@ -45,7 +52,9 @@ if ROOT not in sys.path:
 
 METRIC = "routed-attention TFLOP/s + achieved HBM GB/s (fwd, BF16, D=256) on 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 DEFAULT_WORKLOAD = "right_padded"
+DEFAULT_SELECT_WORKLOAD = "sel_long"
 
 
 def parse_args():
@@ -54,7 +63,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "tile_lists"], default="forward")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward", "tile_lists", "select"],
+                    default="forward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -233,6 +243,10 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.which == "select":
+        run_select(args)
+        return
 
     import torch
 
@@ -424,6 +438,119 @@ def run_tile_lists(args, w, plan, dev):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "tile_lists_kernel",
                      "ms_per_launch": ms, "alg_bytes_per_launch": alg_bytes},
         "cpu_baseline": None,
+    }), flush=True)
+
+
+def select_counts(w):
+    """Scoring flops and algorithmic bytes of one qsa_select_token_ids call.
+
+    Rows that see nv > kb blocks score every visible block: 2*H*D flops per
+    (row, block).  Bytes: index queries of those rows and the block keys read,
+    fp32 scores written and read back once, every output slot written."""
+    c, kb = w.compress_ratio, w.token_budget // w.compress_ratio
+    n_sum = rows_scored = 0
+    for b in range(w.B):
+        t = w.q_offset + np.arange(w.S_q, dtype=np.int64)
+        nv = (t + 1) // c
+        live = (t < w.lengths[b]) & (nv > kb) & (kb > 0)
+        n_sum += int(nv[live].sum())
+        rows_scored += int(live.sum())
+    flops = 2 * w.H * w.D * n_sum
+    alg_bytes = (2 * w.H * w.D * rows_scored + 2 * w.D * w.B * w.n_blocks + 8 * n_sum
+                 + 4 * w.B * w.S_q * w.width)
+    return flops, alg_bytes, n_sum, rows_scored
+
+
+def select_cpu_baseline(w, iq, ck, lens, target_s: float):
+    """Time the fp64 oracle's selection on query rows from the end of the workload (the longest rows)."""
+    import oracle
+
+    def run(nrows):
+        r0 = w.S_q - nrows
+        t0 = time.perf_counter()
+        oracle.select_token_ids(iq, ck, lens, w.token_budget, w.compress_ratio, w.q_offset, rows=(r0, w.S_q))
+        dt = time.perf_counter() - t0
+        t = w.q_offset + np.arange(r0, w.S_q)
+        nv = (t + 1) // w.compress_ratio
+        kb = w.token_budget // w.compress_ratio
+        n_sum = sum(int(nv[(t < L) & (nv > kb)].sum()) for L in w.lengths)
+        return dt, n_sum, nrows
+
+    dt, n_sum, nrows = run(4)
+    while dt < 0.5 and nrows < w.S_q:
+        dt, n_sum, nrows = run(min(w.S_q, nrows * 4))
+    if dt < target_s and nrows < w.S_q:
+        dt, n_sum, nrows = run(min(w.S_q, max(nrows, int(nrows * target_s / max(dt, 1e-3)))))
+    return {
+        "value": 2 * w.H * w.D * n_sum / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 oracle selection on the last {nrows} query rows of every batch row "
+                  f"({n_sum} scored (row, block) pairs, {dt:.2f} s)",
+    }
+
+
+def run_select(args):
+    import torch
+
+    import route_sparse_gqa_amd as qsa
+    from workloads import SELECT_WORKLOADS, make_select_inputs
+
+    name = DEFAULT_SELECT_WORKLOAD if args.workload == DEFAULT_WORKLOAD else args.workload
+    w = SELECT_WORKLOADS[name]
+    print(f"[bench] generating selection workload {w.name}: {w.description}", file=sys.stderr, flush=True)
+    _, iq, ck, lens = make_select_inputs(w.name)
+    dev = torch.device("cuda", 0)
+    L = qsa.lib()
+    tq = torch.from_numpy(iq.view(np.int16)).to(dev).view(torch.bfloat16)
+    tk = torch.from_numpy(ck.view(np.int16)).to(dev).view(torch.bfloat16)
+    tl = torch.from_numpy(lens).to(dev)
+    out = torch.empty((w.B, w.S_q, w.width), dtype=torch.int32, device=dev)
+    ws_bytes = qsa.qsa_select_workspace_size(w.B, w.S_q, w.H, w.q_offset, w.compress_ratio)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    st = lambda t: (ctypes.c_int64 * t.dim())(*t.stride())
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    call_args = (p(tq), st(tq), p(tk), st(tk), p(tl), w.B, w.S_q, w.H, w.D, w.S_global, w.q_offset, w.token_budget,
+                 w.compress_ratio, p(out), p(ws), ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream.cuda_stream))
+
+    def call():
+        rc = L.qsa_select_token_ids(*call_args)
+        if rc != 0:
+            raise RuntimeError(f"qsa_select_token_ids failed with status {rc}")
+
+    print(f"[bench] select warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(max(args.warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        call()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    flops, alg_bytes, n_sum, rows_scored = select_counts(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle's selection on a bounded sample", file=sys.stderr, flush=True)
+        cpu = select_cpu_baseline(w, iq, ck, lens, args.cpu_seconds)
+    print(json.dumps({
+        "metric": "route-selection block-scoring TFLOP/s (scores + top-k + expansion, BF16 in, FP32 scores) on 1 MI355X",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S_q": w.S_q, "S_global": w.S_global, "H": w.H, "D": w.D,
+                   "compress_ratio": w.compress_ratio, "token_budget": w.token_budget, "q_offset": w.q_offset,
+                   "rows_scored": rows_scored, "scored_pairs": n_sum},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "qsa_select_token_ids (select_scores_kernel + select_topk_kernel)",
+                     "ms_per_launch": ms, "alg_bytes_per_launch": alg_bytes,
+                     "alg_bytes_rate_GBs": alg_bytes / (ms * 1e-3) / 1e9},
+        "cpu_baseline": cpu,
     }), flush=True)
 
 

@@ -13,19 +13,20 @@
 //
 // Design:
 //  * select_scores_kernel -- a workgroup owns 16/HG query rows of one batch
-//    (HG = head groups of 16) and 128 consecutive blocks.  The 128 block
-//    keys are staged once in LDS (row stride 2D + 16 bytes, so the operand
-//    reads are conflict-free) and shared by the four waves.  Per 16 blocks a
-//    wave runs v_mfma_f32_16x16x32_bf16 with the 16 index heads of a row on
-//    M (A operand = the row's queries, held in registers for the whole
-//    workgroup) and the 16 blocks on N; lane (n, g) then holds heads
-//    4g .. 4g+3 of block n, so the relu and three adds give a partial sum and
-//    a two-step exchange across the lane groups (xor 32, then xor 16) both
-//    completes the sums of four rows and leaves row g's sum in lane group g,
-//    which stores it.  Workgroups are mapped so that every block chunk of a
-//    row tile runs on the same XCD (the tile's queries stay in that L2).
-//    fp32 scores go to a [rows, ld] workspace, only for rows that see more
-//    than kb blocks, only for visible blocks.
+//    (HG = head groups of 16) and a segment of up to 4096 blocks, walked in
+//    LDS chunks of 32 KB of block keys (row stride 2D + 16 bytes, so operand
+//    reads are conflict-free).  The next chunk is prefetched into registers
+//    while the current one is used; the rows' queries are loaded once and
+//    stay in registers as the A operand.  Per 16 blocks a wave runs
+//    v_mfma_f32_16x16x32_bf16 with the 16 index heads of a row on M and the
+//    16 blocks on N; lane (n, g) then holds heads 4g .. 4g+3 of block n, so
+//    the relu and three adds give a partial sum, and three gfx950 lane swaps
+//    (two across the wave's halves, one across 16-lane rows; registers only)
+//    complete the sums of four rows and leave row g's sum in lane group g,
+//    which stores it.  The
+//    segments of one row tile run on one XCD; the tiles that see the most
+//    blocks are dispatched first.  fp32 scores go to a [rows, ld] workspace,
+//    only for rows that see more than kb blocks, only for visible blocks.
 //  * select_topk_kernel -- one workgroup per query row.  Scores sit in
 //    registers (E per thread, coalesced loads); three LDS-histogram passes
 //    over the float bit patterns (non-negative floats order like their bits;
@@ -46,15 +47,20 @@ namespace qsa {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kScoreBlocks = 128;  // blocks per score workgroup: 8 MFMA tiles of 16
-constexpr int kBins = 2048;        // histogram bins of one radix pass (11 bits)
+constexpr int kSegmentBlocks = 4096;  // blocks per score workgroup at most
+constexpr int kBins = 2048;           // histogram bins of one radix pass (11 bits)
 
 template <int D>
 struct SelGeo {
-  static constexpr int kSteps = D / 32;   // K-slices of one 16x16x32 product
-  static constexpr int kStride = D + 8;   // LDS row stride (bf16): 2D + 16 bytes
-  static constexpr int kPieces = D / 8;   // 16-byte pieces of one key row
+  static constexpr int kSteps = D / 32;             // K-slices of one 16x16x32 product
+  static constexpr int kStride = D + 8;             // LDS row stride (bf16): 2D + 16 bytes
+  static constexpr int kPieces = D / 8;             // 16-byte pieces of one key row
+  static constexpr int kChunk = 16384 / D;          // blocks per LDS chunk (32 KB of keys)
+  static constexpr int kPerThread = kChunk * kPieces / kScoreThreads;  // 16-byte pieces per thread: 8
 };
+
+// relu on the bit pattern: negative values and -0.0 (sign bit set, negative as int32) become +0.0.
+__device__ __forceinline__ float relu(float v) { return __int_as_float(max(__float_as_int(v), 0)); }
 
 __device__ __forceinline__ int64_t clamp_len(int64_t L, int64_t q_end) { return L < 0 ? 0 : (L > q_end ? q_end : L); }
 
@@ -64,31 +70,32 @@ __global__ void __launch_bounds__(kScoreThreads)
                          const uint16_t* __restrict__ ck, int64_t cs0, int64_t cs1,
                          const int64_t* __restrict__ seq_lens, int64_t S_q, int64_t H, int64_t q_offset,
                          int64_t c, int64_t kb, int64_t tile0, int64_t n_tiles, int64_t tiles_per_batch,
-                         int64_t n_chunks, int64_t row_base, int64_t ld, float* __restrict__ scores) {
+                         int64_t n_segments, int64_t row_base, int64_t ld, float* __restrict__ scores) {
   using Geo = SelGeo<D>;
   constexpr int RW = 4 / HG;   // query rows per wave
   constexpr int RPW = 4 * RW;  // query rows per workgroup
-  __shared__ __attribute__((aligned(16))) uint16_t kslab[kScoreBlocks * Geo::kStride];
+  __shared__ __attribute__((aligned(16))) uint16_t kslab[Geo::kChunk * Geo::kStride];
 
-  // Workgroup w -> (tile, chunk): tiles go in groups of 8, tile 8q + x to
-  // workgroups congruent to x mod 8, i.e. always to the same XCD.
+  // Workgroup w -> (tile, segment): tiles in groups of 8, the segments of
+  // tile 8q + x on workgroups congruent to x mod 8 (one XCD); tiles are taken
+  // from the last (which see the most blocks) to the first.
   const int64_t w = blockIdx.x;
-  const int64_t group = w / (8 * n_chunks), rem = w % (8 * n_chunks);
-  const int64_t local_tile = group * 8 + rem % 8;
-  const int64_t chunk = rem / 8;
-  if (local_tile >= n_tiles) return;  // every exit precedes the only barrier
-  const int64_t tile = tile0 + local_tile;
+  const int64_t x = w % 8, rest = w / 8;
+  const int64_t seg = rest % n_segments;
+  const int64_t rank = (rest / n_segments) * 8 + x;
+  if (rank >= n_tiles) return;  // every exit precedes the first barrier
+  const int64_t tile = tile0 + (n_tiles - 1 - rank);
   const int64_t b = tile / tiles_per_batch;
   const int64_t i0 = (tile % tiles_per_batch) * RPW;
-  const int64_t q_end = q_offset + S_q;
-  const int64_t L = clamp_len(seq_lens[b], q_end);
+  const int64_t L = clamp_len(seq_lens[b], q_offset + S_q);
   // Non-padding rows are a prefix of the tile; the last one sees the most blocks.
   const int64_t i_last = min(min(i0 + RPW - 1, S_q - 1), L - 1 - q_offset);
   if (i_last < i0) return;
   const int64_t nv_max = (q_offset + i_last + 1) / c;
-  const int64_t j0 = chunk * kScoreBlocks;
-  if (nv_max <= kb || j0 >= nv_max) return;
-  const int nblk = static_cast<int>(min(static_cast<int64_t>(kScoreBlocks), nv_max - j0));
+  const int64_t seg0 = seg * kSegmentBlocks;
+  if (nv_max <= kb || seg0 >= nv_max) return;
+  const int64_t seg_end = min(nv_max, seg0 + kSegmentBlocks);
+  const int n_chunks = static_cast<int>((seg_end - seg0 + Geo::kChunk - 1) / Geo::kChunk);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -96,14 +103,25 @@ __global__ void __launch_bounds__(kScoreThreads)
   const int m = lane & 15;  // head row of the A operand; block column of B and of the result
   const int g = lane >> 4;  // k-group of the operands; head quad of the result
 
-  // Block keys j0 .. j0 + nblk - 1 into LDS (zeros past them).
+  // Key pieces of one chunk: thread tid holds pieces tid + 256 u (zeros past seg_end).
   const uint16_t* kbase = ck + b * cs0;
-  for (int p = tid; p < kScoreBlocks * Geo::kPieces; p += kScoreThreads) {
-    const int blk = p / Geo::kPieces, piece = p % Geo::kPieces;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (blk < nblk) v = load16(kbase + (j0 + blk) * cs1 + 8 * piece);
-    *reinterpret_cast<u32x4*>(kslab + blk * Geo::kStride + 8 * piece) = v;
-  }
+  u32x4 pre[Geo::kPerThread];
+  auto fetch = [&](int64_t j0) {
+#pragma unroll
+    for (int u = 0; u < Geo::kPerThread; ++u) {
+      const int p = tid + kScoreThreads * u;
+      const int64_t blk = j0 + p / Geo::kPieces;
+      pre[u] = blk < seg_end ? load16(kbase + blk * cs1 + 8 * (p % Geo::kPieces)) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < Geo::kPerThread; ++u) {
+      const int p = tid + kScoreThreads * u;
+      *reinterpret_cast<u32x4*>(kslab + (p / Geo::kPieces) * Geo::kStride + 8 * (p % Geo::kPieces)) = pre[u];
+    }
+  };
+  fetch(seg0);
 
   // Queries as the A operand: lane (m, g) holds head 16 hg + m, dims 32s + 8g .. +7.
   bf16x8 qf[RW][HG][Geo::kSteps];
@@ -128,40 +146,50 @@ __global__ void __launch_bounds__(kScoreThreads)
   const bool my_store = my_row && my_nv > kb;
   float* my_out = scores + (my_store ? (b * S_q + my_i - row_base) * ld : 0);
 
+  stage();
   __syncthreads();
 
-  const int n_sub = (nblk + 15) / 16;
-  for (int sc = 0; sc < n_sub; ++sc) {
-    bf16x8 kf[Geo::kSteps];
-    const uint16_t* kp = kslab + (16 * sc + m) * Geo::kStride + 8 * g;
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const int64_t j0 = seg0 + static_cast<int64_t>(ch) * Geo::kChunk;
+    const bool more = ch + 1 < n_chunks;
+    if (more) fetch(j0 + Geo::kChunk);  // in flight while this chunk is scored
+    const int n_sub = static_cast<int>((min(static_cast<int64_t>(Geo::kChunk), seg_end - j0) + 15) / 16);
+    for (int sc = 0; sc < n_sub; ++sc) {
+      bf16x8 kf[Geo::kSteps];
+      const uint16_t* kp = kslab + (16 * sc + m) * Geo::kStride + 8 * g;
 #pragma unroll
-    for (int s = 0; s < Geo::kSteps; ++s) kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 32 * s));
+      for (int s = 0; s < Geo::kSteps; ++s)
+        kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 32 * s));
 
-    float part[4] = {0.f, 0.f, 0.f, 0.f};  // rows past RW stay 0
+      float part[4] = {0.f, 0.f, 0.f, 0.f};  // rows past RW stay 0
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      float sum = 0.f;
+      for (int r = 0; r < RW; ++r) {
 #pragma unroll
-      for (int hg = 0; hg < HG; ++hg) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int hg = 0; hg < HG; ++hg) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < Geo::kSteps; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[r][hg][s], kf[s], acc, 0, 0, 0);
-        sum += fmaxf(acc[0], 0.f) + fmaxf(acc[1], 0.f) + fmaxf(acc[2], 0.f) + fmaxf(acc[3], 0.f);
+          for (int s = 0; s < Geo::kSteps; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[r][hg][s], kf[s], acc, 0, 0, 0);
+          const float sum = relu(acc[0]) + relu(acc[1]) + relu(acc[2]) + relu(acc[3]);
+          part[r] = hg == 0 ? sum : part[r] + sum;
+        }
       }
-      part[r] = sum;
+      // Lane groups 0+2 and 1+3 combine rows 0 and 2 (x) and rows 1 and 3 (y); then groups 0+1
+      // and 2+3 finish them, leaving row g's sum in lane group g.
+      const u32x2 x = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+      const u32x2 y = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+      const float xs = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+      const float ys = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      const u32x2 z = __builtin_amdgcn_permlane16_swap(__float_as_uint(xs), __float_as_uint(ys), false, false);
+      const float total = __uint_as_float(z[0]) + __uint_as_float(z[1]);  // >= +0.0: sums of relu terms
+      const int64_t j = j0 + 16 * sc + m;
+      if (my_store && j < my_nv) my_out[j] = total;
     }
-    // Lane groups g and g^2 swap halves: groups 0, 1 keep rows 0, 1; groups 2, 3 keep rows 2, 3.
-    const bool upper = g >= 2;
-    float keep0 = upper ? part[2] : part[0];
-    float keep1 = upper ? part[3] : part[1];
-    keep0 += __shfl_xor(upper ? part[0] : part[2], 32);
-    keep1 += __shfl_xor(upper ? part[1] : part[3], 32);
-    // Groups g and g^1: even groups finish their first kept row, odd ones the second.
-    const bool odd = (g & 1) != 0;
-    float total = (odd ? keep1 : keep0) + __shfl_xor(odd ? keep0 : keep1, 16);
-    total = total > 0.f ? total : 0.f;  // one zero: -0.0 would order below +0.0 by bits
-    const int64_t j = j0 + 16 * sc + m;
-    if (my_store && j < my_nv) my_out[j] = total;
+    if (more) {
+      __syncthreads();  // every wave is done with this chunk's keys
+      stage();
+      __syncthreads();
+    }
   }
 }
 
@@ -302,23 +330,26 @@ __global__ void __launch_bounds__(NT)
     __syncthreads();
   }
 
-  for (int64_t s = tid; s < W; s += NT) {
-    int64_t v = -1;
-    if (s < mc) v = sparse ? static_cast<int64_t>(kept[s / c]) * c + s % c : s;
-    else if (s >= budget && s - budget < tail_n) v = tail0 + (s - budget);
-    orow[s] = static_cast<int32_t>(v);
+  // Kept blocks as c token IDs each, then -1 up to the budget, then the tail (no division).
+  const int ci = static_cast<int>(c), mi = static_cast<int>(mc / c), Wi = static_cast<int>(W);
+  const int budget_i = static_cast<int>(budget), tail0_i = static_cast<int>(tail0), tail_ni = static_cast<int>(tail_n);
+  for (int r = tid; r < mi; r += NT) {
+    const int blk = sparse ? kept[r] : r;
+    for (int u = 0; u < ci; ++u) orow[r * ci + u] = blk * ci + u;
   }
+  for (int s = mi * ci + tid; s < budget_i; s += NT) orow[s] = -1;
+  for (int s = budget_i + tid; s < Wi; s += NT) orow[s] = s - budget_i < tail_ni ? tail0_i + (s - budget_i) : -1;
 }
 
 template <int D>
 hipError_t launch_scores_d(const SelectArgs& a, int hg, int64_t tile0, int64_t n_tiles, int64_t tiles_per_batch,
-                           int64_t n_chunks, int64_t row_base, int64_t ld, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>((n_tiles + 7) / 8 * 8 * n_chunks));
+                           int64_t n_segments, int64_t row_base, int64_t ld, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>((n_tiles + 7) / 8 * 8 * n_segments));
   const int64_t kb = a.token_budget / a.compress_ratio;
 #define QSA_SCORES(HG)                                                                                          \
   hipLaunchKernelGGL((select_scores_kernel<D, HG>), grid, dim3(kScoreThreads), 0, stream, a.iq, a.qs[0],       \
                      a.qs[1], a.qs[2], a.ck, a.cs[0], a.cs[1], a.seq_lens, a.S_q, a.H, a.q_offset,              \
-                     a.compress_ratio, kb, tile0, n_tiles, tiles_per_batch, n_chunks, row_base, ld, a.scores)
+                     a.compress_ratio, kb, tile0, n_tiles, tiles_per_batch, n_segments, row_base, ld, a.scores)
   switch (hg) {
     case 1: QSA_SCORES(1); break;
     case 2: QSA_SCORES(2); break;
@@ -366,7 +397,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   const int64_t tiles_per_pass =
       scoring ? static_cast<int64_t>(a.workspace_bytes / (static_cast<size_t>(rpt * ld) * sizeof(float))) : n_tiles;
   if (tiles_per_pass < 1) return hipErrorInvalidValue;  // the entry point checks the size first
-  const int64_t n_chunks = (nv_all + kScoreBlocks - 1) / kScoreBlocks;
+  const int64_t n_segments = (nv_all + kSegmentBlocks - 1) / kSegmentBlocks;
   for (int64_t t0 = 0; t0 < n_tiles; t0 += tiles_per_pass) {
     const int64_t t1 = std::min(n_tiles, t0 + tiles_per_pass);
     const int64_t row_base = (t0 / tiles_per_batch) * a.S_q + (t0 % tiles_per_batch) * rpt;
@@ -375,9 +406,9 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
     if (scoring) {
       hipError_t e;
       switch (a.D) {
-        case 64: e = launch_scores_d<64>(a, hg, t0, t1 - t0, tiles_per_batch, n_chunks, row_base, ld, stream); break;
-        case 128: e = launch_scores_d<128>(a, hg, t0, t1 - t0, tiles_per_batch, n_chunks, row_base, ld, stream); break;
-        default: e = launch_scores_d<256>(a, hg, t0, t1 - t0, tiles_per_batch, n_chunks, row_base, ld, stream); break;
+        case 64: e = launch_scores_d<64>(a, hg, t0, t1 - t0, tiles_per_batch, n_segments, row_base, ld, stream); break;
+        case 128: e = launch_scores_d<128>(a, hg, t0, t1 - t0, tiles_per_batch, n_segments, row_base, ld, stream); break;
+        default: e = launch_scores_d<256>(a, hg, t0, t1 - t0, tiles_per_batch, n_segments, row_base, ld, stream); break;
       }
       if (e != hipSuccess) return e;
     }

@@ -37,6 +37,27 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ORs `bits` into words[w] for every lane of the wavefront whose w is not
+// 0xFFFFFFFF.  Consecutive lanes holding the same word (the runs that
+// consecutive token IDs produce) are first merged by a segmented OR over
+// shuffles, so each run costs one LDS atomic instead of one per lane (lanes
+// of one atomic instruction that hit the same address are serialised).
+// Every lane of the wavefront must call it.
+__device__ __forceinline__ void wave_or_runs(uint32_t* words, uint32_t w, uint32_t bits) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t prev = static_cast<uint32_t>(__shfl_up(static_cast<int>(w), 1));
+  const bool head = lane == 0 || prev != w;
+  const uint64_t heads = __ballot(head);
+  const uint64_t after = heads & ~((2ull << lane) - 1ull);  // heads above this lane (lane 63: none)
+  const int next = after != 0ull ? __builtin_ctzll(after) : 64;  // first lane of the next run
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t other = static_cast<uint32_t>(__shfl_down(static_cast<int>(bits), o));
+    if (lane + o < next) bits |= other;  // lanes l .. min(l + 2o, next) - 1 are now merged
+  }
+  if (head && w != 0xFFFFFFFFu && bits != 0u) atomicOr(&words[w], bits);
+}
+
 // Byte offset of a gathered row: 32-bit when every row of the tensor lies
 // within 4 GiB of its (batch, head) base, else 64-bit.
 template <bool kNarrow>

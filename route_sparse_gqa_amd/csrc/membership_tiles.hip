@@ -9,7 +9,9 @@
 // Design: one workgroup owns 16 rows of one 128-row tile row of one batch and
 // one segment of up to 65536 columns; each of its four wavefronts owns one
 // row at a time with a private LDS bitmap of the segment.  Per row the wave
-// scatters the row's list into the bitmap (atomic OR, integer only), expands
+// scatters the row's list into the bitmap (atomic OR, integer only; the
+// sorted list's runs of IDs in one word are merged in registers first, one
+// atomic per run), expands
 // it to bytes with 16-byte stores (every byte of the row, padding included,
 // is written exactly once) and adds each 128-column tile's popcount to a
 // register counter of the lane that owns the tile.  The workgroup sums its
@@ -19,6 +21,7 @@
 // the classes deterministic.
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -33,14 +36,10 @@ constexpr int kGroupRows = 16;                   // rows per workgroup
 constexpr int kGroups = kTile / kGroupRows;      // workgroups per tile row and segment
 constexpr int kTilesPerLane = kSegTiles / 64;  // 8
 
+constexpr int kBatch = 16;  // list entries per lane loaded together
+
 // Four bits -> four bytes holding 0 or 1 (bit k lands in byte k).
 __device__ __forceinline__ uint32_t spread4(uint32_t nibble) { return (nibble * 0x00204081u) & 0x01010101u; }
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 __global__ void __launch_bounds__(kThreads)
     membership_tiles_kernel(const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count,
@@ -74,13 +73,25 @@ __global__ void __launch_bounds__(kThreads)
   int members[kTilesPerLane] = {};
   for (int64_t i = r0 + wave; i < r1; i += kWaves) {
     const int64_t row = b * S_q + i;
+    const int n = static_cast<int>(min(max(static_cast<int64_t>(route_count[row]), int64_t{0}), K));
     for (int w = lane; w < seg_words; w += 64) bits[w] = 0u;
     wave_lds_sync();
-    const int n = static_cast<int>(min(max(static_cast<int64_t>(route_count[row]), int64_t{0}), K));
     const int32_t* lst = route_list + row * K;
-    for (int j = lane; j < n; j += 64) {
-      const int64_t col = static_cast<int64_t>(lst[j]) - c0;
-      if (col >= 0 && col < seg_cols) atomicOr(&bits[col >> 5], 1u << (col & 31));
+    // Batches of kBatch IDs per lane: a batch's loads are all in flight before any is used.
+    for (int j0 = 0; j0 < n; j0 += 64 * kBatch) {  // wave-uniform
+      int32_t id[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = j0 + 64 * u + lane;
+        id[u] = j < n ? lst[j] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j0 + 64 * u >= n) continue;  // wave-uniform
+        const int64_t col = static_cast<int64_t>(id[u]) - c0;
+        const bool ok = id[u] >= 0 && col >= 0 && col < seg_cols;
+        wave_or_runs(bits, ok ? static_cast<uint32_t>(col >> 5) : 0xFFFFFFFFu, ok ? 1u << (col & 31) : 0u);
+      }
     }
     wave_lds_sync();
     if (membership != nullptr) {

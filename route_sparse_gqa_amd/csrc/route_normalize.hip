@@ -17,8 +17,20 @@
 // sort; per-thread keep counts are prefix-summed with one ballot per count
 // bit, then the kept keys are compacted through LDS and written out
 // coalesced.
+//
+// When the key range is small (kv_length <= 32 * kBitmapWords = 131072) and
+// K <= kBitmapWords, a row is instead marked in an LDS bitmap of
+// kv_length bits (integer atomic OR, so duplicates collapse by
+// construction; runs of consecutive IDs in neighbouring slots are merged
+// within the wavefront first).  One workgroup prefix sum over contiguous
+// runs of words then gives every non-zero word its index in a compact list
+// and the number of IDs before it; half-wavefronts expand one listed word
+// each (lane j writes bit j's ID at its rank), so the IDs come out ascending
+// with no sort and no per-bit loop: O(K + kv_length / 32) work per row
+// instead of O(K log^2 K).
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -168,6 +180,97 @@ __global__ void __launch_bounds__(64 * W * RowsPerBlock<W>::value)
   }
 }
 
+constexpr int kBitmapThreads = 256;
+constexpr int kBitmapWords = 4096;  // largest bitmap: kv_length <= 131072, K <= 4096
+
+// kWords bitmap words (kv_length <= 32 kWords) and kWords route slots (K <= kWords) per row.
+template <int kWords, typename RouteT>
+__global__ void __launch_bounds__(kBitmapThreads)
+    route_bitmap_kernel(const RouteT* __restrict__ routes, int64_t rs0, int64_t rs1, int64_t rs2, int64_t S_q,
+                        int64_t K, int64_t kv_length, int32_t* __restrict__ route_list,
+                        int32_t* __restrict__ route_count, int32_t* __restrict__ zero_buf, int64_t zero_count) {
+  constexpr int T = kBitmapThreads;
+  constexpr int kBitmapRun = kWords / T;  // bitmap words (and route slots) per thread
+  __shared__ uint32_t region[kWords];   // the row's bitmap
+  __shared__ uint32_t nonzero[kWords];  // its non-zero words: index << 16 | IDs before the word
+  __shared__ int wave_tot[T / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int nw = static_cast<int>((kv_length + 31) / 32);
+  const int run = (nw + T - 1) / T;  // words per thread (<= kBitmapRun)
+  const int Ki = static_cast<int>(K);
+
+  // Every slot of the row is loaded before any is used (one memory latency per row).
+  const RouteT* src = routes + (row / S_q) * rs0 + (row % S_q) * rs1;
+  int64_t x[kBitmapRun];  // K <= kBitmapRun * T slots
+#pragma unroll
+  for (int q = 0; q < kBitmapRun; ++q) {
+    const int s = q * T + tid;
+    x[q] = s < Ki ? static_cast<int64_t>(src[s * rs2]) : int64_t{-1};  // int32 IDs sign-extend
+  }
+  for (int w = tid; w < nw; w += T) region[w] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kBitmapRun; ++q) {
+    if (q * T >= Ki) continue;  // workgroup-uniform: every lane meets the shuffles
+    const bool ok = x[q] >= 0 && x[q] < kv_length;
+    wave_or_runs(region, ok ? static_cast<uint32_t>(x[q] >> 5) : 0xFFFFFFFFu, ok ? 1u << (x[q] & 31) : 0u);
+  }
+  __syncthreads();
+
+  // Thread tid owns words tid*run .. tid*run + run - 1.  One prefix sum over threads of
+  // (non-zero words << 16 | set bits) places every non-zero word and every ID (both <= 4096).
+  uint32_t mine[kBitmapRun];
+  int packed = 0;
+#pragma unroll
+  for (int q = 0; q < kBitmapRun; ++q) {
+    const int w = tid * run + q;
+    mine[q] = (q < run && w < nw) ? region[w] : 0u;
+    packed += (mine[q] != 0u ? 1 << 16 : 0) + __popc(mine[q]);
+  }
+  int incl = packed;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = incl - packed, all = 0;
+#pragma unroll
+  for (int q = 0; q < T / 64; ++q) {
+    before += q < wave ? wave_tot[q] : 0;
+    all += wave_tot[q];
+  }
+  int slot = before >> 16, ids = before & 0xFFFF;
+#pragma unroll
+  for (int q = 0; q < kBitmapRun; ++q) {
+    if (mine[q] != 0u) {
+      nonzero[slot++] = static_cast<uint32_t>((tid * run + q) << 16 | ids);
+      ids += __popc(mine[q]);
+    }
+  }
+  __syncthreads();
+  const int n_nonzero = all >> 16, total = all & 0xFFFF;
+
+  // Each half-wavefront expands one non-zero word: lane j writes bit j's ID at its rank.
+  int32_t* dst = route_list + row * K;
+  const int half = lane >> 5, j = lane & 31;
+  for (int e = 2 * wave + half; e < n_nonzero; e += 2 * (T / 64)) {
+    const uint32_t entry = nonzero[e];
+    const int w = static_cast<int>(entry >> 16);
+    const uint32_t word = region[w];
+    if ((word >> j) & 1u) dst[(entry & 0xFFFFu) + __popc(word & ((1u << j) - 1u))] = 32 * w + j;
+  }
+  for (int s = total + tid; s < Ki; s += T) dst[s] = -1;
+  if (tid == 0) route_count[row] = total;
+  if (zero_buf != nullptr) {  // side job: clear the tile member counters (grid-stride)
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t z = static_cast<int64_t>(blockIdx.x) * blockDim.x + tid; z < zero_count; z += stride)
+      zero_buf[z] = 0;
+  }
+}
+
 template <int E, int W, typename RouteT>
 hipError_t launch_sorted(const RouteT* routes, const int64_t* st, int64_t B, int64_t S_q, int64_t K,
                          int64_t kv_length, int32_t* list, int32_t* count, int32_t* zb, int64_t zn,
@@ -185,6 +288,17 @@ template <typename RouteT>
 hipError_t dispatch(const RouteT* routes, const int64_t* st, int64_t B, int64_t S_q, int64_t K,
                     int64_t kv_length, int32_t* list, int32_t* count, int32_t* zb, int64_t zn,
                     hipStream_t stream) {
+  const dim3 rows(static_cast<uint32_t>(B * S_q)), threads(kBitmapThreads);
+  if (kv_length <= 32 * 512 && K <= 512) {  // small rows: 4 KB of LDS, many workgroups per CU
+    hipLaunchKernelGGL((route_bitmap_kernel<512, RouteT>), rows, threads, 0, stream, routes, st[0], st[1], st[2], S_q,
+                       K, kv_length, list, count, zb, zn);
+    return hipGetLastError();
+  }
+  if (kv_length <= 32 * int64_t{kBitmapWords} && K <= kBitmapWords) {
+    hipLaunchKernelGGL((route_bitmap_kernel<kBitmapWords, RouteT>), rows, threads, 0, stream, routes, st[0], st[1],
+                       st[2], S_q, K, kv_length, list, count, zb, zn);
+    return hipGetLastError();
+  }
   if (K <= 64) return launch_sorted<1, 1>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
   if (K <= 128) return launch_sorted<2, 1>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);
   if (K <= 256) return launch_sorted<4, 1>(routes, st, B, S_q, K, kv_length, list, count, zb, zn, stream);

@@ -80,6 +80,24 @@ def test_large_route_counts_and_segments():
         check_forward(gpu_bf16_bits(out), oracle.forward(q, k, v, r, 0.125), ocnt, v, "large K")
 
 
+@pytest.mark.parametrize("S_kv,K,dtype", [(131072, 4096, np.int64), (131072, 4097, np.int64), (131073, 64, np.int32),
+                                          (1 << 31, 300, np.int64), (64, 4096, np.int32), (16384, 512, np.int64),
+                                          (16385, 512, np.int32), (16384, 513, np.int64)])
+def test_route_lists_at_the_bitmap_limits(S_kv, K, dtype):
+    """Every normalisation path at its boundaries (bitmaps: kv <= 16384 and K <= 512, kv <= 131072 and
+    K <= 4096; else sorting)."""
+    print(f"route lists kv={S_kv} K={K} {np.dtype(dtype).name}", flush=True)
+    rng = np.random.Generator(np.random.PCG64(S_kv + K))
+    B, S_q = 2, 5
+    r = rng.integers(-3, min(S_kv + 3, np.iinfo(dtype).max), size=(B, S_q, K), dtype=np.int64)
+    r[:, :, K // 2:] = r[:, :, :K - K // 2]  # every value of the first half appears again
+    r = r.astype(dtype)
+    lst, cnt, _, _ = qsa.qsa_preprocess(torch.from_numpy(r).to(device()), S_kv)
+    olst, ocnt = oracle.route_lists(r, S_kv)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), ocnt)
+    np.testing.assert_array_equal(lst.cpu().numpy(), olst)
+
+
 def test_full_tiles_and_edge_tiles():
     # every pair of tile (0,0) a member, a full ragged edge tile, a partial and an absent tile
     S_q, kv = 200, 130

@@ -6,9 +6,9 @@
 // 1 partial, 2 full); flex_qsa page, `_membership_flat_offset` (table
 // offsets must be 64-bit once B*S_q*kv_length passes 2^31).
 //
-// Design: one workgroup owns 16 rows of one 128-row tile row of one batch and
+// Design: one workgroup owns 4 rows of one 128-row tile row of one batch and
 // one segment of up to 65536 columns; each of its four wavefronts owns one
-// row at a time with a private LDS bitmap of the segment.  Per row the wave
+// row with a private LDS bitmap of the segment (LDS sized to the segment).  Per row the wave
 // scatters the row's list into the bitmap (atomic OR, integer only; the
 // sorted list's runs of IDs in one word are merged in registers first, one
 // atomic per run), expands
@@ -32,7 +32,7 @@ constexpr int kSegCols = 65536;              // columns per workgroup segment
 constexpr int kSegTiles = kSegCols / kTile;  // 512 tiles per segment
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kGroupRows = 16;                   // rows per workgroup
+constexpr int kGroupRows = kWaves;               // rows per workgroup: one per wavefront
 constexpr int kGroups = kTile / kGroupRows;      // workgroups per tile row and segment
 constexpr int kTilesPerLane = kSegTiles / 64;  // 8
 
@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(kThreads)
     membership_tiles_kernel(const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count,
                             int64_t S_q, int64_t K, int64_t ldm, int64_t n_ti, int64_t n_tj, int64_t n_seg,
                             uint8_t* __restrict__ membership, int32_t* __restrict__ tile_count) {
-  __shared__ uint32_t lds[kWaves * (kSegCols / 32) + kSegTiles];  // per-wave bitmaps, then tile counters
+  extern __shared__ uint32_t lds[];  // per-wave bitmaps of the segment, then its tile counters (sized at launch)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   int64_t blk = blockIdx.x;
@@ -161,7 +161,9 @@ hipError_t launch_membership_tiles(const int32_t* route_list, const int32_t* rou
   const int64_t blocks = B * n_ti * n_seg * kGroups;
   // tile_class holds member counts until the final pass; the route-normalise
   // launch that precedes this one on the stream has zeroed it.
-  hipLaunchKernelGGL(membership_tiles_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, stream,
+  const int64_t seg_cols = ldm < kSegCols ? ldm : kSegCols;
+  const size_t lds_bytes = sizeof(uint32_t) * static_cast<size_t>(kWaves * (seg_cols / 32) + seg_cols / kTile);
+  hipLaunchKernelGGL(membership_tiles_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), lds_bytes, stream,
                      route_list, route_count, S_q, K, ldm, n_ti, n_tj, n_seg, membership, tile_class);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || tile_class == nullptr) return e;

@@ -44,6 +44,7 @@ namespace {
 
 constexpr int kWaves = 4;   // work units per workgroup
 constexpr int kChunk = 16;  // keys per dq iteration; keys per dkdv tile; MFMA rows per dkdv batch
+constexpr int kRecChunk = 1024;  // segment records staged in LDS at a time by dkdv
 
 template <int D>
 struct Geo {
@@ -237,6 +238,7 @@ __global__ void __launch_bounds__(64 * kWaves)
   __shared__ __attribute__((aligned(16))) uint16_t slab[2][2][kChunk * Gm::kTrStride];
   __shared__ float2 stat[2][kChunk];
   __shared__ uint2 cmask[2][kChunk];
+  __shared__ int4 recs[kRecChunk];  // segment records of the part (a chunk at a time)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -280,17 +282,21 @@ __global__ void __launch_bounds__(64 * kWaves)
   const int cols = rows_per_batch * G;  // MFMA rows in use: (row slot, head) = (col / G, col % G)
   const int32_t s_begin = seg_start[unit] + part * part_len;
   const int32_t s_end = min(seg_start[unit + 1], s_begin + part_len);
-  const int32_t n_batches = (s_end - s_begin + rows_per_batch - 1) / rows_per_batch;
   const int64_t q_head0 = hk * G;
   const int32_t row_max = static_cast<int32_t>(S_q - 1);
 
-  // Batch staging, in two halves so the loads of batch i + 1 overlap the
-  // MFMAs of batch i: fetch() issues the global loads into registers,
-  // stash() writes them to one LDS buffer.
-  u32x4 pre[kPer];
-  float2 pre_stat = {0.f, 0.f};
-  uint2 pre_mask = {0u, 0u};
-  auto fetch = [&](int32_t sb) {
+  // The part's segment records are staged in LDS (kRecChunk at a time), so a
+  // batch's loads take their addresses from LDS and never wait on another
+  // global load.  Batches then flow through two register stages (loads of
+  // batches i + 1 and i + 2 in flight while batch i is computed) into a
+  // double-buffered LDS slab.
+  struct Stage {
+    u32x4 pre[kPer];
+    float2 stat;
+    uint2 mask;
+  };
+  int32_t n_rec = 0;  // records staged for the current chunk
+  auto fetch = [&](Stage& S, int32_t sb) {  // sb: first record of the batch, within the chunk
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int pc = tid + kThreads * u;
@@ -298,52 +304,41 @@ __global__ void __launch_bounds__(64 * kWaves)
       const int col = (pc / Gm::kLanesPerRow) % kChunk;
       const int piece = 8 * (pc % Gm::kLanesPerRow);
       const int slot = col / G;
-      const bool ok = col < cols && sb + slot < s_end;
-      const int32_t ir = ok ? min(max(segs[sb + slot].x, 0), row_max) : 0;
+      const bool ok = col < cols && sb + slot < n_rec;
+      const int32_t ir = ok ? min(max(recs[sb + slot].x, 0), row_max) : 0;
       const int64_t h = q_head0 + (ok ? col % G : 0);
       const uint16_t* src = m == 0 ? q + b * qs0 + ir * qs1 + h * qs2 : dout + b * gs0 + ir * gs1 + h * gs2;
-      pre[u] = ok ? load16(src + piece) : u32x4{0u, 0u, 0u, 0u};
+      S.pre[u] = ok ? load16(src + piece) : u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < kChunk) {
       const int col = tid;
       const int slot = col / G;
-      const bool ok = col < cols && sb + slot < s_end;
-      if (ok) {
-        const int4 e = segs[sb + slot];
+      if (col < cols && sb + slot < n_rec) {
+        const int4 e = recs[sb + slot];
         const int64_t idx = (b * S_q + min(max(e.x, 0), row_max)) * Hq + q_head0 + col % G;
-        pre_stat = float2{lse[idx] * kLog2e, delta[idx]};
-        pre_mask = uint2{static_cast<uint32_t>(e.y), static_cast<uint32_t>(e.z)};
+        S.stat = float2{lse[idx] * kLog2e, delta[idx]};
+        S.mask = uint2{static_cast<uint32_t>(e.y), static_cast<uint32_t>(e.z)};
       } else {
-        pre_stat = float2{0.f, 0.f};
-        pre_mask = uint2{0u, 0u};
+        S.stat = float2{0.f, 0.f};
+        S.mask = uint2{0u, 0u};
       }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](const Stage& S, int buf) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int pc = tid + kThreads * u;
       const int m = pc / (kChunk * Gm::kLanesPerRow);
       const int col = (pc / Gm::kLanesPerRow) % kChunk;
       const int piece = 8 * (pc % Gm::kLanesPerRow);
-      *reinterpret_cast<u32x4*>(&slab[buf][m][col * Gm::kTrStride + piece]) = pre[u];
+      *reinterpret_cast<u32x4*>(&slab[buf][m][col * Gm::kTrStride + piece]) = S.pre[u];
     }
     if (tid < kChunk) {
-      stat[buf][tid] = pre_stat;
-      cmask[buf][tid] = pre_mask;
+      stat[buf][tid] = S.stat;
+      cmask[buf][tid] = S.mask;
     }
   };
-
-  if (n_batches > 0) {
-    fetch(s_begin);
-    stash(0);
-  }
-  __syncthreads();
-  for (int32_t bi = 0; bi < n_batches; ++bi) {
-    const int cur = bi & 1;
-    const bool more = bi + 1 < n_batches;  // uniform over the workgroup
-    if (more) fetch(s_begin + (bi + 1) * rows_per_batch);
-
+  auto compute = [&](int cur) {
     // Per-column statistics for this lane's columns 4g .. 4g+3 and key c.
     float lse2[4], dl[4];
     bool on[4];
@@ -390,9 +385,32 @@ __global__ void __launch_bounds__(64 * kWaves)
         acc_k[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(qtr + 16 * t), di, acc_k[t], 0, 0, 0);
       }
     }
+  };
 
-    if (more) stash(cur ^ 1);  // the other buffer was last read before the previous barrier
+  Stage A, B;
+  for (int32_t c0 = s_begin; c0 < s_end; c0 += kRecChunk) {
+    n_rec = min(s_end - c0, static_cast<int32_t>(kRecChunk));
+    __syncthreads();  // the previous chunk's records and slabs are no longer read
+    for (int x = tid; x < n_rec; x += kThreads) recs[x] = segs[c0 + x];
     __syncthreads();
+    const int32_t n_batches = (n_rec + rows_per_batch - 1) / rows_per_batch;
+    fetch(A, 0);
+    stash(A, 0);
+    if (n_batches > 1) fetch(A, rows_per_batch);
+    if (n_batches > 2) fetch(B, 2 * rows_per_batch);
+    __syncthreads();
+    // X holds batch bi + 1 and Y batch bi + 2; the two stages swap roles every batch.
+    auto step = [&](int32_t bi, Stage& X, Stage& Y) {
+      const int cur = bi & 1;
+      compute(cur);
+      if (bi + 1 < n_batches) stash(X, cur ^ 1);  // the other buffer was last read before the previous barrier
+      if (bi + 3 < n_batches) fetch(X, (bi + 3) * rows_per_batch);
+      __syncthreads();
+    };
+    for (int32_t bi = 0; bi < n_batches; bi += 2) {  // workgroup-uniform
+      step(bi, A, B);
+      if (bi + 1 < n_batches) step(bi + 1, B, A);
+    }
   }
 
   if (n_parts > 1) {

@@ -444,50 +444,67 @@ __global__ void __launch_bounds__(64 * kWaves)
 
 // Split tiles: sum the parts' partial sums in part order (a fixed order, so
 // the result is deterministic) and write dk and dv.  One workgroup per
-// (b, 64-key tile, hk), wave w for keys 16w .. 16w+15; tiles that were not
-// split were written by dkdv_kernel.
+// (b, 64-key tile, hk, key group w of dkdv_kernel's wave w); its four waves
+// each sum a quarter of the group's dk and dv slices, two parts' loads in
+// flight at a time.  Tiles that were not split were written by dkdv_kernel.
 template <int D>
 __global__ void __launch_bounds__(64 * kWaves)
     dkdv_reduce_kernel(const int32_t* __restrict__ part_start, const int32_t* __restrict__ slot_start,
                        const float* __restrict__ partial, int64_t S_kv, int64_t Hkv, int64_t n_kt, int64_t n_tiles,
                        float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   using Gm = Geo<D>;
+  constexpr int kSlices = 2 * Gm::kDimTiles;  // dk tiles, then dv tiles, per key group
+  constexpr int kMine = kSlices / kWaves;     // slices per wave: this wave sums slices wave + kWaves * j
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int64_t x = blockIdx.x;
+  int64_t x = blockIdx.x;
   const int64_t hk = x % Hkv;
-  const int64_t unit = x / Hkv;
+  x /= Hkv;
+  const int w = static_cast<int>(x % kWaves);  // key group: keys 16w .. 16w+15 of the tile
+  const int64_t unit = x / kWaves;
   if (unit >= n_tiles) return;
   const int32_t n_parts = part_start[unit + 1] - part_start[unit];
   if (n_parts <= 1) return;
   const int64_t b = unit / n_kt;
-  const int64_t key0 = (unit % n_kt) * 64 + 16 * wave;
+  const int64_t key0 = (unit % n_kt) * 64 + 16 * w;
   const int c = lane & 15;
   const int g = lane >> 4;
-  f32x4 acc_k[Gm::kDimTiles], acc_v[Gm::kDimTiles];
+  auto part_ptr = [&](int32_t p) {
+    return partial + (((static_cast<int64_t>(slot_start[unit]) + p) * Hkv + hk) * kWaves + w) * (kSlices * 256) +
+           lane * 4;
+  };
+  f32x4 acc[kMine];
 #pragma unroll
-  for (int t = 0; t < Gm::kDimTiles; ++t) acc_k[t] = acc_v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int32_t p = 0; p < n_parts; ++p) {
-    const float* src = partial + (((static_cast<int64_t>(slot_start[unit]) + p) * Hkv + hk) * kWaves + wave) *
-                                     (2 * Gm::kDimTiles * 256);
+  for (int j = 0; j < kMine; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int32_t p = 0;
+  for (; p + 1 < n_parts; p += 2) {  // parts p and p + 1 loaded together, added in order
+    const float* s0 = part_ptr(p);
+    const float* s1 = part_ptr(p + 1);
+    f32x4 a0[kMine], a1[kMine];
 #pragma unroll
-    for (int t = 0; t < Gm::kDimTiles; ++t) {
-      acc_k[t] += *reinterpret_cast<const f32x4*>(src + (t * 64 + lane) * 4);
-      acc_v[t] += *reinterpret_cast<const f32x4*>(src + ((Gm::kDimTiles + t) * 64 + lane) * 4);
+    for (int j = 0; j < kMine; ++j) {
+      a0[j] = *reinterpret_cast<const f32x4*>(s0 + (wave + kWaves * j) * 256);
+      a1[j] = *reinterpret_cast<const f32x4*>(s1 + (wave + kWaves * j) * 256);
     }
+#pragma unroll
+    for (int j = 0; j < kMine; ++j) acc[j] = (acc[j] + a0[j]) + a1[j];
+  }
+  if (p < n_parts) {
+    const float* s0 = part_ptr(p);
+#pragma unroll
+    for (int j = 0; j < kMine; ++j) acc[j] += *reinterpret_cast<const f32x4*>(s0 + (wave + kWaves * j) * 256);
   }
   if (key0 + c < S_kv) {
     const int64_t off = ((b * S_kv + key0 + c) * Hkv + hk) * D + 4 * g;
 #pragma unroll
-    for (int t = 0; t < Gm::kDimTiles; ++t) {
-      bf16x4 wk, wv;
+    for (int j = 0; j < kMine; ++j) {
+      const int slice = wave + kWaves * j;
+      const bool is_k = slice < Gm::kDimTiles;
+      const int t = is_k ? slice : slice - Gm::kDimTiles;
+      bf16x4 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        wk[r] = static_cast<__bf16>(acc_k[t][r] * scale);
-        wv[r] = static_cast<__bf16>(acc_v[t][r]);
-      }
-      *reinterpret_cast<u32x2*>(dk + off + 16 * t) = __builtin_bit_cast(u32x2, wk);
-      *reinterpret_cast<u32x2*>(dv + off + 16 * t) = __builtin_bit_cast(u32x2, wv);
+      for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(is_k ? acc[j][r] * scale : acc[j][r]);
+      *reinterpret_cast<u32x2*>((is_k ? dk : dv) + off + 16 * t) = __builtin_bit_cast(u32x2, o);
     }
   }
 }
@@ -524,7 +541,7 @@ hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t stream) {
                      a.partial, a.dk, a.dv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3(static_cast<uint32_t>(n_tiles * a.Hkv)), dim3(64 * kWaves), 0,
+  hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3(static_cast<uint32_t>(n_tiles * kWaves * a.Hkv)), dim3(64 * kWaves), 0,
                      stream, a.part_start, a.slot_start, a.partial, a.S_kv, a.Hkv, n_kt, n_tiles, a.scale, a.dk, a.dv);
   return hipGetLastError();
 }

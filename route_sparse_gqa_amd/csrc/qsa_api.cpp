@@ -389,7 +389,7 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
   if (!bwd_layout(B, S_q, S_kv, Hq, Hkv, D, K, &l)) return QSA_ERR_LIMIT;
   int64_t kv_elems = 0;
   if (!mul_ok(B * S_kv, Hkv * D, &kv_elems) || kv_elems > (INT64_MAX >> 2)) return QSA_ERR_LIMIT;
-  if ((l.n_kt * B + l.max_parts) * Hkv > kMaxGrid || (s.rows + 3) / 4 > kMaxGrid ||
+  if ((l.n_kt * B + l.max_parts) * Hkv > kMaxGrid || l.n_kt * B * 4 * Hkv > kMaxGrid || (s.rows + 3) / 4 > kMaxGrid ||
       (B * ((S_q + qsa::kSegChunkRows - 1) / qsa::kSegChunkRows) * l.n_kt + 255) / 256 > kMaxGrid)
     return QSA_ERR_LIMIT;
   if (workspace == nullptr || workspace_bytes < l.total || !aligned(workspace, kWorkspaceAlign))

@@ -98,12 +98,13 @@ __global__ void __launch_bounds__(kThreads)
       uint8_t* dst = membership + row * ldm + c0;  // 64-bit offset
       for (int ch = lane; ch < n_chunks; ch += 64) {
         const uint32_t h = (bits[ch >> 1] >> ((ch & 1) * 16)) & 0xFFFFu;
-        uint4 o;
+        u32x4 o;
         o.x = spread4(h & 0xFu);
         o.y = spread4((h >> 4) & 0xFu);
         o.z = spread4((h >> 8) & 0xFu);
         o.w = spread4(h >> 12);
-        *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(ch) * 16) = o;
+        // The table is written once and not read back by this path: stream it past the caches.
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(ch) * 16));
       }
     }
     if (tile_count != nullptr) {

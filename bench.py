@@ -12,7 +12,10 @@ Prints ONE JSON line (rank 0):
   roofline     the gather-attention kernel against the 8 TB/s HBM roofline:
                algorithmic bytes per launch (routed K and V rows once per
                (query row, KV head), Q, O, lists and counts) over its average
-               launch time, measured with HIP events on the launch stream;
+               launch time, measured with HIP events on the launch stream
+               (also its median and minimum, and the compulsory bytes: Q, O,
+               lists, counts and each distinct routed K/V row once, with the
+               time floor they and the flops set at 8 TB/s and 2.5 PFLOP/s);
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same rows.
 
 With ``--pass backward`` it times the backward instead (one step = one
@@ -74,7 +77,33 @@ def parse_args():
                     help="JSON with rocprofv3-derived HBM bytes per launch of the attention kernel")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run plain device-to-device copies of this many MiB (counter calibration)")
+    ap.add_argument("--calibrate-matmul", type=int, default=0,
+                    help="only run bf16 n x n x n library matmuls (MFMA busy-counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_matmul(n: int, reps: int = 10) -> None:
+    """Library bf16 matmuls of a known flop count timed with events: the MFMA busy cycles per dispatch
+    at a measured fraction of the bf16 peak give the scale for reading the counter on other kernels."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16).contiguous()
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        torch.matmul(a, b, out=c)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"calibration": "bf16 matmul", "n": n, "ms_median": ms, "tflops": tflops,
+                      "frac_of_peak": tflops / MFMA_BF16_PEAK_TFLOPS}), flush=True)
 
 
 def calibrate_copy(mib: int, reps: int = 5) -> None:
@@ -187,6 +216,14 @@ def algorithmic_counts(w, N: int):
     return flops, kv_bytes + qo_bytes + list_bytes
 
 
+def compulsory_bytes(w, plan, N: int) -> int:
+    """Bytes no schedule can avoid: Q read, O written, lists and counts, and each K/V row some route
+    names read once per KV head (distinct IDs per batch row, from the membership table)."""
+    rows = w.B * w.S_q
+    distinct = int(plan.mem.amax(dim=1).to(dtype=plan.cnt.dtype).sum().item())
+    return 2 * 2 * w.D * w.Hkv * distinct + 2 * 2 * rows * w.Hq * w.D + 4 * N + 4 * rows
+
+
 def backward_counts(w, N: int, segments: int):
     """Algorithmic flops and bytes of one qsa_backward call.
 
@@ -242,6 +279,9 @@ def main():
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)
         return
+    if args.calibrate_matmul:
+        calibrate_matmul(args.calibrate_matmul)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -266,6 +306,7 @@ def main():
     counts = plan.cnt.cpu().numpy()
     N = int(counts.sum())
     flops, alg_bytes = algorithmic_counts(w, N)
+    min_bytes = compulsory_bytes(w, plan, N)
 
     if args.which == "backward":
         run_backward(args, w, plan, dev, N)
@@ -299,7 +340,8 @@ def main():
     total1.record(stream)
     torch.cuda.synchronize()
 
-    ms_att = sum(a.elapsed_time(b) for a, b in att_ev) / args.steps
+    att_ms = sorted(a.elapsed_time(b) for a, b in att_ev)
+    ms_att = sum(att_ms) / args.steps
     ms_pre = sum(a.elapsed_time(b) for a, b in pre_ev) / args.steps
     if scratch is None:
         ms_step = total0.elapsed_time(total1) / args.steps
@@ -346,7 +388,11 @@ def main():
             "traffic": traffic,
             "kernel": "gather_attention",
             "ms_per_launch": ms_att,
+            "ms_per_launch_median": att_ms[len(att_ms) // 2],
+            "ms_per_launch_min": att_ms[0],
             "alg_bytes_per_launch": alg_bytes,
+            "compulsory_bytes": min_bytes,
+            "t_floor_ms": max(min_bytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3,
         },
         "kernels_ms": {"preprocess(route_normalize+membership_tiles)": ms_pre, "gather_attention": ms_att},
         "cpu_baseline": cpu,

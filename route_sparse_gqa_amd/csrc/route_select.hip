@@ -28,13 +28,14 @@
 //    blocks are dispatched first.  fp32 scores go to a [rows, ld] workspace,
 //    only for rows that see more than kb blocks, only for visible blocks.
 //  * select_topk_kernel -- one workgroup per query row.  Scores sit in
-//    registers (E per thread, coalesced loads); three LDS-histogram passes
-//    over the float bit patterns (non-negative floats order like their bits;
-//    11, 11 and 10 bits) find the kb-th largest value tau and how many of
-//    the values equal to tau to keep.  Ballots build bitmaps of the values
-//    above tau and of those equal to it; a block prefix over the words keeps
-//    the lowest-index ties and places every kept block at its rank, in
-//    ascending block order.  The row is then written coalesced.
+//    registers (E per thread, coalesced loads; each launch covers rows whose
+//    length fits its E, slots past the row hold 0); three LDS-histogram
+//    passes over the nonzero float bit patterns (non-negative floats order
+//    like their bits; 11, 11 and 10 bits) find the kb-th largest value tau
+//    and how many of the values equal to tau to keep.  Ballots build bitmaps
+//    of the values above tau and of those equal to it; a block prefix over
+//    the words keeps the lowest-index ties and places every kept block at its
+//    rank, in ascending block order.  The row is then written coalesced.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -222,7 +223,7 @@ template <int NT, int E>
 __global__ void __launch_bounds__(NT)
     select_topk_kernel(const float* __restrict__ scores, int64_t ld, const int64_t* __restrict__ seq_lens,
                        int64_t S_q, int64_t q_offset, int64_t c, int64_t kb, int64_t budget, int64_t W,
-                       int64_t row_base, int32_t* __restrict__ out) {
+                       int64_t row_base, int64_t row0, int32_t* __restrict__ out) {
   constexpr int kWaves = NT / 64;
   constexpr int kWords = NT * E / 64;  // <= NT: one bitmap word per thread at most
   constexpr int kBinsPerThread = kBins / NT;
@@ -235,7 +236,7 @@ __global__ void __launch_bounds__(NT)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int64_t row = row_base + blockIdx.x;  // b * S_q + i
+  const int64_t row = row0 + blockIdx.x;  // b * S_q + i; the workspace starts at row row_base
   const int64_t b = row / S_q, i = row % S_q;
   const int64_t t = q_offset + i;
   int32_t* orow = out + row * W;
@@ -250,26 +251,31 @@ __global__ void __launch_bounds__(NT)
 
   if (sparse) {  // workgroup-uniform
     const float* srow = scores + (row - row_base) * ld;
-    const int n = static_cast<int>(nv);
-    const int ne = (n + NT - 1) / NT;
+    const int n = static_cast<int>(nv);  // <= NT * E (the launch picks E for the row's length)
     uint32_t key[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int idx = e * NT + tid;
-      key[e] = (e < ne && idx < n) ? __float_as_uint(srow[idx]) : 0u;
+      key[e] = idx < n ? __float_as_uint(srow[idx]) : 0u;
     }
+    // Slots past the row hold key 0.  Zero keys (+0.0 scores and those slots) are the smallest
+    // values and are left out of the histograms: while at least `remaining` nonzero keys carry
+    // the prefix, the kb-th largest value is the same with or without them; when fewer do (only
+    // possible with prefix 0), tau is 0 and the rest are zeros, which the lowest-index rule below
+    // takes from the row's own (lower indices, and the row has more than kb values).
     uint32_t prefix = 0, hi_mask = 0;
     int remaining = static_cast<int>(kb);
+    bool settled = false;  // workgroup-uniform: tau found to be 0
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
+      if (settled) continue;
       const int sh = p == 0 ? 21 : (p == 1 ? 10 : 0);
       const uint32_t dmask = p == 2 ? 0x3FFu : 0x7FFu;
       for (int q = tid; q < kBins; q += NT) hist[q] = 0u;
       __syncthreads();
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const int idx = e * NT + tid;
-        if (e < ne && idx < n && (key[e] & hi_mask) == prefix) atomicAdd(&hist[(key[e] >> sh) & dmask], 1u);
+        if (key[e] != 0u && (key[e] & hi_mask) == prefix) atomicAdd(&hist[(key[e] >> sh) & dmask], 1u);
       }
       __syncthreads();
       int local = 0;
@@ -277,6 +283,12 @@ __global__ void __launch_bounds__(NT)
       for (int q = 0; q < kBinsPerThread; ++q) local += static_cast<int>(hist[tid * kBinsPerThread + q]);
       int total = 0;
       const int before = block_exclusive_scan<NT>(local, wave_tot, &total);
+      if (total < remaining) {  // workgroup-uniform
+        prefix = 0u;
+        remaining -= total;
+        settled = true;
+        continue;
+      }
       const int above = total - before - local;  // candidates in higher bins than this thread's
       if (above < remaining && above + local >= remaining) {
         int acc = above;
@@ -298,12 +310,13 @@ __global__ void __launch_bounds__(NT)
     }
     const uint32_t tau = prefix;  // the kb-th largest value; keep `remaining` of the values equal to it
 
+    // A zero past the row is never above tau; it equals tau only when tau is 0, and then the
+    // lowest-index rule below takes the row's own zeros (all at lower indices, and at least
+    // `remaining` of them) first.
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int idx = e * NT + tid;
-      const bool valid = e < ne && idx < n;
-      const uint64_t bg = __ballot(valid && key[e] > tau);
-      const uint64_t be = __ballot(valid && key[e] == tau);
+      const uint64_t bg = __ballot(key[e] > tau);
+      const uint64_t be = __ballot(key[e] == tau);
       if (lane == 0) {
         gt_words[e * kWaves + wave] = bg;  // word e * kWaves + wave covers blocks 64 * word .. +63
         eq_words[e * kWaves + wave] = be;
@@ -359,21 +372,69 @@ hipError_t launch_scores_d(const SelectArgs& a, int hg, int64_t tile0, int64_t n
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const SelectArgs& a, int64_t nv_all, int64_t row_base, int64_t rows, int64_t ld,
-                       hipStream_t stream) {
+// Register width of the top-k for rows that see up to nv blocks: 256 threads x E slots, E a power
+// of two from 4 to 64, then 1024 x 64.
+int topk_class(int64_t nv) {
+  int cls = 0;
+  while (cls < 4 && nv > (int64_t{256} << (cls + 2))) ++cls;
+  return nv > 256 * 64 ? 5 : cls;
+}
+
+hipError_t launch_topk_rows(const SelectArgs& a, int cls, int64_t row_base, int64_t row0, int64_t rows, int64_t ld,
+                            hipStream_t stream) {
   const int64_t c = a.compress_ratio, kb = a.token_budget / c, W = a.token_budget + c - 1;
   const dim3 grid(static_cast<uint32_t>(rows));
 #define QSA_TOPK(NT, E)                                                                                          \
   hipLaunchKernelGGL((select_topk_kernel<NT, E>), grid, dim3(NT), 0, stream, a.scores, ld, a.seq_lens, a.S_q, \
-                     a.q_offset, c, kb, a.token_budget, W, row_base, a.out)
-  if (nv_all <= 256 * 4) QSA_TOPK(256, 4);
-  else if (nv_all <= 256 * 8) QSA_TOPK(256, 8);
-  else if (nv_all <= 256 * 16) QSA_TOPK(256, 16);
-  else if (nv_all <= 256 * 32) QSA_TOPK(256, 32);
-  else if (nv_all <= 256 * 64) QSA_TOPK(256, 64);
-  else QSA_TOPK(1024, 64);
+                     a.q_offset, c, kb, a.token_budget, W, row_base, row0, a.out)
+  switch (cls) {
+    case 0: QSA_TOPK(256, 4); break;
+    case 1: QSA_TOPK(256, 8); break;
+    case 2: QSA_TOPK(256, 16); break;
+    case 3: QSA_TOPK(256, 32); break;
+    case 4: QSA_TOPK(256, 64); break;
+    default: QSA_TOPK(1024, 64); break;
+  }
 #undef QSA_TOPK
   return hipGetLastError();
+}
+
+// Rows [row_base, row_base + rows) of the pass, split into runs of rows of one register class
+// (the visible blocks grow with the query position), one launch per run.  With more runs than
+// kMaxTopkLaunches (many batch rows that each span several classes) one launch at the class of
+// the longest row does all.
+hipError_t launch_topk(const SelectArgs& a, int64_t nv_all, int64_t row_base, int64_t rows, int64_t ld,
+                       hipStream_t stream) {
+  constexpr int64_t kMaxTopkLaunches = 64;
+  const int64_t c = a.compress_ratio, row_end = row_base + rows;
+  auto class_of_row = [&](int64_t r) { return topk_class((a.q_offset + r % a.S_q + 1) / c); };
+  // Next row after r (same batch row) whose class differs, or the batch row's end.
+  auto run_end = [&](int64_t r) {
+    const int cls = class_of_row(r);
+    const int64_t batch_end = (r / a.S_q + 1) * a.S_q;
+    if (cls == 5) return min(batch_end, row_end);
+    // last position t with (t + 1) / c <= 256 << (cls + 2): t + 1 < ((256 << (cls + 2)) + 1) * c
+    const int64_t t_lim = ((int64_t{256} << (cls + 2)) + 1) * c - 1;  // first t past the class
+    const int64_t r_lim = r - r % a.S_q + (t_lim - a.q_offset);
+    return min(min(batch_end, row_end), max(r_lim, r + 1));
+  };
+  // Adjacent runs of one class (the next batch row starting where the last one ended) merge.
+  auto merged_end = [&](int64_t r) {
+    const int cls = class_of_row(r);
+    int64_t e = run_end(r);
+    while (e < row_end && class_of_row(e) == cls) e = run_end(e);
+    return e;
+  };
+  int64_t n_runs = 0;
+  for (int64_t r = row_base; r < row_end && n_runs <= kMaxTopkLaunches; r = merged_end(r)) ++n_runs;
+  if (n_runs > kMaxTopkLaunches) return launch_topk_rows(a, topk_class(nv_all), row_base, row_base, rows, ld, stream);
+  for (int64_t r = row_base; r < row_end;) {
+    const int64_t e = merged_end(r);
+    const hipError_t err = launch_topk_rows(a, class_of_row(r), row_base, r, e - r, ld, stream);
+    if (err != hipSuccess) return err;
+    r = e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace

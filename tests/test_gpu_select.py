@@ -128,6 +128,44 @@ def test_select_all_ties_keep_lowest_blocks():
     assert (got[0, -1, :budget] == np.arange(budget)).all()
 
 
+def test_select_fewer_nonzero_scores_than_the_budget():
+    """Only every seventh block has a nonzero key, so many rows have fewer positive scores than kb
+    blocks: every positive block is kept and the lowest-index zero-score blocks fill the rest."""
+    B, S_q, H, D, c, budget = 1, 2600, 4, 64, 2, 512
+    iq, ck = random_select_case(77, B, S_q, H, D, S_q // c, integer=True)
+    ck[:, np.arange(S_q // c) % 7 != 0] = 0
+    lens = np.array([S_q], np.int64)
+    assert (oracle.block_scores(iq, ck, rows=(S_q - 1, S_q)) > 0).sum() < budget // c  # even the last row
+    got = run_gpu(iq, ck, lens, budget, c)
+    np.testing.assert_array_equal(got, oracle.select_token_ids(iq, ck, lens, budget, c))
+
+
+def test_select_rows_at_the_topk_register_classes():
+    """c = 1: rows see t + 1 blocks, so the rows cross every register width of the top-k (256 x 4 ..
+    256 x 64 slots); rows on both sides of each boundary match the oracle exactly."""
+    B, S_q, H, D, c, budget = 2, 9000, 2, 64, 1, 600
+    iq, ck = random_select_case(78, B, S_q, H, D, S_q, integer=True)
+    lens = np.array([S_q, 8500], np.int64)
+    got = run_gpu(iq, ck, lens, budget, c)
+    for edge in (1024, 2048, 4096, 8192, 9000):
+        rows = (edge - 3, min(edge + 3, S_q))
+        want = oracle.select_token_ids(iq, ck, lens, budget, c, rows=rows)
+        np.testing.assert_array_equal(got[:, rows[0]:rows[1]], want, err_msg=f"rows {rows}")
+
+
+def test_select_many_batch_rows_one_topk_launch():
+    """33 batch rows that each span two register widths (66 runs) take one launch at the widest."""
+    B, S_q, H, D, c, budget = 33, 1100, 2, 64, 1, 256
+    iq, ck = random_select_case(79, B, S_q, H, D, S_q, integer=True)
+    lens = np.full(B, S_q, np.int64)
+    lens[5] = 600
+    got = run_gpu(iq, ck, lens, budget, c)
+    rows = (1000, S_q)
+    want = oracle.select_token_ids(iq, ck, lens, budget, c, rows=rows)
+    np.testing.assert_array_equal(got[:, rows[0]:rows[1]], want)
+    np.testing.assert_array_equal(got[:, 240:260], oracle.select_token_ids(iq, ck, lens, budget, c, rows=(240, 260)))
+
+
 # --------------------------------------------------------- continuous cases
 
 CONT_CASES = [  # B, S_q, H, D, c, budget

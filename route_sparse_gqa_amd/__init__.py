@@ -138,6 +138,14 @@ def _require_gpu(*tensors: torch.Tensor) -> torch.device:
     return dev
 
 
+def _on_device(t: torch.Tensor, dev: torch.device, name: str) -> torch.Tensor:
+    """A caller-supplied output or workspace: it must live on the inputs' GPU (the library writes
+    through its raw pointer)."""
+    if t.device != dev:
+        raise ValueError(f"{name} must be on the inputs' device {dev}, got {t.device}")
+    return t
+
+
 def _route_dtype(routes: torch.Tensor) -> int:
     if routes.dtype == torch.int64:
         return QSA_INT64
@@ -248,6 +256,7 @@ def qsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, routes: torch
     ws_bytes = qsa_forward_workspace_size(B, S_q, K)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _on_device(workspace, dev, "workspace")
     st = lib().qsa_forward(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(routes), dt,
                            _strides(routes), B, S_q, S_kv, Hq, Hkv, D, K, _scale(scale, D), _ptr(out),
                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
@@ -313,6 +322,7 @@ def qsa_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.T
     ws_bytes = qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _on_device(workspace, dev, "workspace")
     st = lib().qsa_backward(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(out),
                             _ptr(dout), _strides(dout), _ptr(lse), _ptr(route_list), _ptr(route_count), B, S_q,
                             S_kv, Hq, Hkv, D, K, _scale(scale, D), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
@@ -352,6 +362,7 @@ def qsa_select_token_ids(index_queries: torch.Tensor, compressed_keys: torch.Ten
         out = torch.empty((B, S_q, max(width, 0)), dtype=torch.int32, device=dev)
     elif out.dtype != torch.int32 or tuple(out.shape) != (B, S_q, width) or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous int32 tensor of shape {(B, S_q, width)}")
+    _on_device(out, dev, "out")
     if workspace is None:
         full = qsa_select_workspace_size(B, S_q, H, q_off, c)
         ws_bytes = full
@@ -361,6 +372,7 @@ def qsa_select_token_ids(index_queries: torch.Tensor, compressed_keys: torch.Ten
             per_tile = full // tiles
             ws_bytes = min(full, max(1, -(-int(query_chunk_size) // tile_rows)) * per_tile)
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _on_device(workspace, dev, "workspace")
     st = lib().qsa_select_token_ids(_ptr(iq), _strides(iq), _ptr(ck), _strides(ck), _ptr(lens), B, S_q, H, D,
                                     S_global, q_off, budget, c, _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(dev))

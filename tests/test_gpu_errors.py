@@ -131,3 +131,18 @@ def test_cpu_tensors_fail_loudly():
     q, k, v, r = (t.cpu() for t in _inputs())
     with pytest.raises(ValueError, match="ROCm GPU"):
         qsa.qsa_forward(q, k, v, r)
+
+
+def test_caller_buffers_on_another_device_fail_before_any_launch():
+    """A workspace or output the caller passes must be on the inputs' GPU: the library writes
+    through its pointer, so a host tensor is refused by the binding."""
+    q, k, v, r = _inputs()
+    with pytest.raises(ValueError, match="workspace must be on"):
+        qsa.qsa_forward(q, k, v, r, workspace=torch.empty(1 << 16, dtype=torch.uint8))
+    iq = torch.zeros(1, 64, 4, 64, dtype=torch.bfloat16, device=device())
+    ck = torch.zeros(1, 16, 1, 64, dtype=torch.bfloat16, device=device())
+    lens = torch.full((1,), 64, dtype=torch.int64, device=device())
+    with pytest.raises(ValueError, match="out must be on"):
+        qsa.qsa_select_token_ids(iq, ck, lens, 16, 4, out=torch.empty(1, 64, 19, dtype=torch.int32))
+    with pytest.raises(ValueError, match="workspace must be on"):
+        qsa.qsa_select_token_ids(iq, ck, lens, 16, 4, workspace=torch.empty(1 << 20, dtype=torch.uint8))

@@ -104,23 +104,30 @@ __global__ void __launch_bounds__(kScoreThreads)
   const int m = lane & 15;  // head row of the A operand; block column of B and of the result
   const int g = lane >> 4;  // k-group of the operands; head quad of the result
 
-  // Key pieces of one chunk: thread tid holds pieces tid + 256 u (zeros past seg_end).
-  const uint16_t* kbase = ck + b * cs0;
+  // Key pieces of one chunk: thread tid holds piece tid % kPieces of blocks tid / kPieces + u kRows
+  // (zeros past seg_end).  One address per chunk and a constant stride per piece; only the last,
+  // partial chunk of a segment tests its blocks against seg_end.
+  constexpr int kRows = kScoreThreads / Geo::kPieces;  // blocks covered by one piece per thread
+  const int prow = tid / Geo::kPieces, pcol = 8 * (tid % Geo::kPieces);
+  const uint16_t* kbase = ck + b * cs0 + prow * cs1 + pcol;
+  const int64_t kstep = kRows * cs1;
   u32x4 pre[Geo::kPerThread];
   auto fetch = [&](int64_t j0) {
+    const uint16_t* src = kbase + j0 * cs1;
+    if (j0 + Geo::kChunk <= seg_end) {  // workgroup-uniform
 #pragma unroll
-    for (int u = 0; u < Geo::kPerThread; ++u) {
-      const int p = tid + kScoreThreads * u;
-      const int64_t blk = j0 + p / Geo::kPieces;
-      pre[u] = blk < seg_end ? load16(kbase + blk * cs1 + 8 * (p % Geo::kPieces)) : u32x4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < Geo::kPerThread; ++u) pre[u] = load16(src + u * kstep);
+    } else {
+      const int64_t left = seg_end - j0 - prow;  // this thread's blocks in range: kRows u < left
+#pragma unroll
+      for (int u = 0; u < Geo::kPerThread; ++u)
+        pre[u] = kRows * u < left ? load16(src + u * kstep) : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  uint16_t* sdst = kslab + prow * Geo::kStride + pcol;
   auto stage = [&]() {
 #pragma unroll
-    for (int u = 0; u < Geo::kPerThread; ++u) {
-      const int p = tid + kScoreThreads * u;
-      *reinterpret_cast<u32x4*>(kslab + (p / Geo::kPieces) * Geo::kStride + 8 * (p % Geo::kPieces)) = pre[u];
-    }
+    for (int u = 0; u < Geo::kPerThread; ++u) *reinterpret_cast<u32x4*>(sdst + u * kRows * Geo::kStride) = pre[u];
   };
   fetch(seg0);
 

@@ -77,6 +77,8 @@ def parse_args():
                     help="JSON with rocprofv3-derived HBM bytes per launch of the attention kernel")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run plain device-to-device copies of this many MiB (counter calibration)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step (preprocess + attention) in a HIP graph and time its replays")
     ap.add_argument("--calibrate-matmul", type=int, default=0,
                     help="only run bf16 n x n x n library matmuls (MFMA busy-counter calibration)")
     return ap.parse_args()
@@ -153,6 +155,12 @@ class Plan:
                          i8(self.cnt), B, S_q, w.S_kv, w.Hq, w.Hkv, w.D, K, ctypes.c_float(w.scale),
                          i8(self.out), None, self.stream)
 
+    def set_stream(self, stream: ctypes.c_void_p) -> None:
+        """Point the pre-marshalled calls at another HIP stream (the stream is their last argument)."""
+        self.stream = stream
+        self.pre_args = self.pre_args[:-1] + (stream,)
+        self.fwd_args = self.fwd_args[:-1] + (stream,)
+
     def setup_backward(self, dev):
         """Forward with log-sum-exp once, then pre-marshal qsa_backward (dout drawn from its own stream)."""
         import torch
@@ -214,6 +222,31 @@ def algorithmic_counts(w, N: int):
     qo_bytes = 2 * 2 * rows * w.Hq * w.D         # Q read + O written, bf16
     list_bytes = 4 * N + 4 * rows                # compacted IDs read + counts
     return flops, kv_bytes + qo_bytes + list_bytes
+
+
+def time_graph_replays(plan, dev, steps: int, warmup: int, flops: int) -> dict:
+    """One step (preprocess + attention) captured in a HIP graph; replays timed with HIP events."""
+    import torch
+
+    eager_stream = plan.stream
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):  # torch's capture stream is current inside
+        plan.set_stream(ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+        plan.preprocess()
+        plan.attention()
+    plan.set_stream(eager_stream)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": ms, "value": flops / (ms * 1e-3) / 1e12}
 
 
 def compulsory_bytes(w, plan, N: int) -> int:
@@ -349,6 +382,10 @@ def main():
         ms_step = sum(p[0].elapsed_time(a[1]) for p, a in zip(pre_ev, att_ev)) / args.steps
     achieved = alg_bytes / (ms_att * 1e-3) / 1e9
 
+    graph = None
+    if args.graph:
+        graph = time_graph_replays(plan, dev, args.steps, args.warmup, flops)
+
     traffic = None
     if os.path.exists(args.traffic):
         with open(args.traffic) as f:
@@ -395,6 +432,7 @@ def main():
             "t_floor_ms": max(min_bytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3,
         },
         "kernels_ms": {"preprocess(route_normalize+membership_tiles)": ms_pre, "gather_attention": ms_att},
+        "graph": graph,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -104,6 +104,7 @@ EXACT_CASES = [  # B, S_q, H, D, c, budget, lens, q_offset, S_global
     (1, 129, 16, 128, 4, 3, (129,), 0, 129),           # budget < c: tails only
     (1, 600, 16, 64, 4, 1000, (600,), 0, 600),         # budget above every row's visible blocks
     (1, 2500, 8, 64, 2, 512, (2500,), 0, 2500),        # 1250 blocks: 5 score chunks, radix over 1250
+    (1, 64, 4, 64, 1, 700, (17000,), 16360, 17000),    # rows across 16384 blocks: 256 x 64 and 1024 x 64 top-k
 ]
 
 

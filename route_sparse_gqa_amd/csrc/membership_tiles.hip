@@ -103,8 +103,7 @@ __global__ void __launch_bounds__(kThreads)
         o.y = spread4((h >> 4) & 0xFu);
         o.z = spread4((h >> 8) & 0xFu);
         o.w = spread4(h >> 12);
-        // The table is written once and not read back by this path: stream it past the caches.
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(ch) * 16));
+        *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(ch) * 16) = o;
       }
     }
     if (tile_count != nullptr) {

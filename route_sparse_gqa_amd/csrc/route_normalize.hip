@@ -27,7 +27,8 @@
 // and the number of IDs before it; half-wavefronts expand one listed word
 // each (lane j writes bit j's ID at its rank), so the IDs come out ascending
 // with no sort and no per-bit loop: O(K + kv_length / 32) work per row
-// instead of O(K log^2 K).
+// instead of O(K log^2 K).  Rows with kv_length <= 16384 and K <= 1024 take
+// one wavefront each (route_wave_kernel), the others one workgroup.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -284,14 +285,108 @@ hipError_t launch_sorted(const RouteT* routes, const int64_t* st, int64_t B, int
   return hipGetLastError();
 }
 
+// Small rows (kv_length <= 32 * kWaveWords = 16384, K <= 1024): the bitmap
+// method of route_bitmap_kernel with one wavefront per row and four rows per
+// workgroup, so no workgroup barrier is needed and every row of a call is in
+// flight at once.  Lane l holds slots q * 64 + l and owns bitmap words
+// l * wpl .. l * wpl + wpl - 1 (wpl = ceil(words / 64) <= 8) for the scan.
+constexpr int kWaveRows = 4;
+constexpr int kWaveWords = 512;
+
+template <int kSlots, typename RouteT>
+__global__ void __launch_bounds__(64 * kWaveRows)
+    route_wave_kernel(const RouteT* __restrict__ routes, int64_t rs0, int64_t rs1, int64_t rs2, int64_t S_q,
+                      int64_t n_rows, int64_t K, int64_t kv_length, int32_t* __restrict__ route_list,
+                      int32_t* __restrict__ route_count, int32_t* __restrict__ zero_buf, int64_t zero_count) {
+  constexpr int kWpl = kWaveWords / 64;  // bitmap words per lane at most
+  __shared__ uint32_t region[kWaveRows][kWaveWords];   // each wavefront's bitmap
+  __shared__ uint32_t nonzero[kWaveRows][kWaveWords];  // its non-zero words: index << 16 | IDs before
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaveRows + wave;
+  if (row < n_rows) {  // wavefront-uniform; the wavefronts never wait for one another
+    uint32_t* bits = region[wave];
+    const int nw = static_cast<int>((kv_length + 31) / 32);
+    const int wpl = (nw + 63) / 64;
+    const int Ki = static_cast<int>(K);
+    const RouteT* src = routes + (row / S_q) * rs0 + (row % S_q) * rs1;
+    int64_t x[kSlots];  // every slot is loaded before any is used
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+      const int s = q * 64 + lane;
+      x[q] = s < Ki ? static_cast<int64_t>(src[s * rs2]) : int64_t{-1};  // int32 IDs sign-extend
+    }
+    for (int w = lane; w < nw; w += 64) bits[w] = 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+      if (q * 64 >= Ki) continue;  // wavefront-uniform: every lane meets the shuffles
+      const bool ok = x[q] >= 0 && x[q] < kv_length;
+      wave_or_runs(bits, ok ? static_cast<uint32_t>(x[q] >> 5) : 0xFFFFFFFFu, ok ? 1u << (x[q] & 31) : 0u);
+    }
+    wave_lds_sync();
+
+    // One wavefront prefix sum of (non-zero words << 16 | set bits) over the lanes' word runs.
+    uint32_t mine[kWpl];
+    int packed = 0;
+#pragma unroll
+    for (int q = 0; q < kWpl; ++q) {
+      const int w = lane * wpl + q;
+      mine[q] = (q < wpl && w < nw) ? bits[w] : 0u;
+      packed += (mine[q] != 0u ? 1 << 16 : 0) + __popc(mine[q]);
+    }
+    int incl = packed;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int all = __shfl(incl, 63);
+    const int before = incl - packed;
+    int slot = before >> 16, ids = before & 0xFFFF;
+#pragma unroll
+    for (int q = 0; q < kWpl; ++q) {
+      if (mine[q] != 0u) {
+        nonzero[wave][slot++] = static_cast<uint32_t>((lane * wpl + q) << 16 | ids);
+        ids += __popc(mine[q]);
+      }
+    }
+    wave_lds_sync();
+    const int n_nonzero = all >> 16, total = all & 0xFFFF;
+
+    // Each half-wavefront expands one non-zero word: lane j writes bit j's ID at its rank.
+    int32_t* dst = route_list + row * K;
+    const int half = lane >> 5, j = lane & 31;
+    for (int e = half; e < n_nonzero; e += 2) {
+      const uint32_t entry = nonzero[wave][e];
+      const int w = static_cast<int>(entry >> 16);
+      const uint32_t word = bits[w];
+      if ((word >> j) & 1u) dst[(entry & 0xFFFFu) + __popc(word & ((1u << j) - 1u))] = 32 * w + j;
+    }
+    for (int s = total + lane; s < Ki; s += 64) dst[s] = -1;
+    if (lane == 0) route_count[row] = total;
+  }
+  if (zero_buf != nullptr) {  // side job: clear the tile member counters (grid-stride)
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t z = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; z < zero_count; z += stride)
+      zero_buf[z] = 0;
+  }
+}
+
 template <typename RouteT>
 hipError_t dispatch(const RouteT* routes, const int64_t* st, int64_t B, int64_t S_q, int64_t K,
                     int64_t kv_length, int32_t* list, int32_t* count, int32_t* zb, int64_t zn,
                     hipStream_t stream) {
   const dim3 rows(static_cast<uint32_t>(B * S_q)), threads(kBitmapThreads);
-  if (kv_length <= 32 * 512 && K <= 512) {  // small rows: 4 KB of LDS, many workgroups per CU
-    hipLaunchKernelGGL((route_bitmap_kernel<512, RouteT>), rows, threads, 0, stream, routes, st[0], st[1], st[2], S_q,
-                       K, kv_length, list, count, zb, zn);
+  if (kv_length <= 32 * kWaveWords && K <= 1024) {  // small rows: one wavefront each
+    const int64_t n_rows = B * S_q;
+    const dim3 groups(static_cast<uint32_t>((n_rows + kWaveRows - 1) / kWaveRows)), wave_threads(64 * kWaveRows);
+    if (K <= 512)
+      hipLaunchKernelGGL((route_wave_kernel<8, RouteT>), groups, wave_threads, 0, stream, routes, st[0], st[1], st[2],
+                         S_q, n_rows, K, kv_length, list, count, zb, zn);
+    else
+      hipLaunchKernelGGL((route_wave_kernel<16, RouteT>), groups, wave_threads, 0, stream, routes, st[0], st[1],
+                         st[2], S_q, n_rows, K, kv_length, list, count, zb, zn);
     return hipGetLastError();
   }
   if (kv_length <= 32 * int64_t{kBitmapWords} && K <= kBitmapWords) {

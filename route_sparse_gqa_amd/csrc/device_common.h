@@ -37,25 +37,36 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// ORs `bits` into words[w] for every lane of the wavefront whose w is not
-// 0xFFFFFFFF.  Consecutive lanes holding the same word (the runs that
-// consecutive token IDs produce) are first merged by a segmented OR over
-// shuffles, so each run costs one LDS atomic instead of one per lane (lanes
-// of one atomic instruction that hit the same address are serialised).
-// Every lane of the wavefront must call it.
-__device__ __forceinline__ void wave_or_runs(uint32_t* words, uint32_t w, uint32_t bits) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t prev = static_cast<uint32_t>(__shfl_up(static_cast<int>(w), 1));
-  const bool head = lane == 0 || prev != w;
-  const uint64_t heads = __ballot(head);
-  const uint64_t after = heads & ~((2ull << lane) - 1ull);  // heads above this lane (lane 63: none)
-  const int next = after != 0ull ? __builtin_ctzll(after) : 64;  // first lane of the next run
+// ORs bit (id & 31) into bits[id >> 5] for N consecutive entries of a route row staged in LDS
+// (`slots`, 16-byte aligned; -1 = no ID).  Consecutive entries usually hold consecutive token IDs,
+// so IDs that share a 32-bit word are merged in registers and one atomic OR is issued per run of
+// such entries (lanes of one atomic instruction that hit the same address serialise); any order
+// of IDs gives the same bitmap.
+template <int N>
+__device__ __forceinline__ void or_slot_run(uint32_t* bits, const int32_t* slots) {
+  int32_t id[N];
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t other = static_cast<uint32_t>(__shfl_down(static_cast<int>(bits), o));
-    if (lane + o < next) bits |= other;  // lanes l .. min(l + 2o, next) - 1 are now merged
+  for (int u = 0; u < N; u += 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(slots + u);
+    id[u] = static_cast<int32_t>(v.x);
+    id[u + 1] = static_cast<int32_t>(v.y);
+    id[u + 2] = static_cast<int32_t>(v.z);
+    id[u + 3] = static_cast<int32_t>(v.w);
   }
-  if (head && w != 0xFFFFFFFFu && bits != 0u) atomicOr(&words[w], bits);
+  uint32_t cur_w = 0xFFFFFFFFu, cur_b = 0u;
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const uint32_t w = id[u] >= 0 ? static_cast<uint32_t>(id[u]) >> 5 : 0xFFFFFFFFu;
+    const uint32_t b = id[u] >= 0 ? 1u << (id[u] & 31) : 0u;
+    if (w != cur_w) {
+      if (cur_b != 0u) atomicOr(&bits[cur_w], cur_b);
+      cur_w = w;
+      cur_b = b;
+    } else {
+      cur_b |= b;
+    }
+  }
+  if (cur_b != 0u) atomicOr(&bits[cur_w], cur_b);
 }
 
 // Byte offset of a gathered row: 32-bit when every row of the tensor lies

@@ -10,7 +10,8 @@
 // one segment of up to 65536 columns; each of its four wavefronts owns one
 // row with a private LDS bitmap of the segment (LDS sized to the segment).  Per row the wave
 // scatters the row's list into the bitmap (atomic OR, integer only; the
-// sorted list's runs of IDs in one word are merged in registers first, one
+// list passes through a small LDS buffer so that each lane takes consecutive
+// entries of the sorted list and merges those in one word in registers, one
 // atomic per run), expands
 // it to bytes with 16-byte stores (every byte of the row, padding included,
 // is written exactly once) and adds each 128-column tile's popcount to a
@@ -37,6 +38,7 @@ constexpr int kGroups = kTile / kGroupRows;      // workgroups per tile row and 
 constexpr int kTilesPerLane = kSegTiles / 64;  // 8
 
 constexpr int kBatch = 16;  // list entries per lane loaded together
+constexpr int kStage = 4;   // entries per lane per pass through the wave's LDS staging buffer
 
 // Four bits -> four bytes holding 0 or 1 (bit k lands in byte k).
 __device__ __forceinline__ uint32_t spread4(uint32_t nibble) { return (nibble * 0x00204081u) & 0x01010101u; }
@@ -45,7 +47,8 @@ __global__ void __launch_bounds__(kThreads)
     membership_tiles_kernel(const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count,
                             int64_t S_q, int64_t K, int64_t ldm, int64_t n_ti, int64_t n_tj, int64_t n_seg,
                             uint8_t* __restrict__ membership, int32_t* __restrict__ tile_count) {
-  extern __shared__ uint32_t lds[];  // per-wave bitmaps of the segment, then its tile counters (sized at launch)
+  // Per-wave bitmaps of the segment, its tile counters, then per-wave staging buffers (sized at launch).
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   int64_t blk = blockIdx.x;
@@ -63,6 +66,8 @@ __global__ void __launch_bounds__(kThreads)
   const int n_tiles = seg_cols / kTile;
   uint32_t* bits = lds + wave * seg_words;
   int* tile_sum = reinterpret_cast<int*>(lds + kWaves * seg_words);
+  // 16-byte aligned: seg_words is a multiple of 4 and the counters take a multiple of 4 words
+  int32_t* stage = reinterpret_cast<int32_t*>(lds + kWaves * seg_words + (n_tiles + 3) / 4 * 4) + wave * 64 * kStage;
   const int64_t r0 = ti * kTile + grp * kGroupRows;
   const int64_t r1 = min(r0 + kGroupRows, min(ti * kTile + kTile, S_q));
 
@@ -85,12 +90,21 @@ __global__ void __launch_bounds__(kThreads)
         const int j = j0 + 64 * u + lane;
         id[u] = j < n ? lst[j] : -1;
       }
+      // In passes of 64 * kStage entries through LDS, so that each lane takes kStage consecutive
+      // (ascending) entries and merges those in one bitmap word before its atomic.
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (j0 + 64 * u >= n) continue;  // wave-uniform
-        const int64_t col = static_cast<int64_t>(id[u]) - c0;
-        const bool ok = id[u] >= 0 && col >= 0 && col < seg_cols;
-        wave_or_runs(bits, ok ? static_cast<uint32_t>(col >> 5) : 0xFFFFFFFFu, ok ? 1u << (col & 31) : 0u);
+      for (int r = 0; r < kBatch / kStage; ++r) {
+        if (j0 + 64 * kStage * r >= n) continue;  // wave-uniform
+#pragma unroll
+        for (int t = 0; t < kStage; ++t) {
+          const int u = kStage * r + t;
+          const int64_t col = static_cast<int64_t>(id[u]) - c0;
+          const bool ok = id[u] >= 0 && col >= 0 && col < seg_cols;
+          stage[t * 64 + lane] = ok ? static_cast<int32_t>(col) : -1;
+        }
+        wave_lds_sync();
+        or_slot_run<kStage>(bits, stage + lane * kStage);
+        wave_lds_sync();  // the buffer is rewritten by the next pass
       }
     }
     wave_lds_sync();
@@ -162,7 +176,9 @@ hipError_t launch_membership_tiles(const int32_t* route_list, const int32_t* rou
   // tile_class holds member counts until the final pass; the route-normalise
   // launch that precedes this one on the stream has zeroed it.
   const int64_t seg_cols = ldm < kSegCols ? ldm : kSegCols;
-  const size_t lds_bytes = sizeof(uint32_t) * static_cast<size_t>(kWaves * (seg_cols / 32) + seg_cols / kTile);
+  const int64_t counter_words = (seg_cols / kTile + 3) / 4 * 4;  // tile counters, padded to 16 bytes
+  const size_t lds_bytes =
+      sizeof(uint32_t) * static_cast<size_t>(kWaves * (seg_cols / 32) + counter_words + kWaves * 64 * kStage);
   hipLaunchKernelGGL(membership_tiles_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), lds_bytes, stream,
                      route_list, route_count, S_q, K, ldm, n_ti, n_tj, n_seg, membership, tile_class);
   hipError_t e = hipGetLastError();

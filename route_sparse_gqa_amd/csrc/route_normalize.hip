@@ -21,8 +21,9 @@
 // When the key range is small (kv_length <= 32 * kBitmapWords = 131072) and
 // K <= kBitmapWords, a row is instead marked in an LDS bitmap of
 // kv_length bits (integer atomic OR, so duplicates collapse by
-// construction; runs of consecutive IDs in neighbouring slots are merged
-// within the wavefront first).  One workgroup prefix sum over contiguous
+// construction; the slots pass through LDS so that each lane takes a run of
+// consecutive slots and merges the IDs that share a bitmap word in
+// registers, one atomic per run).  One workgroup prefix sum over contiguous
 // runs of words then gives every non-zero word its index in a compact list
 // and the number of IDs before it; half-wavefronts expand one listed word
 // each (lane j writes bit j's ID at its rank), so the IDs come out ascending
@@ -193,7 +194,8 @@ __global__ void __launch_bounds__(kBitmapThreads)
   constexpr int T = kBitmapThreads;
   constexpr int kBitmapRun = kWords / T;  // bitmap words (and route slots) per thread
   __shared__ uint32_t region[kWords];   // the row's bitmap
-  __shared__ uint32_t nonzero[kWords];  // its non-zero words: index << 16 | IDs before the word
+  // The slots as IDs, then its non-zero words: index << 16 | IDs before the word.
+  __shared__ __attribute__((aligned(16))) uint32_t nonzero[kWords];
   __shared__ int wave_tot[T / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
@@ -210,13 +212,15 @@ __global__ void __launch_bounds__(kBitmapThreads)
     x[q] = s < Ki ? static_cast<int64_t>(src[s * rs2]) : int64_t{-1};  // int32 IDs sign-extend
   }
   for (int w = tid; w < nw; w += T) region[w] = 0u;
-  __syncthreads();
+  // The slots as validated int32 IDs in slot order, staged in the list array (free until the scan).
 #pragma unroll
   for (int q = 0; q < kBitmapRun; ++q) {
-    if (q * T >= Ki) continue;  // workgroup-uniform: every lane meets the shuffles
     const bool ok = x[q] >= 0 && x[q] < kv_length;
-    wave_or_runs(region, ok ? static_cast<uint32_t>(x[q] >> 5) : 0xFFFFFFFFu, ok ? 1u << (x[q] & 31) : 0u);
+    nonzero[q * T + tid] = ok ? static_cast<uint32_t>(x[q]) : 0xFFFFFFFFu;
   }
+  __syncthreads();
+  if (tid * kBitmapRun < Ki)
+    or_slot_run<kBitmapRun>(region, reinterpret_cast<const int32_t*>(nonzero) + tid * kBitmapRun);
   __syncthreads();
 
   // Thread tid owns words tid*run .. tid*run + run - 1.  One prefix sum over threads of
@@ -300,7 +304,8 @@ __global__ void __launch_bounds__(64 * kWaveRows)
                       int32_t* __restrict__ route_count, int32_t* __restrict__ zero_buf, int64_t zero_count) {
   constexpr int kWpl = kWaveWords / 64;  // bitmap words per lane at most
   __shared__ uint32_t region[kWaveRows][kWaveWords];   // each wavefront's bitmap
-  __shared__ uint32_t nonzero[kWaveRows][kWaveWords];  // its non-zero words: index << 16 | IDs before
+  // Its slots as IDs, then its non-zero words: index << 16 | IDs before the word.
+  __shared__ __attribute__((aligned(16))) uint32_t nonzero[kWaveRows][64 * kSlots];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaveRows + wave;
@@ -317,13 +322,14 @@ __global__ void __launch_bounds__(64 * kWaveRows)
       x[q] = s < Ki ? static_cast<int64_t>(src[s * rs2]) : int64_t{-1};  // int32 IDs sign-extend
     }
     for (int w = lane; w < nw; w += 64) bits[w] = 0u;
-    wave_lds_sync();
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) {
-      if (q * 64 >= Ki) continue;  // wavefront-uniform: every lane meets the shuffles
       const bool ok = x[q] >= 0 && x[q] < kv_length;
-      wave_or_runs(bits, ok ? static_cast<uint32_t>(x[q] >> 5) : 0xFFFFFFFFu, ok ? 1u << (x[q] & 31) : 0u);
+      nonzero[wave][q * 64 + lane] = ok ? static_cast<uint32_t>(x[q]) : 0xFFFFFFFFu;
     }
+    wave_lds_sync();
+    if (lane * kSlots < Ki)
+      or_slot_run<kSlots>(bits, reinterpret_cast<const int32_t*>(nonzero[wave]) + lane * kSlots);
     wave_lds_sync();
 
     // One wavefront prefix sum of (non-zero words << 16 | set bits) over the lanes' word runs.

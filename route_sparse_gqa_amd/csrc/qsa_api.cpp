@@ -26,15 +26,20 @@ struct Range {
   uintptr_t lo = 0, hi = 0;  // [lo, hi) bytes; empty when lo == hi
 };
 
-// Byte range touched by a strided tensor (shape/strides in elements).
-Range extent(const void* p, const int64_t* shape, const int64_t* strides, int rank, int64_t elem) {
+// Byte range touched by a strided tensor (shape/strides in elements, shape >= 1); false when an
+// offset does not fit in 64 bits (such strides are rejected as a size limit).
+bool extent(const void* p, const int64_t* shape, const int64_t* strides, int rank, int64_t elem, Range* out) {
   int64_t lo = 0, hi = 0;
   for (int d = 0; d < rank; ++d) {
-    const int64_t span = (shape[d] - 1) * strides[d];
-    if (span < 0) lo += span; else hi += span;
+    int64_t span = 0;
+    if (__builtin_mul_overflow(shape[d] - 1, strides[d], &span)) return false;
+    if (__builtin_add_overflow(span < 0 ? lo : hi, span, span < 0 ? &lo : &hi)) return false;
   }
+  int64_t lo_b = 0, hi_b = 0;
+  if (__builtin_mul_overflow(lo, elem, &lo_b) || __builtin_mul_overflow(hi + 1, elem, &hi_b)) return false;
   const uintptr_t base = reinterpret_cast<uintptr_t>(p);
-  return Range{base + static_cast<uintptr_t>(lo * elem), base + static_cast<uintptr_t>((hi + 1) * elem)};
+  *out = Range{base + static_cast<uintptr_t>(lo_b), base + static_cast<uintptr_t>(hi_b)};
+  return true;
 }
 
 Range dense(const void* p, int64_t bytes) {
@@ -147,7 +152,8 @@ QSA_EXPORT int qsa_preprocess(const void* routes, int routes_dtype, int64_t B, i
     return QSA_ERR_LIMIT;
 
   const int64_t rshape[3] = {B, S_q, K};
-  const Range r_in = extent(routes, rshape, route_strides, 3, relem);
+  Range r_in;
+  if (!extent(routes, rshape, route_strides, 3, relem, &r_in)) return QSA_ERR_LIMIT;
   const Range outs[4] = {dense(route_list, s.list_bytes), dense(route_count, s.count_bytes),
                          membership ? dense(membership, mem_bytes) : Range{},
                          tile_class ? dense(tile_class, 4 * tiles) : Range{}};
@@ -216,11 +222,13 @@ int check_attention(const void* q, const int64_t q_strides[4], const void* k, co
   if (!aligned(out, 16)) return QSA_ERR_LAYOUT;
   int64_t units = 0, out_elems = 0;
   if (!mul_ok(s->rows, Hkv, &units) || (s->rows + 3) / 4 * Hkv > kMaxGrid) return QSA_ERR_LIMIT;
-  if (!mul_ok(s->rows, Hq * D, &out_elems) || out_elems > (INT64_MAX >> 2)) return QSA_ERR_LIMIT;
+  int64_t row_elems = 0;
+  if (!mul_ok(Hq, D, &row_elems) || !mul_ok(s->rows, row_elems, &out_elems) || out_elems > (INT64_MAX >> 2))
+    return QSA_ERR_LIMIT;
   const int64_t qshape[4] = {B, S_q, Hq, D}, kshape[4] = {B, S_kv, Hkv, D};
-  *r_q = extent(q, qshape, q_strides, 4, 2);
-  *r_k = extent(k, kshape, k_strides, 4, 2);
-  *r_v = extent(v, kshape, v_strides, 4, 2);
+  if (!extent(q, qshape, q_strides, 4, 2, r_q) || !extent(k, kshape, k_strides, 4, 2, r_k) ||
+      !extent(v, kshape, v_strides, 4, 2, r_v))
+    return QSA_ERR_LIMIT;
   *r_out = dense(out, 2 * out_elems);
   if (overlap(*r_out, *r_q) || overlap(*r_out, *r_k) || overlap(*r_out, *r_v)) return QSA_ERR_ALIAS;
   return QSA_OK;
@@ -266,7 +274,8 @@ QSA_EXPORT int qsa_forward(const void* q, const int64_t q_strides[4], const void
   const size_t need = qsa_forward_workspace_size(B, S_q, K);
   if (need == 0 || workspace_bytes < need || !aligned(workspace, kWorkspaceAlign)) return QSA_ERR_WORKSPACE;
   const int64_t rshape[3] = {B, S_q, K};
-  const Range r_in = extent(routes, rshape, route_strides, 3, relem);
+  Range r_in;
+  if (!extent(routes, rshape, route_strides, 3, relem, &r_in)) return QSA_ERR_LIMIT;
   const Range r_ws = dense(workspace, static_cast<int64_t>(need));
   if (overlap(r_out, r_in) || overlap(r_out, r_ws) || overlap(r_ws, r_q) || overlap(r_ws, r_k) ||
       overlap(r_ws, r_v) || overlap(r_ws, r_in))
@@ -397,7 +406,8 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
 
   const int64_t qshape[4] = {B, S_q, Hq, D};
   const Range r_o = dense(out, 2 * s.rows * Hq * D);
-  const Range r_g = extent(dout, qshape, dout_strides, 4, 2);
+  Range r_g;
+  if (!extent(dout, qshape, dout_strides, 4, 2, &r_g)) return QSA_ERR_LIMIT;
   const Range r_lse = dense(lse, 4 * s.rows * Hq);
   const Range r_list = dense(route_list, s.list_bytes), r_count = dense(route_count, s.count_bytes);
   const Range r_dk = dense(dk, 2 * kv_elems), r_dv = dense(dv, 2 * kv_elems);
@@ -526,8 +536,9 @@ QSA_EXPORT int qsa_select_token_ids(const void* index_q, const int64_t q_strides
 
   const int64_t n_blocks = S_global / c;
   const int64_t qshape[4] = {B, S_q, H, D}, kshape[4] = {B, n_blocks > 0 ? n_blocks : 1, 1, D};
-  const Range r_q = extent(index_q, qshape, q_strides, 4, 2);
-  const Range r_k = extent(block_k, kshape, ks, 4, 2);
+  Range r_q, r_k;
+  if (!extent(index_q, qshape, q_strides, 4, 2, &r_q) || !extent(block_k, kshape, ks, 4, 2, &r_k))
+    return QSA_ERR_LIMIT;
   const Range r_len = dense(seq_lens, 8 * B);
   const Range r_out = dense(out, 4 * z.rows * z.width);
   const size_t used = std::min(workspace_bytes, static_cast<size_t>(z.full_bytes));

@@ -116,11 +116,11 @@ def test_backward_workspace_size():
 
 
 def _call_backward(B=1, S_q=4, S_kv=32, Hq=2, Hkv=1, D=64, K=2, scale=0.1, ws_bytes=1 << 30, alias_dq_q=False,
-                   null_lse=False):
+                   null_lse=False, k_row_stride=None):
     """Every call made with this helper carries one invalid argument (fake pointers never reach a launch)."""
     L = qsa.lib()
     sq = (ctypes.c_int64 * 4)(S_q * Hq * D, Hq * D, D, 1)
-    sk = (ctypes.c_int64 * 4)(S_kv * Hkv * D, Hkv * D, D, 1)
+    sk = (ctypes.c_int64 * 4)(S_kv * Hkv * D, Hkv * D if k_row_stride is None else k_row_stride, D, 1)
     f = [ctypes.c_void_p(n << 32) for n in range(1, 14)]  # distinct, never dereferenced
     q, k, v, o, g, lse, lst, cnt, dq, dk, dv, ws = f[:12]
     if alias_dq_q:
@@ -137,6 +137,8 @@ def test_backward_host_checks():
     assert _call_backward(null_lse=True) == -1
     assert _call_backward(alias_dq_q=True) == -9
     assert _call_backward(ws_bytes=16) == -10
+    assert _call_backward(k_row_stride=1 << 61) == -11    # the key tensor's extent overflows 64 bits
+    assert _call_backward(k_row_stride=-(1 << 61)) == -11
 
 
 def test_tile_lists_host_checks():
@@ -162,10 +164,10 @@ def test_select_workspace_size():
 
 
 def _call_select(B=1, S_q=64, H=4, D=64, S_global=64, q_offset=0, budget=8, c=4, ws_bytes=1 << 20,
-                 null_lens=False, alias_out_q=False, k_last_stride=1, misaligned_ws=False):
+                 null_lens=False, alias_out_q=False, k_last_stride=1, misaligned_ws=False, q_row_stride=None):
     """Every call made with this helper carries one invalid argument (fake pointers never reach a launch)."""
     L = qsa.lib()
-    sq = (ctypes.c_int64 * 4)(S_q * H * D, H * D, D, 1)
+    sq = (ctypes.c_int64 * 4)(S_q * H * D, H * D if q_row_stride is None else q_row_stride, D, 1)
     nb = max(S_global // max(c, 1), 1)
     sk = (ctypes.c_int64 * 4)(nb * D, D, D, k_last_stride)
     fq, fk, fl, fo, fw = (ctypes.c_void_p(n << 32) for n in range(1, 6))
@@ -193,3 +195,4 @@ def test_select_host_checks():
     assert _call_select(alias_out_q=True) == -9
     assert _call_select(ws_bytes=16) == -10          # smaller than one 16-row tile of scores
     assert _call_select(misaligned_ws=True) == -10
+    assert _call_select(q_row_stride=1 << 60) == -11        # the query tensor's extent overflows 64 bits

@@ -266,8 +266,8 @@ size_t qsa_select_workspace_size(int64_t B, int64_t S_q, int64_t H, int64_t q_of
  * qsa_select_token_ids -- route selection by compressed-block scores: the
  * producer of the routes the attention entry points consume.
  *
- * Definition (qsa page, `select_qsa_token_ids`; `Qwen3_8_FlashNextQSAIndexer`
- * for the output width token_budget + compress_ratio - 1): local query row i
+ * Definition (qsa page, `select_qsa_token_ids`; the page's indexer class for
+ * the output width token_budget + compress_ratio - 1): local query row i
  * stands at global position t = q_offset + i (q_offset = cp_rank * S_q under
  * contiguous context parallelism, 0 otherwise).  With c = compress_ratio and
  * kb = token_budget / c (integer division):

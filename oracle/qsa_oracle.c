@@ -391,7 +391,7 @@ void oracle_tile_lists(const int32_t *kinds, int64_t B, int64_t n_rows, int64_t 
 
 /*
  * Route selection by compressed-block scores (qsa page,
- * `select_qsa_token_ids`; `Qwen3_8_FlashNextQSAIndexer` for the output
+ * `select_qsa_token_ids`; the page's indexer class for the output
  * width).
  *
  * Inputs: index queries iq [B, S_q, H, D] and compressed block keys

@@ -119,6 +119,35 @@ def test_select_exact_integer_inputs(case):
     np.testing.assert_array_equal(got, want)
 
 
+def _draw_select_cases(n: int, seed: int = 7_2026):
+    """Seeded random selection shapes (integer inputs, so results must be exact), resampled while the
+    oracle's work would exceed 4 GFLOP."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    while len(cases) < n:
+        B, S_q = int(rng.integers(1, 4)), int(rng.integers(1, 500))
+        H, D = int(rng.integers(1, 65)), int(rng.choice([64, 128, 256]))
+        c = int(rng.choice([1, 2, 4, 8]))
+        q_offset = int(rng.integers(0, 400)) if rng.random() < 0.4 else 0
+        S_global = q_offset + S_q + (int(rng.integers(0, 100)) if q_offset else 0)
+        budget = int(rng.integers(1, 700))
+        lens = tuple(int(rng.integers(0, S_global + 1)) if rng.random() < 0.5 else S_global for _ in range(B))
+        if 2.0 * B * S_q * (S_global // c) * H * D > 4e9:
+            continue
+        cases.append((B, S_q, H, D, c, budget, lens, q_offset, S_global, int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _draw_select_cases(12), ids=lambda c: "x".join(map(str, c[:6])) + f"_off{c[7]}")
+def test_select_random_integer_shapes(case):
+    B, S_q, H, D, c, budget, lens, q_offset, S_global, seed = case
+    print(f"select random case {case}", flush=True)
+    iq, ck = random_select_case(seed, B, S_q, H, D, max(S_global // c, 1), integer=True)
+    lens = np.array(lens, dtype=np.int64)
+    got = run_gpu(iq, ck, lens, budget, c, q_offset, S_global)
+    np.testing.assert_array_equal(got, oracle.select_token_ids(iq, ck, lens, budget, c, q_offset))
+
+
 def test_select_all_ties_keep_lowest_blocks():
     B, S_q, H, D, c, budget = 1, 256, 16, 128, 4, 40
     iq = np.zeros((B, S_q, H, D), np.uint16)

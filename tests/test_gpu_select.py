@@ -138,7 +138,8 @@ def _draw_select_cases(n: int, seed: int = 7_2026):
     return cases
 
 
-@pytest.mark.parametrize("case", _draw_select_cases(12), ids=lambda c: "x".join(map(str, c[:6])) + f"_off{c[7]}")
+@pytest.mark.parametrize("case", _draw_select_cases(12),
+                         ids=lambda c: "x".join(map(str, c[:6])) + f"_off{c[7]}")
 def test_select_random_integer_shapes(case):
     B, S_q, H, D, c, budget, lens, q_offset, S_global, seed = case
     print(f"select random case {case}", flush=True)
@@ -214,6 +215,18 @@ def test_select_continuous_inputs(case):
     got = run_gpu(iq, ck, lens, budget, c)
     n_diff = check_rows(got, iq, ck, lens, budget, c, 0, (0, S_q), "continuous")
     assert n_diff <= 0.02 * B * S_q, f"{n_diff} rows differ from the oracle"
+
+
+@pytest.mark.parametrize("case", _draw_select_cases(6, seed=8_2026),
+                         ids=lambda c: "x".join(map(str, c[:6])) + f"_off{c[7]}")
+def test_select_random_continuous_shapes(case):
+    B, S_q, H, D, c, budget, lens, q_offset, S_global, seed = case
+    print(f"select random continuous case {case}", flush=True)
+    iq, ck = random_select_case(seed, B, S_q, H, D, max(S_global // c, 1))
+    lens = np.array(lens, dtype=np.int64)
+    got = run_gpu(iq, ck, lens, budget, c, q_offset, S_global)
+    n_diff = check_rows(got, iq, ck, lens, budget, c, q_offset, (0, S_q), "random continuous")
+    assert n_diff <= 0.02 * B * S_q + 1, f"{n_diff} rows differ from the oracle"
 
 
 def test_select_chunked_equals_one_pass():

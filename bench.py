@@ -79,9 +79,54 @@ def parse_args():
                     help="only run plain device-to-device copies of this many MiB (counter calibration)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step (preprocess + attention) in a HIP graph and time its replays")
+    ap.add_argument("--calibrate-gather", action="store_true",
+                    help="only measure the row-gather ceiling (libqsa_probe.so) for several table sizes")
     ap.add_argument("--calibrate-matmul", type=int, default=0,
                     help="only run bf16 n x n x n library matmuls (MFMA busy-counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_gather(reps: int = 5) -> None:
+    """Ceiling of the attention kernels' gather: random 512-byte rows of a table laid out like a K or V
+    tensor with two KV heads (1024-byte row stride), copied into LDS by the probe kernel with no
+    arithmetic, for tables whose rows fit the L2, the Infinity Cache, or neither."""
+    import torch
+
+    from route_sparse_gqa_amd.build import PROBE_LIB_PATH
+
+    L = ctypes.CDLL(PROBE_LIB_PATH)
+    L.qsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.qsa_probe_gather.restype = ctypes.c_int
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    n_waves, chunks, row_bytes, stride = 32768, 32, 512, 1024
+    n_ids = n_waves * chunks * 16
+    out = torch.empty(n_waves * 64, dtype=torch.int32, device=dev)
+    for rows in (4096, 8192, 16384, 32768, 65536, 262144, 1048576):
+        table = torch.ones(rows * stride, dtype=torch.uint8, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(rows)
+        ids = torch.randint(0, rows, (n_ids,), dtype=torch.int32, device=dev, generator=g)
+        for direct in (0, 1):  # through registers and LDS writes, or straight to LDS
+            args = (ctypes.c_void_p(table.data_ptr()), rows, stride, ctypes.c_void_p(ids.data_ptr()), n_waves,
+                    chunks, direct, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+            if L.qsa_probe_gather(*args) != 0:
+                raise RuntimeError("qsa_probe_gather failed")
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                L.qsa_probe_gather(*args)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+            print(json.dumps({"calibration": "row gather", "path": "direct to LDS" if direct else "registers",
+                              "rows": rows, "row_bytes": row_bytes, "row_stride_bytes": stride,
+                              "distinct_row_mib": rows * row_bytes / 2 ** 20, "gathered_bytes": n_ids * row_bytes,
+                              "ms_median": ms, "tb_per_s": n_ids * row_bytes / (ms * 1e-3) / 1e12}), flush=True)
+        del table, ids
 
 
 def calibrate_matmul(n: int, reps: int = 10) -> None:
@@ -314,6 +359,9 @@ def main():
         return
     if args.calibrate_matmul:
         calibrate_matmul(args.calibrate_matmul)
+        return
+    if args.calibrate_gather:
+        calibrate_gather()
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

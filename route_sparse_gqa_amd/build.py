@@ -33,6 +33,10 @@ SOURCES = [
     "qsa_api.cpp",
 ]
 
+# Measuring tool for bench.py --calibrate-gather, kept out of the attention library's API.
+PROBE_SOURCES = ["probe_gather.hip"]
+PROBE_LIB_PATH = os.path.join(PKG, "libqsa_probe.so")
+
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
@@ -65,19 +69,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+def _link(objs, path: str) -> None:
+    tmp = path + f".tmp{os.getpid()}"
     # -z defs: an entry point whose kernel file is missing fails here, not at load time
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES) + len(PROBE_SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB_PATH)
+    _link(objs[len(SOURCES):], PROBE_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PROBE_LIB_PATH}")
     return LIB_PATH
 
 

@@ -196,3 +196,20 @@ def test_select_host_checks():
     assert _call_select(ws_bytes=16) == -10          # smaller than one 16-row tile of scores
     assert _call_select(misaligned_ws=True) == -10
     assert _call_select(q_row_stride=1 << 60) == -11        # the query tensor's extent overflows 64 bits
+
+
+def test_probe_library_loads_and_checks_its_arguments():
+    """libqsa_probe.so (the gather-ceiling probe behind bench.py --calibrate-gather) is built beside the
+    library; every call below fails its host check, so nothing launches."""
+    from route_sparse_gqa_amd.build import PROBE_LIB_PATH
+
+    P = ctypes.CDLL(PROBE_LIB_PATH)
+    P.qsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.qsa_probe_gather.restype = ctypes.c_int
+    t, i, o = (ctypes.c_void_p(n << 32) for n in range(1, 4))  # distinct, never dereferenced
+    assert P.qsa_probe_gather(None, 16, 1024, i, 64, 1, 0, o, None) == -1
+    assert P.qsa_probe_gather(t, 0, 1024, i, 64, 1, 0, o, None) == -1         # no rows
+    assert P.qsa_probe_gather(t, 16, 256, i, 64, 1, 0, o, None) == -1         # stride below one row
+    assert P.qsa_probe_gather(t, 16, 1024, i, 64, 1, 2, o, None) == -1        # unknown path
+    assert P.qsa_probe_gather(ctypes.c_void_p((1 << 32) + 8), 16, 1024, i, 64, 1, 0, o, None) == -1  # misaligned

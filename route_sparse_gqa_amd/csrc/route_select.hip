@@ -51,13 +51,13 @@ constexpr int kScoreThreads = 256;
 constexpr int kSegmentBlocks = 4096;  // blocks per score workgroup at most
 constexpr int kBins = 2048;           // histogram bins of one radix pass (11 bits)
 
-template <int D>
+template <int D, int kChunkKB>
 struct SelGeo {
-  static constexpr int kSteps = D / 32;             // K-slices of one 16x16x32 product
-  static constexpr int kStride = D + 8;             // LDS row stride (bf16): 2D + 16 bytes
-  static constexpr int kPieces = D / 8;             // 16-byte pieces of one key row
-  static constexpr int kChunk = 16384 / D;          // blocks per LDS chunk (32 KB of keys)
-  static constexpr int kPerThread = kChunk * kPieces / kScoreThreads;  // 16-byte pieces per thread: 8
+  static constexpr int kSteps = D / 32;                  // K-slices of one 16x16x32 product
+  static constexpr int kStride = D + 8;                  // LDS row stride (bf16): 2D + 16 bytes
+  static constexpr int kPieces = D / 8;                  // 16-byte pieces of one key row
+  static constexpr int kChunk = kChunkKB * 512 / D;      // blocks per LDS chunk (kChunkKB KB of keys)
+  static constexpr int kPerThread = kChunk * kPieces / kScoreThreads;  // 16-byte pieces per thread: 8 or 4
 };
 
 // relu on the bit pattern: negative values and -0.0 (sign bit set, negative as int32) become +0.0.
@@ -65,14 +65,16 @@ __device__ __forceinline__ float relu(float v) { return __int_as_float(max(__flo
 
 __device__ __forceinline__ int64_t clamp_len(int64_t L, int64_t q_end) { return L < 0 ? 0 : (L > q_end ? q_end : L); }
 
-template <int D, int HG>
-__global__ void __launch_bounds__(kScoreThreads)
+// kChunkKB = 32: half the barriers; 16 (D = 128, rows that see more than one segment): the smaller
+// prefetch leaves room for four wavefronts per SIMD instead of three, which the compiler is held to.
+template <int D, int HG, int kChunkKB>
+__global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(kChunkKB == 16 ? 4 : 1)))
     select_scores_kernel(const uint16_t* __restrict__ iq, int64_t qs0, int64_t qs1, int64_t qs2,
                          const uint16_t* __restrict__ ck, int64_t cs0, int64_t cs1,
                          const int64_t* __restrict__ seq_lens, int64_t S_q, int64_t H, int64_t q_offset,
                          int64_t c, int64_t kb, int64_t tile0, int64_t n_tiles, int64_t tiles_per_batch,
                          int64_t n_segments, int64_t row_base, int64_t ld, float* __restrict__ scores) {
-  using Geo = SelGeo<D>;
+  using Geo = SelGeo<D, kChunkKB>;
   constexpr int RW = 4 / HG;   // query rows per wave
   constexpr int RPW = 4 * RW;  // query rows per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t kslab[Geo::kChunk * Geo::kStride];
@@ -366,14 +368,26 @@ hipError_t launch_scores_d(const SelectArgs& a, int hg, int64_t tile0, int64_t n
                            int64_t n_segments, int64_t row_base, int64_t ld, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>((n_tiles + 7) / 8 * 8 * n_segments));
   const int64_t kb = a.token_budget / a.compress_ratio;
-#define QSA_SCORES(HG)                                                                                          \
-  hipLaunchKernelGGL((select_scores_kernel<D, HG>), grid, dim3(kScoreThreads), 0, stream, a.iq, a.qs[0],       \
+#define QSA_SCORES(HG, KB)                                                                                      \
+  hipLaunchKernelGGL((select_scores_kernel<D, HG, KB>), grid, dim3(kScoreThreads), 0, stream, a.iq, a.qs[0],   \
                      a.qs[1], a.qs[2], a.ck, a.cs[0], a.cs[1], a.seq_lens, a.S_q, a.H, a.q_offset,              \
                      a.compress_ratio, kb, tile0, n_tiles, tiles_per_batch, n_segments, row_base, ld, a.scores)
-  switch (hg) {
-    case 1: QSA_SCORES(1); break;
-    case 2: QSA_SCORES(2); break;
-    default: QSA_SCORES(4); break;
+  if constexpr (D == 128) {
+    if (n_segments > 1) {  // long rows: many workgroups per tile, occupancy pays
+      switch (hg) {
+        case 1: QSA_SCORES(1, 16); break;
+        case 2: QSA_SCORES(2, 16); break;
+        default: QSA_SCORES(4, 16); break;
+      }
+      return hipGetLastError();
+    }
+  }
+  {
+    switch (hg) {
+      case 1: QSA_SCORES(1, 32); break;
+      case 2: QSA_SCORES(2, 32); break;
+      default: QSA_SCORES(4, 32); break;
+    }
   }
 #undef QSA_SCORES
   return hipGetLastError();

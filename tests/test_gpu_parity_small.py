@@ -16,6 +16,7 @@ import torch
 import oracle
 import route_sparse_gqa_amd as qsa
 from gpu_util import bf16_to_gpu, bits_to_f64, check_forward, device, gpu_bf16_bits
+from test_gpu_backward import check_lse
 from workloads.generators import random_small_case
 
 pytestmark = pytest.mark.gpu
@@ -126,6 +127,30 @@ def test_tile_classes_without_membership():
 def _run(q, k, v, r, scale=0.125):
     out = qsa.qsa_forward(bf16_to_gpu(q), bf16_to_gpu(k), bf16_to_gpu(v), torch.from_numpy(r).to(device()), scale)
     return gpu_bf16_bits(out)
+
+
+@pytest.mark.parametrize("K,Hq,Hkv", [(64, 16, 2), (16, 4, 1), (48, 8, 8)])
+def test_route_counts_at_every_chunk_boundary(K, Hq, Hkv):
+    """Rows routing 0, 1, 15, 16, 17, ..., K-1 and K distinct keys (16-key chunks), the last rows of
+    the buffer full; D = 256 with K a multiple of 16 is the configuration whose chunk IDs are read as
+    whole 64-byte windows of the list."""
+    B, S_q, S_kv, D = 2, 21, 3000, 256
+    rng = np.random.Generator(np.random.PCG64(K * 7 + Hq))
+    lengths = sorted({0, 1, 15, 16, 17, 31, 32, 33, K - 17, K - 16, K - 15, K - 1, K} & set(range(K + 1)))
+    routes = np.full((B, S_q, K), -1, dtype=np.int64)
+    for b in range(B):
+        for i in range(S_q):
+            n = K if i >= S_q - 2 else lengths[(b * S_q + i) % len(lengths)]
+            routes[b, i, :n] = rng.choice(S_kv, size=n, replace=False)
+            routes[b, i] = routes[b, i, rng.permutation(K)]
+    q, k, v, _ = random_small_case(K + Hq, B, S_q, S_kv, Hq, Hkv, D, 1)
+    out, lse = qsa.qsa_forward_preprocessed(
+        bf16_to_gpu(q), bf16_to_gpu(k), bf16_to_gpu(v),
+        *qsa.qsa_preprocess(torch.from_numpy(routes).to(device()), S_kv)[:2], 0.0625, return_lse=True)
+    _, ocnt = oracle.route_lists(routes, S_kv)
+    assert int(ocnt.max()) == K and int(ocnt.min()) == 0
+    check_forward(gpu_bf16_bits(out), oracle.forward(q, k, v, routes, 0.0625), ocnt, v, "chunk boundaries")
+    check_lse(lse.cpu().numpy().astype(np.float64), oracle.lse(q, k, routes, 0.0625), "chunk boundaries lse")
 
 
 def test_single_route_returns_v_row_bitwise():

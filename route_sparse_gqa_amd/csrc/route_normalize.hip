@@ -29,7 +29,9 @@
 // each (lane j writes bit j's ID at its rank), so the IDs come out ascending
 // with no sort and no per-bit loop: O(K + kv_length / 32) work per row
 // instead of O(K log^2 K).  Rows with kv_length <= 16384 and K <= 1024 take
-// one wavefront each (route_wave_kernel), the others one workgroup.
+// one wavefront each (route_wave_kernel), the others one workgroup, whose
+// LDS is sized for kv_length <= 65536 and K <= 2048 when that suffices (16
+// KB, so more rows are in flight per CU) and for the limits above otherwise.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -184,6 +186,7 @@ __global__ void __launch_bounds__(64 * W * RowsPerBlock<W>::value)
 
 constexpr int kBitmapThreads = 256;
 constexpr int kBitmapWords = 4096;  // largest bitmap: kv_length <= 131072, K <= 4096
+constexpr int kBitmapWordsHalf = 2048;  // kv_length <= 65536, K <= 2048: half the LDS, more rows per CU
 
 // kWords bitmap words (kv_length <= 32 kWords) and kWords route slots (K <= kWords) per row.
 template <int kWords, typename RouteT>
@@ -393,6 +396,11 @@ hipError_t dispatch(const RouteT* routes, const int64_t* st, int64_t B, int64_t 
     else
       hipLaunchKernelGGL((route_wave_kernel<16, RouteT>), groups, wave_threads, 0, stream, routes, st[0], st[1],
                          st[2], S_q, n_rows, K, kv_length, list, count, zb, zn);
+    return hipGetLastError();
+  }
+  if (kv_length <= 32 * int64_t{kBitmapWordsHalf} && K <= kBitmapWordsHalf) {
+    hipLaunchKernelGGL((route_bitmap_kernel<kBitmapWordsHalf, RouteT>), rows, threads, 0, stream, routes, st[0],
+                       st[1], st[2], S_q, K, kv_length, list, count, zb, zn);
     return hipGetLastError();
   }
   if (kv_length <= 32 * int64_t{kBitmapWords} && K <= kBitmapWords) {

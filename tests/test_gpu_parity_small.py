@@ -84,10 +84,12 @@ def test_large_route_counts_and_segments():
 @pytest.mark.parametrize("S_kv,K,dtype", [(131072, 4096, np.int64), (131072, 4097, np.int64), (131073, 64, np.int32),
                                           (1 << 31, 300, np.int64), (64, 4096, np.int32), (16384, 512, np.int64),
                                           (16385, 512, np.int32), (16384, 513, np.int64), (16384, 1024, np.int32),
-                                          (16384, 1025, np.int64), (33, 1, np.int64)])
+                                          (16384, 1025, np.int64), (33, 1, np.int64), (65536, 2048, np.int64),
+                                          (65537, 2048, np.int32), (65536, 2049, np.int64), (16385, 1, np.int32)])
 def test_route_lists_at_the_bitmap_limits(S_kv, K, dtype):
     """Every normalisation path at its boundaries (one wavefront per row: kv <= 16384 and K <= 1024, with
-    8 or 16 slots per lane; one workgroup per row: kv <= 131072 and K <= 4096; else sorting)."""
+    8 or 16 slots per lane; one workgroup per row: kv <= 65536 and K <= 2048 with the half-size bitmap,
+    kv <= 131072 and K <= 4096 with the full one; else sorting)."""
     print(f"route lists kv={S_kv} K={K} {np.dtype(dtype).name}", flush=True)
     rng = np.random.Generator(np.random.PCG64(S_kv + K))
     B, S_q = 2, 5

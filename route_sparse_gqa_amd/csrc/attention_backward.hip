@@ -391,7 +391,7 @@ __global__ void __launch_bounds__(64 * kWaves)
   for (int32_t c0 = s_begin; c0 < s_end; c0 += kRecChunk) {
     n_rec = min(s_end - c0, static_cast<int32_t>(kRecChunk));
     __syncthreads();  // the previous chunk's records and slabs are no longer read
-    for (int x = tid; x < n_rec; x += kThreads) recs[x] = segs[c0 + x];
+    for (int e = tid; e < n_rec; e += kThreads) recs[e] = segs[c0 + e];
     __syncthreads();
     const int32_t n_batches = (n_rec + rows_per_batch - 1) / rows_per_batch;
     fetch(A, 0);
@@ -399,8 +399,8 @@ __global__ void __launch_bounds__(64 * kWaves)
     if (n_batches > 1) fetch(A, rows_per_batch);
     if (n_batches > 2) fetch(B, 2 * rows_per_batch);
     __syncthreads();
-    // X holds batch bi + 1 and Y batch bi + 2; the two stages swap roles every batch.
-    auto step = [&](int32_t bi, Stage& X, Stage& Y) {
+    // X holds batch bi + 1 (the other stage holds bi + 2); the two stages swap roles every batch.
+    auto step = [&](int32_t bi, Stage& X) {
       const int cur = bi & 1;
       compute(cur);
       if (bi + 1 < n_batches) stash(X, cur ^ 1);  // the other buffer was last read before the previous barrier
@@ -408,8 +408,8 @@ __global__ void __launch_bounds__(64 * kWaves)
       __syncthreads();
     };
     for (int32_t bi = 0; bi < n_batches; bi += 2) {  // workgroup-uniform
-      step(bi, A, B);
-      if (bi + 1 < n_batches) step(bi + 1, B, A);
+      step(bi, A);
+      if (bi + 1 < n_batches) step(bi + 1, B);
     }
   }
 

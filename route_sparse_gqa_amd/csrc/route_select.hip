@@ -184,12 +184,12 @@ __global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per
           part[r] = hg == 0 ? sum : part[r] + sum;
         }
       }
-      // Lane groups 0+2 and 1+3 combine rows 0 and 2 (x) and rows 1 and 3 (y); then groups 0+1
-      // and 2+3 finish them, leaving row g's sum in lane group g.
-      const u32x2 x = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
-      const u32x2 y = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
-      const float xs = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-      const float ys = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      // Lane groups 0+2 and 1+3 combine rows 0 and 2 (p02) and rows 1 and 3 (p13); then groups
+      // 0+1 and 2+3 finish them, leaving row g's sum in lane group g.
+      const u32x2 p02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+      const u32x2 p13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+      const float xs = __uint_as_float(p02[0]) + __uint_as_float(p02[1]);
+      const float ys = __uint_as_float(p13[0]) + __uint_as_float(p13[1]);
       const u32x2 z = __builtin_amdgcn_permlane16_swap(__float_as_uint(xs), __float_as_uint(ys), false, false);
       const float total = __uint_as_float(z[0]) + __uint_as_float(z[1]);  // >= +0.0: sums of relu terms
       const int64_t j = j0 + 16 * sc + m;

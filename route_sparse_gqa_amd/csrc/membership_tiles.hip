@@ -29,12 +29,13 @@ namespace qsa {
 namespace {
 
 constexpr int kTile = 128;
-constexpr int kSegCols = 65536;              // columns per workgroup segment
+constexpr int kSegCols = static_cast<int>(kMemSegCols);  // columns per workgroup segment
 constexpr int kSegTiles = kSegCols / kTile;  // 512 tiles per segment
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroupRows = kWaves;               // rows per workgroup: one per wavefront
 constexpr int kGroups = kTile / kGroupRows;      // workgroups per tile row and segment
+static_assert(kGroups == kMemGroups, "the host's grid-size check uses kMemGroups");
 constexpr int kTilesPerLane = kSegTiles / 64;  // 8
 
 constexpr int kBatch = 16;  // list entries per lane loaded together

@@ -148,7 +148,8 @@ QSA_EXPORT int qsa_preprocess(const void* routes, int routes_dtype, int64_t B, i
   if (membership != nullptr && !mul_ok(s.rows, ldm, &mem_bytes)) return QSA_ERR_LIMIT;
   if (!mul_ok(B * n_ti, n_tj, &tiles) || tiles > (INT64_MAX >> 3)) return QSA_ERR_LIMIT;
   if ((membership != nullptr || tile_class != nullptr) &&
-      (B * n_ti * ((ldm + 65535) / 65536) * 8 > kMaxGrid || (tiles + 255) / 256 > kMaxGrid))
+      (B * n_ti * ((ldm + qsa::kMemSegCols - 1) / qsa::kMemSegCols) * qsa::kMemGroups > kMaxGrid ||
+       (tiles + 255) / 256 > kMaxGrid))
     return QSA_ERR_LIMIT;
 
   const int64_t rshape[3] = {B, S_q, K};

@@ -15,7 +15,12 @@ hipError_t launch_route_normalize(const void* routes, bool routes_int64, int64_t
                                   int32_t* route_list, int32_t* route_count, int32_t* zero_buf,
                                   int64_t zero_count, hipStream_t stream);
 
-// Membership table and/or 128x128 tile classes from compacted lists.
+// Membership table and/or 128x128 tile classes from compacted lists: one
+// workgroup per (batch, 128-row tile row, segment of kMemSegCols columns,
+// group of 128 / kMemGroups rows), i.e. B * ceil(S_q/128) * ceil(ldm/kMemSegCols)
+// * kMemGroups workgroups.
+constexpr int64_t kMemSegCols = 65536;
+constexpr int64_t kMemGroups = 32;
 hipError_t launch_membership_tiles(const int32_t* route_list, const int32_t* route_count, int64_t B,
                                    int64_t S_q, int64_t K, int64_t kv_length, uint8_t* membership,
                                    int32_t* tile_class, hipStream_t stream);

@@ -92,6 +92,12 @@ def test_other_host_checks():
     assert L.qsa_preprocess(fake, 1, 1, 2, 3, s3, 0, fake, fake, None, None, None) == -3
     assert L.qsa_preprocess(fake, 9, 1, 2, 3, s3, 5, fake, fake, None, None, None) == -6
     assert L.qsa_preprocess(None, 1, 1, 2, 3, s3, 5, fake, fake, None, None, None) == -1
+    # membership grid: 2048 tile rows x 32768 segments (kv_length 2^31) x 32 row groups = 2^31 workgroups
+    S_q, kv = 2048 * 128, 1 << 31
+    s_rows = (ctypes.c_int64 * 3)(S_q, 1, 1)
+    low = [ctypes.c_void_p(n << 32) for n in (1, 2, 3)]  # routes, list, count; the table lies above them
+    assert L.qsa_preprocess(low[0], 1, 1, S_q, 1, s_rows, kv, low[1], low[2], ctypes.c_void_p(4 << 32), None,
+                            None) == -11
 
 
 def _bwd_ws(B, S_q, S_kv, Hq, Hkv, D, K):

@@ -6,7 +6,10 @@ slots, route dtype, scale, share of invalid slots and empty rows) so that
 combinations nobody picked are exercised too.  Every case checks the whole
 path against the fp64 oracle: preprocessing bit for bit (lists, counts,
 membership, tile classes), the forward and its log-sum-exp within their
-tolerances, and the three gradients within theirs.
+tolerances, and the three gradients within theirs.  A second sweep draws
+key ranges up to 140000 and up to 5000 route slots, across every
+route-normalisation path (one wavefront per row, the two bitmap sizes, the
+sort), and checks preprocessing alone, bit for bit.
 """
 
 from __future__ import annotations
@@ -74,3 +77,37 @@ def test_random_shape_whole_path(c):
     check_grad(gpu_bf16_bits(dq), rq, "dq", floor)
     check_grad(gpu_bf16_bits(dk), rk, "dk", floor)
     check_grad(gpu_bf16_bits(dv), rv, "dv")
+
+
+def _draw_preprocess_cases(n: int, seed: int = 20261203):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for _ in range(n):
+        kv = int(rng.choice([int(rng.integers(1, 16385)), int(rng.integers(16385, 65537)),
+                             int(rng.integers(65537, 140001))]))
+        K = int(rng.choice([int(rng.integers(1, 1025)), int(rng.integers(1025, 2049)), int(rng.integers(2049, 5001))]))
+        cases.append(dict(B=int(rng.integers(1, 3)), S_q=int(rng.integers(1, 6)), S_kv=kv, K=K,
+                          dtype=np.int32 if rng.random() < 0.5 else np.int64, seed=int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+PRE_CASES = _draw_preprocess_cases(16)
+
+
+@pytest.mark.parametrize("c", PRE_CASES, ids=lambda c: "B{B}_Sq{S_q}_Skv{S_kv}_K{K}".format(**c))
+def test_random_shape_preprocess(c):
+    print("random preprocess B{B} Sq{S_q} Skv{S_kv} K{K}".format(**c), flush=True)
+    rng = np.random.Generator(np.random.PCG64(c["seed"]))
+    B, S_q, S_kv, K = c["B"], c["S_q"], c["S_kv"], c["K"]
+    r = rng.integers(-5, S_kv + 5, size=(B, S_q, K), dtype=np.int64)
+    runs = rng.integers(0, S_kv, size=(B, S_q, 1)) + np.arange(K)[None, None, :] // 2  # runs of consecutive IDs
+    take = rng.random((B, S_q, K)) < 0.5
+    r = np.where(take, runs, r)
+    if c["dtype"] == np.int32:
+        r = r.astype(np.int32)
+    lst, cnt, mem, tc = qsa.qsa_preprocess(torch.from_numpy(r).to(device()), S_kv, membership=True, tile_class=True)
+    olst, ocnt = oracle.route_lists(r, S_kv)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), ocnt)
+    np.testing.assert_array_equal(lst.cpu().numpy(), olst)
+    np.testing.assert_array_equal(mem.cpu().numpy(), oracle.membership(r, S_kv))
+    np.testing.assert_array_equal(tc.cpu().numpy(), oracle.tile_class(r, S_kv))

@@ -7,7 +7,8 @@
 // [B, Q, Hkv, G, D]: query head h reads KV head h / G).
 //
 // Design (one wavefront per (b, i, hk) work unit, four rows of one KV head
-// per workgroup, mapped so that each XCD serves one KV head):
+// per workgroup, mapped so that each XCD serves one KV head, rows taken from
+// the last to the first):
 //  * The G query heads of the unit are the N = 16 columns of the MFMA (zero
 //    padded when G < 16).  Scores are computed transposed, S^T = K Q^T with
 //    v_mfma_f32_16x16x32_bf16, 16 routed keys as the M rows, so each lane
@@ -71,14 +72,16 @@ __global__ void __launch_bounds__(64 * kWaves)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));  // wave-uniform
-  // Workgroup x -> (KV head x % Hkv, rows 4 (x / Hkv) ..): workgroups are
+  // Workgroup x -> (KV head x % Hkv, four neighbouring rows): workgroups are
   // dealt round-robin to the 8 XCDs, so when Hkv divides 8 each XCD serves a
   // single KV head (half the K/V working set per L2 at Hkv = 2), while rows
-  // still spread evenly over the XCDs.
+  // still spread evenly over the XCDs.  Rows are taken from the last to the
+  // first: with causal routes later rows route more keys, so the longest
+  // rows start first and the short ones fill the end of the launch.
   const int64_t x = blockIdx.x;
   const int64_t hk = x % Hkv;
-  const int64_t row = (x / Hkv) * kWaves + wave;  // b * S_q + i
-  if (row >= n_units / Hkv) return;  // no workgroup barriers in this kernel
+  const int64_t row = n_units / Hkv - 1 - ((x / Hkv) * kWaves + wave);  // b * S_q + i
+  if (row < 0) return;  // the last workgroup's surplus waves; no workgroup barriers in this kernel
   const int64_t b = row / S_q;
   const int64_t i = row % S_q;
   const int c = lane & 15;  // head column of this lane; also key/dim row within a 16-tile

@@ -78,8 +78,9 @@ __global__ void __launch_bounds__(64 * kWaves)
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t x = blockIdx.x;
   const int64_t hk = x % Hkv;  // one KV head per XCD, as in the forward
-  const int64_t row = (x / Hkv) * kWaves + wave;
-  if (row >= n_rows) return;  // no workgroup barriers in this kernel
+  // Rows from the last to the first, as in the forward: with causal routes the longest start first.
+  const int64_t row = n_rows - 1 - ((x / Hkv) * kWaves + wave);
+  if (row < 0) return;  // the last workgroup's surplus waves; no workgroup barriers in this kernel
   const int64_t b = row / S_q;
   const int64_t i = row % S_q;
   const int c = lane & 15;  // head column (N side); key / dim row within a 16-tile

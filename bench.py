@@ -89,28 +89,36 @@ def parse_args():
 def calibrate_gather(reps: int = 5) -> None:
     """Ceiling of the attention kernels' gather: random 512-byte rows of a table laid out like a K or V
     tensor with two KV heads (1024-byte row stride), copied into LDS by the probe kernel with no
-    arithmetic, for tables whose rows fit the L2, the Infinity Cache, or neither."""
+    arithmetic, for tables whose rows fit the L2, the Infinity Cache, or neither; then, for an
+    L2-resident and a larger table, at lower occupancy (unused LDS per workgroup: five, two and one
+    wavefronts per SIMD)."""
     import torch
 
     from route_sparse_gqa_amd.build import PROBE_LIB_PATH
 
     L = ctypes.CDLL(PROBE_LIB_PATH)
     L.qsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
-                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
     L.qsa_probe_gather.restype = ctypes.c_int
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream(dev)
     n_waves, chunks, row_bytes, stride = 32768, 32, 512, 1024
     n_ids = n_waves * chunks * 16
     out = torch.empty(n_waves * 64, dtype=torch.int32, device=dev)
-    for rows in (4096, 8192, 16384, 32768, 65536, 262144, 1048576):
+    # (rows, path, unused LDS bytes per workgroup): the slabs take 32 KB per workgroup, so a pad of
+    # 48 KB leaves two workgroups (two wavefronts per SIMD) and 100 KB one
+    runs = [(rows, direct, 0) for rows in (4096, 8192, 16384, 32768, 65536, 262144, 1048576) for direct in (0, 1)]
+    runs += [(rows, 0, pad) for rows in (8192, 65536) for pad in (49152, 102400)]
+    occupancy = {0: 5, 49152: 2, 102400: 1}
+    for rows in sorted({r for r, _, _ in runs}):
         table = torch.ones(rows * stride, dtype=torch.uint8, device=dev)
         g = torch.Generator(device=dev)
         g.manual_seed(rows)
         ids = torch.randint(0, rows, (n_ids,), dtype=torch.int32, device=dev, generator=g)
-        for direct in (0, 1):  # through registers and LDS writes, or straight to LDS
+        for _, direct, pad in [x for x in runs if x[0] == rows]:
             args = (ctypes.c_void_p(table.data_ptr()), rows, stride, ctypes.c_void_p(ids.data_ptr()), n_waves,
-                    chunks, direct, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+                    chunks, direct, pad, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
             if L.qsa_probe_gather(*args) != 0:
                 raise RuntimeError("qsa_probe_gather failed")
             torch.cuda.synchronize()
@@ -125,6 +133,7 @@ def calibrate_gather(reps: int = 5) -> None:
             print(json.dumps({"calibration": "row gather", "path": "direct to LDS" if direct else "registers",
                               "rows": rows, "row_bytes": row_bytes, "row_stride_bytes": stride,
                               "distinct_row_mib": rows * row_bytes / 2 ** 20, "gathered_bytes": n_ids * row_bytes,
+                              "lds_pad_bytes": pad, "wavefronts_per_simd": occupancy[pad],
                               "ms_median": ms, "tb_per_s": n_ids * row_bytes / (ms * 1e-3) / 1e12}), flush=True)
         del table, ids
 

@@ -7,7 +7,10 @@
 // 16-byte LDS writes), and does no arithmetic, so the time measures what the
 // chip can deliver for that access pattern.  With a table that fits the L2,
 // the Infinity Cache or neither, it gives the gather ceiling that bounds the
-// attention kernels at each working-set size.
+// attention kernels at each working-set size.  Unused dynamic LDS per
+// workgroup (lds_pad) lowers the number of workgroups a CU holds, to measure
+// the ceiling at the attention kernels' occupancy (two wavefronts per SIMD at
+// D = 256).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -68,23 +71,24 @@ __global__ void __launch_bounds__(64 * kWaves)
 
 // table: n_rows rows of >= 512 bytes, `stride` bytes apart (16-byte aligned); ids: n_waves * chunks * 16
 // row indices (clamped into [0, n_rows)); out: n_waves * 64 words; direct: 0 through registers, 1
-// straight to LDS.  Returns 0, -1 for a bad argument, -12 for a launch error.
+// straight to LDS; lds_pad: unused dynamic LDS bytes per workgroup, 0 .. 131072 (the 32 KB of slabs
+// plus the pad stay within a CU's 160 KB).  Returns 0, -1 for a bad argument, -12 for a launch error.
 extern "C" __attribute__((visibility("default"))) int qsa_probe_gather(const void* table, int64_t n_rows,
                                                                        int64_t stride, const int32_t* ids,
                                                                        int64_t n_waves, int chunks, int direct,
-                                                                       uint32_t* out, void* stream) {
+                                                                       int lds_pad, uint32_t* out, void* stream) {
   if (table == nullptr || ids == nullptr || out == nullptr || n_rows < 1 || stride < kRowBytes || stride % 16 != 0 ||
       n_waves < 1 || chunks < 1 || (direct != 0 && direct != 1) || (reinterpret_cast<uintptr_t>(table) & 15) != 0 ||
-      (n_waves + kWaves - 1) / kWaves > (int64_t{1} << 31) - 1)
+      lds_pad < 0 || lds_pad > 131072 || (n_waves + kWaves - 1) / kWaves > (int64_t{1} << 31) - 1)
     return -1;
   const dim3 grid(static_cast<uint32_t>((n_waves + kWaves - 1) / kWaves));
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint8_t* t = static_cast<const uint8_t*>(table);
   if (direct)
-    hipLaunchKernelGGL(probe_gather_kernel<true>, grid, dim3(64 * kWaves), 0, st, t, n_rows, stride, ids, n_waves,
+    hipLaunchKernelGGL(probe_gather_kernel<true>, grid, dim3(64 * kWaves), static_cast<size_t>(lds_pad), st, t, n_rows, stride, ids, n_waves,
                        chunks, out);
   else
-    hipLaunchKernelGGL(probe_gather_kernel<false>, grid, dim3(64 * kWaves), 0, st, t, n_rows, stride, ids, n_waves,
+    hipLaunchKernelGGL(probe_gather_kernel<false>, grid, dim3(64 * kWaves), static_cast<size_t>(lds_pad), st, t, n_rows, stride, ids, n_waves,
                        chunks, out);
   return hipGetLastError() == hipSuccess ? 0 : -12;
 }

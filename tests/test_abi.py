@@ -211,11 +211,13 @@ def test_probe_library_loads_and_checks_its_arguments():
 
     P = ctypes.CDLL(PROBE_LIB_PATH)
     P.qsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
-                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     P.qsa_probe_gather.restype = ctypes.c_int
     t, i, o = (ctypes.c_void_p(n << 32) for n in range(1, 4))  # distinct, never dereferenced
-    assert P.qsa_probe_gather(None, 16, 1024, i, 64, 1, 0, o, None) == -1
-    assert P.qsa_probe_gather(t, 0, 1024, i, 64, 1, 0, o, None) == -1         # no rows
-    assert P.qsa_probe_gather(t, 16, 256, i, 64, 1, 0, o, None) == -1         # stride below one row
-    assert P.qsa_probe_gather(t, 16, 1024, i, 64, 1, 2, o, None) == -1        # unknown path
-    assert P.qsa_probe_gather(ctypes.c_void_p((1 << 32) + 8), 16, 1024, i, 64, 1, 0, o, None) == -1  # misaligned
+    assert P.qsa_probe_gather(None, 16, 1024, i, 64, 1, 0, 0, o, None) == -1
+    assert P.qsa_probe_gather(t, 0, 1024, i, 64, 1, 0, 0, o, None) == -1         # no rows
+    assert P.qsa_probe_gather(t, 16, 256, i, 64, 1, 0, 0, o, None) == -1         # stride below one row
+    assert P.qsa_probe_gather(t, 16, 1024, i, 64, 1, 2, 0, o, None) == -1        # unknown path
+    assert P.qsa_probe_gather(t, 16, 1024, i, 64, 1, 0, -1, o, None) == -1       # negative LDS pad
+    assert P.qsa_probe_gather(t, 16, 1024, i, 64, 1, 0, 131073, o, None) == -1   # LDS pad past the CU
+    assert P.qsa_probe_gather(ctypes.c_void_p((1 << 32) + 8), 16, 1024, i, 64, 1, 0, 0, o, None) == -1  # misaligned

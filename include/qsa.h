@@ -8,9 +8,10 @@
  *   - flex_qsa page, module description: padded batches, packed THD rows and
  *     context parallelism all reduce to "each query row attends to its route
  *     IDs"; rows without a valid route give exactly zero output.
- *   - fa4_qsa page, `_preprocess` and `fa4_sparse_gqa_attention`: duplicate
- *     IDs select a token once; invalid IDs, including huge int64 values, are
- *     discarded; no causal or other mask is added beyond the routes.
+ *   - fa4_qsa page, `_preprocess` and `fa4_sparse_gqa_attention`: a
+ *     repeated ID selects its token once; an ID outside [0, kv_length),
+ *     however large, is ignored; no causal or other mask is added beyond
+ *     the routes.
  *   - qsa page, `_gathered_qsa_gqa_attention_chunk`: grouped query layout
  *     [B, Q, Hkv, G, D], i.e. query head h reads KV head h / G, G = Hq / Hkv.
  *

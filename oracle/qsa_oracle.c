@@ -14,7 +14,7 @@
  *    parameters; qsa page, `qsa_gqa_attention` parameters): every slot value
  *    x is widened to int64; x is a valid key iff 0 <= x < kv_length (negative
  *    IDs, -1 padding and out-of-range values, including huge int64 values,
- *    are ignored); duplicates collapse to one.  R(b,i) is that set in
+ *    are ignored); a repeated ID counts once.  R(b,i) is that set in
  *    ascending order.
  *  - Membership table (fa4_qsa page, `_preprocess` return value): uint8
  *    [B, S_q, ldm], 1 iff column c is in R(b,i); columns past kv_length are

@@ -2,10 +2,11 @@
 // (0 <= id < kv_length, int32 inputs sign-extended), sort them ascending,
 // drop duplicates and compact them into an int32 list padded with -1.
 //
-// Definition: fa4_qsa page, `_preprocess` (duplicates collapse; invalid IDs,
-// including large int64 values, are discarded before indexing); flex_qsa
-// page, `_routes_to_membership` (negative or out-of-range entries are
-// padding); qsa page, `QSARouteSelection` (int32 IDs, -1 marks padding).
+// Definition: fa4_qsa page, `_preprocess`, routes parameter (a repeated ID
+// counts once; an ID outside [0, kv_length), however large, is dropped
+// before any address is formed); flex_qsa page, `_routes_to_membership`
+// (negative or out-of-range entries stand for padding); qsa page,
+// `QSARouteSelection` (int32 IDs, -1 marks padding).
 //
 // Design: one row is sorted by T = 64*W threads holding E keys each in
 // registers (P = T*E >= K positions; position of register e of thread t is
@@ -20,7 +21,7 @@
 //
 // When the key range is small (kv_length <= 32 * kBitmapWords = 131072) and
 // K <= kBitmapWords, a row is instead marked in an LDS bitmap of
-// kv_length bits (integer atomic OR, so duplicates collapse by
+// kv_length bits (integer atomic OR, so a repeated ID counts once by
 // construction; the slots pass through LDS so that each lane takes a run of
 // consecutive slots and merges the IDs that share a bitmap word in
 // registers, one atomic per run).  One workgroup prefix sum over contiguous

@@ -23,7 +23,7 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def brute_route_set(row, kv_length: int) -> list[int]:
-    """Valid IDs are 0 <= x < kv_length; duplicates collapse; ascending."""
+    """Valid IDs are 0 <= x < kv_length; a repeated ID counts once; ascending."""
     return sorted({int(x) for x in row if 0 <= int(x) < kv_length})
 
 

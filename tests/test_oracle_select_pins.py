@@ -8,12 +8,16 @@ What fixes the selection independently of the oracle's C code:
 * a numpy brute force: dense float64 scores from ``einsum`` and a
   lexicographic sort (score descending, block ascending);
 * torch.topk (float64, CPU) on tie-free random scores: the same kept set;
+* the oracle's score table (``block_scores``, the yardstick of the GPU
+  selection test on continuous inputs) element by element against torch
+  float64 scores, relu(q k^T) summed over heads over sqrt(D), on row ranges
+  that start and end inside the query length of several batch rows;
 * invariants: rows that see at most token_budget/c blocks keep all of them
   whatever the values; head permutation and positive scaling of the queries
   change nothing; a query slice with its global offset equals the same rows
   of the full call; padding rows are all -1; every ID is causal and distinct.
 
-Eight planted mistakes, each compiled into a copy of the oracle, must each
+Eleven planted mistakes, each compiled into a copy of the oracle, must each
 fail at least one of these pins.
 """
 
@@ -120,6 +124,19 @@ def check_torch_topk(orc):
             assert (got[b, i, m * c:budget] == -1).all()
 
 
+def check_block_scores(orc):
+    """Every (batch, row, block) score of a row range against torch float64 scores of the same bf16 values."""
+    B, S_q, H, D, n_blocks = 3, 37, 5, 24, 11
+    iq, ck = random_select_case(31, B, S_q, H, D, n_blocks)
+    q = torch.from_numpy((iq.astype(np.uint32) << 16).view(np.float32).astype(np.float64))  # [B,S_q,H,D]
+    k = torch.from_numpy((ck[:, :, 0].astype(np.uint32) << 16).view(np.float32).astype(np.float64))  # [B,n,D]
+    want = torch.relu(torch.matmul(q, k.transpose(1, 2).unsqueeze(1).contiguous())).sum(dim=2) / np.sqrt(D)
+    for r0, r1 in ((0, S_q), (0, 1), (5, 19), (36, 37)):
+        got = orc.block_scores(iq, ck, rows=(r0, r1))
+        assert got.shape == (B, r1 - r0, n_blocks), got.shape
+        np.testing.assert_allclose(got, want[:, r0:r1].numpy(), rtol=1e-12, atol=1e-12, err_msg=f"rows {r0}..{r1}")
+
+
 def check_invariants(orc):
     B, S_q, H, D, c, budget = 2, 80, 4, 16, 4, 20
     kb = budget // c
@@ -155,7 +172,7 @@ def check_invariants(orc):
             assert (row[budget:] >= 0).sum() == (i + 1) % c
 
 
-CHECKS = (check_golden, check_brute_force, check_torch_topk, check_invariants)
+CHECKS = (check_golden, check_brute_force, check_torch_topk, check_block_scores, check_invariants)
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
@@ -174,6 +191,16 @@ MUTANTS = {
     "tail stops before the query": ("for (int64_t u = 0; nv * c + u <= t; ++u)", "for (int64_t u = 0; nv * c + u < t; ++u)"),
     "worst blocks kept": ("if (x->score != y->score) return x->score > y->score ? -1 : 1;",
                           "if (x->score != y->score) return x->score < y->score ? -1 : 1;"),
+    # the score table alone (not used by the selection itself)
+    "score table reads rows from the range start": (
+        "block_score(iq + (b * S_q + i) * H * D, ck + (b * n_blocks + j) * D, H, D);\n}",
+        "block_score(iq + (b * S_q + (i - row_begin)) * H * D, ck + (b * n_blocks + j) * D, H, D);\n}"),
+    "score table takes the first batch row's keys": (
+        "block_score(iq + (b * S_q + i) * H * D, ck + (b * n_blocks + j) * D, H, D);\n}",
+        "block_score(iq + (b * S_q + i) * H * D, ck + j * D, H, D);\n}"),
+    "score table blocks transposed with rows": (
+        "scores[(b * n_rows + (i - row_begin)) * n_blocks + j] =",
+        "scores[(b * n_blocks + j) * n_rows + (i - row_begin)] ="),
 }
 
 

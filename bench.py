@@ -4,19 +4,34 @@ One step = one pass of the whole path over one batch of synthetic input
 already resident in HBM:
   1. qsa_preprocess: route normalisation (lists + counts), membership table
      and 128x128 tile classes;
-  2. qsa_forward_preprocessed: the fused gather-attention kernel.
+  2. qsa_forward_preprocessed: the gather-attention kernel(s).
+A 1 GiB scratch write between steps evicts the L2 and the Infinity Cache
+(--flush-mib); the step time excludes it (HIP events per step).
 
-Prints ONE JSON line (rank 0):
+The default workload is long_int64 (B=1, S=65536, K=2048), the largest
+configuration that fits one GPU and the one past the int32 flat-index limit.
+
+Prints ONE JSON line:
   value        routed-attention TFLOP/s of the whole step, F = 4*D*Hq*N flops
-               with N = total distinct valid routes;
-  roofline     the gather-attention kernel against the 8 TB/s HBM roofline:
-               algorithmic bytes per launch (routed K and V rows once per
-               (query row, KV head), Q, O, lists and counts) over its average
-               launch time, measured with HIP events on the launch stream
-               (also its median and minimum, and the compulsory bytes: Q, O,
-               lists, counts and each distinct routed K/V row once, with the
-               time floor they and the flops set at 8 TB/s and 2.5 PFLOP/s);
-  cpu_baseline the fp64 CPU oracle on a bounded sample of the same rows.
+               with N = total distinct valid routes (16384 flop per routed
+               (row, route) pair at D = 256, Hq = 16);
+  roofline     the attention against its roofline on this chip.  The
+               compulsory work sets the floor t_floor = max(B_min / 8 TB/s,
+               F / 2.5 PFLOP/s), B_min = Q read, O written, lists, counts and
+               each distinct routed K/V row once per KV head; for the
+               D = 256 workloads the flops set it, so `bound` is "mfma",
+               `achieved` = F / t_attention and `frac` = achieved / 2.5 PFLOP/s
+               (= t_floor / t).  Beside it: the gather rate (each routed K and
+               V row once per (query row, KV head), plus Q, O, lists: bytes
+               the L2, the Infinity Cache and HBM serve together, not an HBM
+               figure) and, when profiles/traffic.json holds rocprofv3
+               FETCH_SIZE/WRITE_SIZE for the current kernel sources, the
+               physical HBM-side bytes per launch (`traffic`) and their rate;
+  kernels_ms   preprocess, attention, and the fused qsa_forward (route
+               normalisation + attention in one call) timed separately;
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same rows:
+               windows of contiguous rows spread evenly over the sequence,
+               so the sample's mix of row lengths is the workload's.
 
 With ``--pass backward`` it times the backward instead (one step = one
 qsa_backward call: the dq kernel, the key-segment construction and the dk/dv
@@ -32,6 +47,10 @@ block scores, per-row top-k, expansion) on a selection workload (default
 sel_long), reporting scoring TFLOP/s with F = 2*H*D*sum(nv) over the rows
 that see more than token_budget/c blocks (the only rows whose blocks are
 scored), against the bf16 matrix-core peak.
+
+``--counter-reference-mib M`` only runs plain device-to-device copies of M
+MiB: the FETCH_SIZE / WRITE_SIZE counters of that copy, whose bytes are
+known, scale the same counters read on the attention kernels.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--pass forward|backward|tile_lists|select]
@@ -56,7 +75,7 @@ if ROOT not in sys.path:
 METRIC = "routed-attention TFLOP/s + achieved HBM GB/s (fwd, BF16, D=256) on 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-DEFAULT_WORKLOAD = "right_padded"
+DEFAULT_WORKLOAD = "long_int64"
 DEFAULT_SELECT_WORKLOAD = "sel_long"
 
 
@@ -70,99 +89,19 @@ def parse_args():
                     default="forward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--flush-mib", type=int, default=0,
+    ap.add_argument("--flush-mib", type=int, default=1024,
                     help="write this many MiB of scratch between timed steps (evicts L2 and the Infinity Cache); "
-                         "the step time then comes from per-step events, without the flush")
+                         "the step time comes from per-step events, without the flush")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="JSON with rocprofv3-derived HBM bytes per launch of the attention kernel")
-    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="only run plain device-to-device copies of this many MiB (counter calibration)")
+                    help="JSON with rocprofv3-derived HBM bytes per attention call, per workload")
+    ap.add_argument("--counter-reference-mib", type=int, default=0,
+                    help="only run plain device-to-device copies of this many MiB (counter scale reference)")
     ap.add_argument("--graph", action="store_true",
                     help="also capture one step (preprocess + attention) in a HIP graph and time its replays")
-    ap.add_argument("--calibrate-gather", action="store_true",
-                    help="only measure the row-gather ceiling (libqsa_probe.so) for several table sizes")
-    ap.add_argument("--calibrate-matmul", type=int, default=0,
-                    help="only run bf16 n x n x n library matmuls (MFMA busy-counter calibration)")
     return ap.parse_args()
 
 
-def calibrate_gather(reps: int = 5) -> None:
-    """Ceiling of the attention kernels' gather: random 512-byte rows of a table laid out like a K or V
-    tensor with two KV heads (1024-byte row stride), copied into LDS by the probe kernel with no
-    arithmetic, for tables whose rows fit the L2, the Infinity Cache, or neither; then, for an
-    L2-resident and a larger table, at lower occupancy (unused LDS per workgroup: five, two and one
-    wavefronts per SIMD)."""
-    import torch
-
-    from route_sparse_gqa_amd.build import PROBE_LIB_PATH
-
-    L = ctypes.CDLL(PROBE_LIB_PATH)
-    L.qsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
-                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                   ctypes.c_void_p]
-    L.qsa_probe_gather.restype = ctypes.c_int
-    dev = torch.device("cuda", 0)
-    stream = torch.cuda.current_stream(dev)
-    n_waves, chunks, row_bytes, stride = 32768, 32, 512, 1024
-    n_ids = n_waves * chunks * 16
-    out = torch.empty(n_waves * 64, dtype=torch.int32, device=dev)
-    # (rows, path, unused LDS bytes per workgroup): the slabs take 32 KB per workgroup, so a pad of
-    # 48 KB leaves two workgroups (two wavefronts per SIMD) and 100 KB one
-    runs = [(rows, direct, 0) for rows in (4096, 8192, 16384, 32768, 65536, 262144, 1048576) for direct in (0, 1)]
-    runs += [(rows, 0, pad) for rows in (8192, 65536) for pad in (49152, 102400)]
-    occupancy = {0: 5, 49152: 2, 102400: 1}
-    for rows in sorted({r for r, _, _ in runs}):
-        table = torch.ones(rows * stride, dtype=torch.uint8, device=dev)
-        g = torch.Generator(device=dev)
-        g.manual_seed(rows)
-        ids = torch.randint(0, rows, (n_ids,), dtype=torch.int32, device=dev, generator=g)
-        for _, direct, pad in [x for x in runs if x[0] == rows]:
-            args = (ctypes.c_void_p(table.data_ptr()), rows, stride, ctypes.c_void_p(ids.data_ptr()), n_waves,
-                    chunks, direct, pad, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
-            if L.qsa_probe_gather(*args) != 0:
-                raise RuntimeError("qsa_probe_gather failed")
-            torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(reps)]
-            for e0, e1 in ev:
-                e0.record(stream)
-                L.qsa_probe_gather(*args)
-                e1.record(stream)
-            torch.cuda.synchronize()
-            ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
-            print(json.dumps({"calibration": "row gather", "path": "direct to LDS" if direct else "registers",
-                              "rows": rows, "row_bytes": row_bytes, "row_stride_bytes": stride,
-                              "distinct_row_mib": rows * row_bytes / 2 ** 20, "gathered_bytes": n_ids * row_bytes,
-                              "lds_pad_bytes": pad, "wavefronts_per_simd": occupancy[pad],
-                              "ms_median": ms, "tb_per_s": n_ids * row_bytes / (ms * 1e-3) / 1e12}), flush=True)
-        del table, ids
-
-
-def calibrate_matmul(n: int, reps: int = 10) -> None:
-    """Library bf16 matmuls of a known flop count timed with events: the MFMA busy cycles per dispatch
-    at a measured fraction of the bf16 peak give the scale for reading the counter on other kernels."""
-    import torch
-
-    dev = torch.device("cuda", 0)
-    g = torch.Generator(device=dev).manual_seed(0)
-    a = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
-    b = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16).contiguous()
-    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
-        torch.matmul(a, b, out=c)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in ev:
-        e0.record()
-        torch.matmul(a, b, out=c)
-        e1.record()
-    torch.cuda.synchronize()
-    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
-    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-    print(json.dumps({"calibration": "bf16 matmul", "n": n, "ms_median": ms, "tflops": tflops,
-                      "frac_of_peak": tflops / MFMA_BF16_PEAK_TFLOPS}), flush=True)
-
-
-def calibrate_copy(mib: int, reps: int = 5) -> None:
+def counter_reference_copy(mib: int, reps: int = 5) -> None:
     """Plain copies of a known size: FETCH_SIZE / WRITE_SIZE per dispatch of this kernel
     give the scale factor between the counters and bytes actually moved."""
     import torch
@@ -208,12 +147,20 @@ class Plan:
         self.fwd_args = (i8(self.q), st(self.q), i8(self.k), st(self.k), i8(self.v), st(self.v), i8(self.lst),
                          i8(self.cnt), B, S_q, w.S_kv, w.Hq, w.Hkv, w.D, K, ctypes.c_float(w.scale),
                          i8(self.out), None, self.stream)
+        fused_ws = qsa.qsa_forward_workspace_size(B, S_q, K)
+        self.fused_ws = torch.empty(fused_ws, dtype=torch.uint8, device=dev)
+        self.fused_out = torch.empty_like(self.out)
+        self.fused_args = (i8(self.q), st(self.q), i8(self.k), st(self.k), i8(self.v), st(self.v), i8(self.routes),
+                           1 if routes.dtype == np.int64 else 0, st(self.routes), B, S_q, w.S_kv, w.Hq, w.Hkv, w.D,
+                           K, ctypes.c_float(w.scale), i8(self.fused_out), i8(self.fused_ws),
+                           ctypes.c_size_t(fused_ws), self.stream)
 
     def set_stream(self, stream: ctypes.c_void_p) -> None:
         """Point the pre-marshalled calls at another HIP stream (the stream is their last argument)."""
         self.stream = stream
         self.pre_args = self.pre_args[:-1] + (stream,)
         self.fwd_args = self.fwd_args[:-1] + (stream,)
+        self.fused_args = self.fused_args[:-1] + (stream,)
 
     def setup_backward(self, dev):
         """Forward with log-sum-exp once, then pre-marshal qsa_backward (dout drawn from its own stream)."""
@@ -267,6 +214,14 @@ class Plan:
         rc = self.L.qsa_forward_preprocessed(*self.fwd_args)
         if rc != 0:
             raise RuntimeError(f"qsa_forward_preprocessed failed with status {rc}")
+
+    def fused(self):
+        rc = self.L.qsa_forward(*self.fused_args)
+        if rc != 0:
+            raise RuntimeError(f"qsa_forward failed with status {rc}")
+
+    def kernel_name(self) -> str:
+        return "gather_attention_kernel"
 
 
 def algorithmic_counts(w, N: int):
@@ -329,48 +284,65 @@ def backward_counts(w, N: int, segments: int):
     return flops, b_dq + b_seg + b_kv
 
 
-def cpu_baseline(w, q, k, v, routes, counts, target_s: float):
-    """Time the fp64 oracle on contiguous query rows taken from the middle of the workload."""
+def cpu_info() -> dict:
+    """CPU model (/proc/cpuinfo) and the number of cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(w, q, k, v, routes, counts, target_s: float, windows: int = 16):
+    """Time the fp64 oracle on `windows` windows of contiguous query rows centred at evenly spaced
+    positions of the sequence (every batch row), so that the sample mixes short and long causal rows
+    as the whole workload does.  The window length grows until the sample takes about target_s."""
     import oracle
 
     S_q = w.S_q
-    per_row_routes = counts.sum(axis=0)  # summed over the batch
-    start = 0
+    per_row = counts.sum(axis=0)  # routed pairs per query position, summed over the batch
+    threads = oracle.num_threads()
+    n_win = min(windows, S_q)
+    max_m = S_q // n_win
 
-    def run(nrows):
-        r0, r1 = start, min(S_q, start + nrows)
+    def run(m):
+        m = max(1, min(m, max_m))
+        starts = [min(max(0, int((j + 0.5) * S_q / n_win) - m // 2), S_q - m) for j in range(n_win)]
         t0 = time.perf_counter()
-        oracle.forward(q, k, v, routes, w.scale, rows=(r0, r1))
+        for s0 in starts:
+            oracle.forward(q, k, v, routes, w.scale, rows=(s0, s0 + m))
         dt = time.perf_counter() - t0
-        return dt, int(per_row_routes[r0:r1].sum()), r1 - r0
+        return dt, sum(int(per_row[s0:s0 + m].sum()) for s0 in starts), m, starts
 
-    dt, n_routes, nrows = run(4)
-    while dt < 0.5 and nrows < S_q - start:
-        dt, n_routes, nrows = run(min(S_q - start, nrows * 4))
-    if dt < target_s and nrows < S_q - start:
-        want = int(nrows * target_s / max(dt, 1e-3))
-        dt, n_routes, nrows = run(min(S_q - start, max(nrows, want)))
+    dt, n_routes, m, starts = run(max(1, threads // w.B))  # at least one row per thread in each window
+    while dt < 0.5 and m < max_m:
+        dt, n_routes, m, starts = run(m * 4)
+    if dt < target_s and m < max_m:
+        dt, n_routes, m, starts = run(int(m * target_s / max(dt, 1e-3)))
+    rows = w.B * m * n_win
     tflops = 4 * w.D * w.Hq * n_routes / dt / 1e12
     return {
         "value": tflops,
         "unit": "TFLOP/s",
-        "cores": oracle.num_threads(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"fp64 oracle forward on query rows [{start}, {start + nrows}) of every batch row "
-                  f"({n_routes} routed pairs, {dt:.2f} s)",
+        "sample": f"fp64 oracle forward on {n_win} windows of {m} query rows (of every batch row) centred at "
+                  f"evenly spaced positions, first rows {starts[0]}..{starts[-1]}: {rows} rows, {n_routes} "
+                  f"routed pairs (workload average {counts.sum() / counts.size:.1f} per row, sample "
+                  f"{n_routes / rows:.1f}), {dt:.2f} s on {threads} OpenMP threads",
+        **cpu_info(),
     }
 
 
 def main():
     args = parse_args()
-    if args.calibrate_copy_mib:
-        calibrate_copy(args.calibrate_copy_mib)
-        return
-    if args.calibrate_matmul:
-        calibrate_matmul(args.calibrate_matmul)
-        return
-    if args.calibrate_gather:
-        calibrate_gather()
+    if args.counter_reference_mib:
+        counter_reference_copy(args.counter_reference_mib)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -395,7 +367,7 @@ def main():
     torch.cuda.synchronize()
     counts = plan.cnt.cpu().numpy()
     N = int(counts.sum())
-    flops, alg_bytes = algorithmic_counts(w, N)
+    flops, gather_bytes = algorithmic_counts(w, N)
     min_bytes = compulsory_bytes(w, plan, N)
 
     if args.which == "backward":
@@ -409,14 +381,18 @@ def main():
     for _ in range(args.warmup):
         plan.preprocess()
         plan.attention()
+        plan.fused()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    pre_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    att_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    total0, total1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    pre_ev = [ev() for _ in range(args.steps)]
+    att_ev = [ev() for _ in range(args.steps)]
+    fused_ev = [ev() for _ in range(args.steps)]
+    total0, total1 = ev()
     scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib > 0 else None
     torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     total0.record(stream)
     for s in range(args.steps):
         if scratch is not None:
@@ -429,26 +405,29 @@ def main():
         att_ev[s][1].record(stream)
     total1.record(stream)
     torch.cuda.synchronize()
+    # the fused entry point (route normalisation + attention in one call), same protocol
+    for s in range(args.steps):
+        if scratch is not None:
+            scratch.fill_((s + 1) & 0xFF)
+        fused_ev[s][0].record(stream)
+        plan.fused()
+        fused_ev[s][1].record(stream)
+    torch.cuda.synchronize()
 
     att_ms = sorted(a.elapsed_time(b) for a, b in att_ev)
     ms_att = sum(att_ms) / args.steps
     ms_pre = sum(a.elapsed_time(b) for a, b in pre_ev) / args.steps
+    fused_ms = sorted(a.elapsed_time(b) for a, b in fused_ev)
     if scratch is None:
         ms_step = total0.elapsed_time(total1) / args.steps
     else:  # flushes excluded: each step from its preprocess start to its attention end
         ms_step = sum(p[0].elapsed_time(a[1]) for p, a in zip(pre_ev, att_ev)) / args.steps
-    achieved = alg_bytes / (ms_att * 1e-3) / 1e9
 
     graph = None
     if args.graph:
         graph = time_graph_replays(plan, dev, args.steps, args.warmup, flops)
 
-    traffic = None
-    if os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            t = json.load(f)
-        if t.get("workload") == w.name and t.get("kernel_source_sha") == _kernel_sha():
-            traffic = t.get("bytes_per_launch")
+    traffic = read_traffic(args.traffic, w.name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -473,26 +452,59 @@ def main():
             "K": w.K, "q_offset": w.q_offset, "routes_N": N, "route_dtype": str(routes.dtype),
             "cache_flush_mib": args.flush_mib,
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "kernel": "gather_attention",
-            "ms_per_launch": ms_att,
-            "ms_per_launch_median": att_ms[len(att_ms) // 2],
-            "ms_per_launch_min": att_ms[0],
-            "alg_bytes_per_launch": alg_bytes,
-            "compulsory_bytes": min_bytes,
-            "t_floor_ms": max(min_bytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3,
-        },
-        "kernels_ms": {"preprocess(route_normalize+membership_tiles)": ms_pre, "gather_attention": ms_att},
+        "roofline": attention_roofline(w, N, flops, gather_bytes, min_bytes, att_ms, traffic, plan.kernel_name()),
+        "kernels_ms": {"preprocess(route_normalize+membership_tiles)": ms_pre, "attention": ms_att,
+                       "qsa_forward(route_normalize+attention)": sum(fused_ms) / args.steps,
+                       "qsa_forward_median": fused_ms[len(fused_ms) // 2], "qsa_forward_min": fused_ms[0]},
         "graph": graph,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def attention_roofline(w, N, flops, gather_bytes, min_bytes, att_ms, traffic, kernel):
+    """The attention call against the chip's roofline (see the module docstring)."""
+    ms = sum(att_ms) / len(att_ms)
+    t = ms * 1e-3
+    t_flops = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_bytes = min_bytes / (HBM_PEAK_GBS * 1e9)
+    if t_flops >= t_bytes:
+        bound, achieved, peak, unit = "mfma", flops / t / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", min_bytes / t / 1e9, HBM_PEAK_GBS, "GB/s"
+    return {
+        "bound": bound,
+        "achieved": achieved,
+        "peak": peak,
+        "unit": unit,
+        "frac": achieved / peak,
+        "traffic": traffic,
+        "kernel": kernel,
+        "ms_per_launch": ms,
+        "ms_per_launch_median": att_ms[len(att_ms) // 2],
+        "ms_per_launch_min": att_ms[0],
+        "flops_per_launch": flops,
+        "flops_per_routed_pair": 4 * w.D * w.Hq,
+        "routed_pairs": N,
+        "compulsory_bytes": min_bytes,
+        "t_floor_ms": max(t_flops, t_bytes) * 1e3,
+        "gather_bytes_per_launch": gather_bytes,
+        "gather_rate_GBs": gather_bytes / t / 1e9,
+        "hbm_traffic_GBs": traffic / t / 1e9 if traffic else None,
+    }
+
+
+def read_traffic(path: str, workload: str):
+    """HBM-side bytes per attention call from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each scaled by the
+    same counter on a copy of known size), when they were taken on the current kernel sources."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != _kernel_sha():
+        return None
+    entry = t.get("workloads", {}).get(workload)
+    return entry.get("bytes_per_call") if entry else None
 
 
 def run_backward(args, w, plan, dev, N):
@@ -514,10 +526,10 @@ def run_backward(args, w, plan, dev, N):
         ev[s][1].record(stream)
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
-    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
     result = {
         "metric": "routed-attention backward TFLOP/s (dq, dk, dv; BF16) on 1 MI355X",
-        "value": flops / (ms * 1e-3) / 1e12,
+        "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -533,15 +545,17 @@ def run_backward(args, w, plan, dev, N):
             "K": w.K, "routes_N": N, "key_segments": segments,
         },
         "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
+            # the compulsory floor is set by the flops, as for the forward (B_min is a few GB at most)
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
             "traffic": None,
             "kernel": "qsa_backward (dq_kernel + key segments + dkdv_kernel)",
             "ms_per_launch": ms,
-            "alg_bytes_per_launch": alg_bytes,
+            "gather_bytes_per_launch": alg_bytes,
+            "gather_rate_GBs": alg_bytes / (ms * 1e-3) / 1e9,
         },
         "cpu_baseline": None,
     }
@@ -713,12 +727,17 @@ def run_select(args):
     }), flush=True)
 
 
+ATTENTION_SOURCES = ("gather_attention.hip", "device_common.h")
+
+
 def _kernel_sha() -> str:
+    """sha256[:16] over the sources of the attention kernels (the counters are valid for this code only)."""
     import hashlib
 
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "route_sparse_gqa_amd", "csrc", "gather_attention.hip"), "rb") as f:
-        h.update(f.read())
+    for name in ATTENTION_SOURCES:
+        with open(os.path.join(ROOT, "route_sparse_gqa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -264,6 +264,18 @@ int qsa_backward(const void *q, const int64_t q_strides[4], const void *k, const
 size_t qsa_select_workspace_size(int64_t B, int64_t S_q, int64_t H, int64_t q_offset, int64_t compress_ratio);
 
 /*
+ * qsa_select_chunk_workspace_size -- bytes of score workspace with which
+ * qsa_select_token_ids processes its query rows in passes of at least
+ * query_chunk_size rows (whole row tiles; the qsa page's `query_chunk_size`
+ * of `select_qsa_token_ids`, which bounds memory and changes no result):
+ * min(ceil(query_chunk_size / tile_rows) * tile_rows * ld * 4, the one-pass
+ * size of qsa_select_workspace_size), tile_rows and ld as there.
+ * Returns 0 when an argument is out of range or query_chunk_size < 1.
+ */
+size_t qsa_select_chunk_workspace_size(int64_t B, int64_t S_q, int64_t H, int64_t q_offset, int64_t compress_ratio,
+                                       int64_t query_chunk_size);
+
+/*
  * qsa_select_token_ids -- route selection by compressed-block scores: the
  * producer of the routes the attention entry points consume.
  *

@@ -16,7 +16,8 @@ runs in the library's HIP kernels; there is no other code path.
 * ``qsa_select_token_ids(index_queries, compressed_keys, sequence_lengths, token_budget, compress_ratio,
   query_position_offset=0, global_sequence_length=None, query_chunk_size=None)``
 * ``qsa_forward_workspace_size(B, S_q, K)``, ``qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)``,
-  ``qsa_select_workspace_size(B, S_q, H, q_offset, compress_ratio)``
+  ``qsa_select_workspace_size(B, S_q, H, q_offset, compress_ratio)``,
+  ``qsa_select_chunk_workspace_size(B, S_q, H, q_offset, compress_ratio, query_chunk_size)``
 * ``qsa_status_string(status)``
 """
 
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_backward.restype = i32
         L.qsa_select_workspace_size.argtypes = [i64, i64, i64, i64, i64]
         L.qsa_select_workspace_size.restype = ctypes.c_size_t
+        L.qsa_select_chunk_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
+        L.qsa_select_chunk_workspace_size.restype = ctypes.c_size_t
         L.qsa_select_token_ids.argtypes = [p, P64, p, P64, p, i64, i64, i64, i64, i64, i64, i64, i64, p, p,
                                            ctypes.c_size_t, p]
         L.qsa_select_token_ids.restype = i32
@@ -106,6 +109,12 @@ def qsa_backward_workspace_size(B: int, S_q: int, S_kv: int, Hq: int, Hkv: int, 
 
 def qsa_select_workspace_size(B: int, S_q: int, H: int, q_offset: int, compress_ratio: int) -> int:
     return int(lib().qsa_select_workspace_size(int(B), int(S_q), int(H), int(q_offset), int(compress_ratio)))
+
+
+def qsa_select_chunk_workspace_size(B: int, S_q: int, H: int, q_offset: int, compress_ratio: int,
+                                    query_chunk_size: int) -> int:
+    return int(lib().qsa_select_chunk_workspace_size(int(B), int(S_q), int(H), int(q_offset), int(compress_ratio),
+                                                     int(query_chunk_size)))
 
 
 def _check(status: int, where: str) -> None:
@@ -364,13 +373,10 @@ def qsa_select_token_ids(index_queries: torch.Tensor, compressed_keys: torch.Ten
         raise ValueError(f"out must be a contiguous int32 tensor of shape {(B, S_q, width)}")
     _on_device(out, dev, "out")
     if workspace is None:
-        full = qsa_select_workspace_size(B, S_q, H, q_off, c)
-        ws_bytes = full
-        if query_chunk_size is not None and full > 0:
-            tile_rows = 16 if H <= 16 else (8 if H <= 32 else 4)
-            tiles = -(-B * S_q // tile_rows)
-            per_tile = full // tiles
-            ws_bytes = min(full, max(1, -(-int(query_chunk_size) // tile_rows)) * per_tile)
+        if query_chunk_size is None:
+            ws_bytes = qsa_select_workspace_size(B, S_q, H, q_off, c)
+        else:
+            ws_bytes = qsa_select_chunk_workspace_size(B, S_q, H, q_off, c, max(1, int(query_chunk_size)))
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     _on_device(workspace, dev, "workspace")
     st = lib().qsa_select_token_ids(_ptr(iq), _strides(iq), _ptr(ck), _strides(ck), _ptr(lens), B, S_q, H, D,
@@ -383,6 +389,7 @@ def qsa_select_token_ids(index_queries: torch.Tensor, compressed_keys: torch.Ten
 __all__ = [
     "qsa_select_token_ids",
     "qsa_select_workspace_size",
+    "qsa_select_chunk_workspace_size",
     "qsa_preprocess",
     "qsa_tile_lists",
     "qsa_forward",

@@ -33,10 +33,6 @@ SOURCES = [
     "qsa_api.cpp",
 ]
 
-# Measuring tool for bench.py --calibrate-gather, kept out of the attention library's API.
-PROBE_SOURCES = ["probe_gather.hip"]
-PROBE_LIB_PATH = os.path.join(PKG, "libqsa_probe.so")
-
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
@@ -81,12 +77,11 @@ def _link(objs, path: str) -> None:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES) + len(PROBE_SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
-    _link(objs[:len(SOURCES)], LIB_PATH)
-    _link(objs[len(SOURCES):], PROBE_LIB_PATH)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    _link(objs, LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH} and {PROBE_LIB_PATH}")
+        print(f"built {LIB_PATH}")
     return LIB_PATH
 
 

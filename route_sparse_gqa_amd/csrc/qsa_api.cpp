@@ -514,6 +514,18 @@ QSA_EXPORT size_t qsa_select_workspace_size(int64_t B, int64_t S_q, int64_t H, i
   return round_up(static_cast<size_t>(z.full_bytes), kWorkspaceAlign);
 }
 
+QSA_EXPORT size_t qsa_select_chunk_workspace_size(int64_t B, int64_t S_q, int64_t H, int64_t q_offset,
+                                                  int64_t compress_ratio, int64_t query_chunk_size) {
+  SelectSizes z;
+  if (query_chunk_size < 1 || q_offset < 0 || compress_ratio < 1 || S_q < 1 || q_offset > INT64_MAX - S_q) return 0;
+  if (check_select_dims(B, S_q, H, 64, q_offset + S_q, q_offset, 1, compress_ratio, &z) != QSA_OK &&
+      check_select_dims(B, S_q, H, 64, q_offset + S_q, q_offset, compress_ratio, compress_ratio, &z) != QSA_OK)
+    return 0;
+  const int64_t tiles = (query_chunk_size + z.tile_rows - 1) / z.tile_rows;  // whole row tiles per pass
+  const int64_t bytes = tiles < z.tiles ? tiles * z.tile_bytes : z.full_bytes;
+  return round_up(static_cast<size_t>(bytes), kWorkspaceAlign);
+}
+
 QSA_EXPORT int qsa_select_token_ids(const void* index_q, const int64_t q_strides[4], const void* block_k,
                                     const int64_t k_strides[4], const int64_t* seq_lens, int64_t B, int64_t S_q,
                                     int64_t H, int64_t D, int64_t S_global, int64_t q_offset, int64_t token_budget,

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "qsa_preprocess", "qsa_forward", "qsa_forward_preprocessed", "qsa_forward_workspace_size",
         "qsa_backward", "qsa_backward_workspace_size", "qsa_tile_lists", "qsa_status_string",
-        "qsa_select_token_ids", "qsa_select_workspace_size"])
+        "qsa_select_token_ids", "qsa_select_workspace_size", "qsa_select_chunk_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -169,6 +169,18 @@ def test_select_workspace_size():
     assert ws(1, 10, 16, -1, 4) == 0 and ws(1, 10, 16, 0, 0) == 0
 
 
+def test_select_chunk_workspace_size():
+    """Passes of at least query_chunk_size rows in whole row tiles, never more than the one-pass size."""
+    full, chunk = qsa.qsa_select_workspace_size, qsa.qsa_select_chunk_workspace_size
+    assert chunk(1, 65536, 16, 0, 4, 16) == 16 * 16384 * 4          # one 16-row tile
+    assert chunk(1, 65536, 16, 0, 4, 17) == 2 * 16 * 16384 * 4      # rounded up to whole tiles
+    assert chunk(1, 65536, 16, 0, 4, 1000) == 63 * 16 * 16384 * 4
+    assert chunk(2, 20, 40, 0, 4, 5) == 2 * 4 * 64 * 4              # H > 32: 4-row tiles
+    for args in ((1, 65536, 16, 0, 4), (2, 4096, 16, 0, 4), (1, 8192, 16, 24576, 4), (2, 20, 40, 0, 4)):
+        assert chunk(*args, 1 << 40) == full(*args)                  # a chunk past the rows: one pass
+    assert chunk(1, 10, 16, 0, 4, 0) == 0 and chunk(1, 10, 0, 0, 4, 16) == 0
+
+
 def _call_select(B=1, S_q=64, H=4, D=64, S_global=64, q_offset=0, budget=8, c=4, ws_bytes=1 << 20,
                  null_lens=False, alias_out_q=False, k_last_stride=1, misaligned_ws=False, q_row_stride=None):
     """Every call made with this helper carries one invalid argument (fake pointers never reach a launch)."""
@@ -202,22 +214,3 @@ def test_select_host_checks():
     assert _call_select(ws_bytes=16) == -10          # smaller than one 16-row tile of scores
     assert _call_select(misaligned_ws=True) == -10
     assert _call_select(q_row_stride=1 << 60) == -11        # the query tensor's extent overflows 64 bits
-
-
-def test_probe_library_loads_and_checks_its_arguments():
-    """libqsa_probe.so (the gather-ceiling probe behind bench.py --calibrate-gather) is built beside the
-    library; every call below fails its host check, so nothing launches."""
-    from route_sparse_gqa_amd.build import PROBE_LIB_PATH
-
-    P = ctypes.CDLL(PROBE_LIB_PATH)
-    P.qsa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
-                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    P.qsa_probe_gather.restype = ctypes.c_int
-    t, i, o = (ctypes.c_void_p(n << 32) for n in range(1, 4))  # distinct, never dereferenced
-    assert P.qsa_probe_gather(None, 16, 1024, i, 64, 1, 0, 0, o, None) == -1
-    assert P.qsa_probe_gather(t, 0, 1024, i, 64, 1, 0, 0, o, None) == -1         # no rows
-    assert P.qsa_probe_gather(t, 16, 256, i, 64, 1, 0, 0, o, None) == -1         # stride below one row
-    assert P.qsa_probe_gather(t, 16, 1024, i, 64, 1, 2, 0, o, None) == -1        # unknown path
-    assert P.qsa_probe_gather(t, 16, 1024, i, 64, 1, 0, -1, o, None) == -1       # negative LDS pad
-    assert P.qsa_probe_gather(t, 16, 1024, i, 64, 1, 0, 131073, o, None) == -1   # LDS pad past the CU
-    assert P.qsa_probe_gather(ctypes.c_void_p((1 << 32) + 8), 16, 1024, i, 64, 1, 0, 0, o, None) == -1  # misaligned

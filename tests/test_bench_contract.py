@@ -70,3 +70,31 @@ def test_algorithmic_flops_and_bytes():
     flops, alg_bytes = bench.algorithmic_counts(w, closed_form_pairs("right_padded"))
     assert flops == 52_101_578_752 and alg_bytes == 6_659_667_952
     assert np.isclose(alg_bytes / 8e12 * 1e3, 0.8325, atol=1e-4)  # ms at 8 TB/s
+
+
+def test_roofline_is_the_compulsory_floor_over_the_time():
+    """frac = t_floor / t against real peaks: for long_int64 the flops set the floor (2131.9 GFLOP at
+    2.5 PFLOP/s = 0.853 ms, against 1.73 GB of compulsory bytes at 8 TB/s = 0.22 ms)."""
+    w = WORKLOADS["long_int64"]
+    N = closed_form_pairs("long_int64")
+    flops, gather_bytes = bench.algorithmic_counts(w, N)
+    min_bytes = 1_730_000_000
+    for ms in (0.853, 5.0, 24.4):
+        r = bench.attention_roofline(w, N, flops, gather_bytes, min_bytes, [ms], None, "k")
+        assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+        assert np.isclose(r["frac"], r["t_floor_ms"] / ms)
+        assert np.isclose(r["achieved"], flops / (ms * 1e-3) / 1e12)
+        assert r["frac"] <= 1.0 + 1e-3
+        assert np.isclose(r["gather_rate_GBs"], gather_bytes / (ms * 1e-3) / 1e9)
+    assert np.isclose(bench.attention_roofline(w, N, flops, gather_bytes, min_bytes, [24.4], None, "k")["frac"],
+                      0.0349, atol=5e-4)
+    # a workload whose compulsory bytes dominate is counted against HBM
+    r = bench.attention_roofline(w, 1000, 4 * w.D * w.Hq * 1000, 10 ** 9, 8 * 10 ** 9, [2.0], 9 * 10 ** 9, "k")
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and np.isclose(r["frac"], 0.5)
+    assert np.isclose(r["hbm_traffic_GBs"], 4500.0)
+
+
+def test_cpu_info_reports_model_and_affinity():
+    info = bench.cpu_info()
+    assert info["affinity_cores"] == len(os.sched_getaffinity(0)) >= 1
+    assert "cpu_model" in info

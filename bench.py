@@ -144,10 +144,14 @@ class Plan:
         st = lambda t: (ctypes.c_int64 * t.dim())(*t.stride())
         self.pre_args = (i8(self.routes), 1 if routes.dtype == np.int64 else 0, B, S_q, K, st(self.routes),
                          w.S_kv, i8(self.lst), i8(self.cnt), i8(self.mem), i8(self.tc), self.stream)
+        att_ws = qsa.qsa_attention_workspace_size(B, S_q, w.S_kv, w.Hq, w.Hkv, w.D, K)
+        self.att_ws = torch.empty(att_ws, dtype=torch.uint8, device=dev) if att_ws else None
+        self.split = att_ws > 0
         self.fwd_args = (i8(self.q), st(self.q), i8(self.k), st(self.k), i8(self.v), st(self.v), i8(self.lst),
                          i8(self.cnt), B, S_q, w.S_kv, w.Hq, w.Hkv, w.D, K, ctypes.c_float(w.scale),
-                         i8(self.out), None, self.stream)
-        fused_ws = qsa.qsa_forward_workspace_size(B, S_q, K)
+                         i8(self.out), None, i8(self.att_ws) if self.split else None, ctypes.c_size_t(att_ws),
+                         self.stream)
+        fused_ws = qsa.qsa_forward_workspace_size(B, S_q, w.S_kv, w.Hq, w.Hkv, w.D, K)
         self.fused_ws = torch.empty(fused_ws, dtype=torch.uint8, device=dev)
         self.fused_out = torch.empty_like(self.out)
         self.fused_args = (i8(self.q), st(self.q), i8(self.k), st(self.k), i8(self.v), st(self.v), i8(self.routes),
@@ -175,7 +179,7 @@ class Plan:
         st = lambda t: (ctypes.c_int64 * t.dim())(*t.stride())
         self.lse = torch.empty((B, S_q, w.Hq), dtype=torch.float32, device=dev)
         args = list(self.fwd_args)
-        args[-2] = i8(self.lse)
+        args[-4] = i8(self.lse)
         rc = self.L.qsa_forward_preprocessed(*args)
         if rc != 0:
             raise RuntimeError(f"qsa_forward_preprocessed failed with status {rc}")
@@ -221,6 +225,8 @@ class Plan:
             raise RuntimeError(f"qsa_forward failed with status {rc}")
 
     def kernel_name(self) -> str:
+        if self.split:
+            return "range_offsets_kernel + gather_attention_kernel (key-range split) + range_combine_kernel"
         return "gather_attention_kernel"
 
 
@@ -320,10 +326,10 @@ def cpu_baseline(w, q, k, v, routes, counts, target_s: float, windows: int = 16)
         return dt, sum(int(per_row[s0:s0 + m].sum()) for s0 in starts), m, starts
 
     dt, n_routes, m, starts = run(max(1, threads // w.B))  # at least one row per thread in each window
-    while dt < 0.5 and m < max_m:
-        dt, n_routes, m, starts = run(m * 4)
-    if dt < target_s and m < max_m:
-        dt, n_routes, m, starts = run(int(m * target_s / max(dt, 1e-3)))
+    for _ in range(4):  # the first runs also pay thread start-up and page faults: grow until the sample is long
+        if dt >= 0.8 * target_s or m >= max_m:
+            break
+        dt, n_routes, m, starts = run(int(m * min(16.0, 1.1 * target_s / max(dt, 1e-3))) + 1)
     rows = w.B * m * n_win
     tflops = 4 * w.D * w.Hq * n_routes / dt / 1e12
     return {
@@ -727,7 +733,7 @@ def run_select(args):
     }), flush=True)
 
 
-ATTENTION_SOURCES = ("gather_attention.hip", "device_common.h")
+ATTENTION_SOURCES = ("gather_attention.hip", "device_common.h", "qsa_internal.h")
 
 
 def _kernel_sha() -> str:

@@ -133,11 +133,37 @@ int qsa_tile_lists(const int32_t *tile_class, int64_t B, int64_t n_rows, int64_t
                    int32_t *rev_partial_idx, int32_t *rev_full_count, int32_t *rev_full_idx, void *stream);
 
 /*
- * qsa_forward_workspace_size -- bytes of device workspace qsa_forward needs:
- * the compacted lists and counts (4*B*S_q*K + 4*B*S_q) plus alignment.
- * Returns 0 when a size is < 1 or the product overflows.
+ * qsa_attention_workspace_size -- recommended bytes of device workspace for
+ * the attention kernels (qsa_forward_preprocessed), 0 when these shapes need
+ * none.
+ *
+ * When one KV head's K and V rows span more than 4 MiB (S_kv * 4 * D bytes;
+ * one XCD's L2), the attention splits each row's ascending route list at
+ * multiples of W key IDs, W = the largest power of two with W * 4 * D <=
+ * 4 MiB (doubled until P = ceil(S_kv / W) <= 63), and gathers one key range
+ * at a time on every XCD.  Its workspace holds, 256-B aligned each:
+ *   range starts     int32 [B*S_q][P + 1]: for row r, entry p is the first
+ *                    list position whose ID lies in range p or later, and
+ *                    entry P the row's count;
+ *   partial outputs  bf16 [R][Hkv][P][G][D], R = rows per pass;
+ *   partial sums     fp32 [R][Hkv][P][G] (log2 of each partial's softmax
+ *                    sum against its maximum score, log2 domain).
+ * The rows are processed in passes of R rows, R = every row or as many
+ * multiples of 4 as fit (at least min(B*S_q, 256)); the recommended size
+ * takes R = min(B*S_q, 16384).  Results do not depend on R.
+ * Returns 0 as well when a size is out of range.
  */
-size_t qsa_forward_workspace_size(int64_t B, int64_t S_q, int64_t K);
+size_t qsa_attention_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D,
+                                    int64_t K);
+
+/*
+ * qsa_forward_workspace_size -- recommended bytes of device workspace for
+ * qsa_forward: the compacted lists and counts (4*B*S_q*K and 4*B*S_q bytes,
+ * each 256-B aligned), followed by the attention's workspace
+ * (qsa_attention_workspace_size).  Returns 0 when a size is out of range.
+ */
+size_t qsa_forward_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D,
+                                  int64_t K);
 
 /*
  * qsa_forward -- route-sparse GQA attention, BF16 in and out, fp32 softmax.
@@ -157,12 +183,14 @@ size_t qsa_forward_workspace_size(int64_t B, int64_t S_q, int64_t K);
  *   scale    finite and > 0 (the pages default to 1/sqrt(D); callers pass it).
  *   out      OUT [B, S_q, Hq, D] bf16, contiguous, must not overlap any input
  *            or the workspace.
- *   workspace, workspace_bytes   device scratch of at least
- *            qsa_forward_workspace_size(B, S_q, K) bytes, 256-B aligned; it
- *            receives the compacted lists (overwritten each call).
+ *   workspace, workspace_bytes   device scratch, 256-B aligned,
+ *            overwritten each call: the compacted lists and counts, then
+ *            the attention's workspace; qsa_forward_workspace_size(...)
+ *            bytes are recommended, and the lists plus the attention's
+ *            smallest pass suffice (see qsa_attention_workspace_size).
  *
  * Runs the route-normalisation kernel into the workspace, then the
- * gather-attention kernel.  Errors: NULL_POINTER, EMPTY_DIM, KV_LENGTH
+ * gather-attention kernel(s).  Errors: NULL_POINTER, EMPTY_DIM, KV_LENGTH
  * (S_kv > 2^31), HEADS, HEAD_DIM, ROUTE_DTYPE, SCALE, LAYOUT, ALIAS,
  * WORKSPACE, LIMIT, HIP.
  */
@@ -187,13 +215,22 @@ int qsa_forward(const void *q, const int64_t q_strides[4], const void *k, const 
  *            log sum_j exp(s_j) (the statistic the backward needs, fa4_qsa
  *            page: the FA4 kernel owns first-order autograd); -inf for an
  *            empty route set.  Must not overlap any other argument.
+ *   workspace, workspace_bytes   device scratch, 256-B aligned, overwritten
+ *            each call; NULL/0 when qsa_attention_workspace_size(...) is 0,
+ *            else at least the smallest pass (WORKSPACE otherwise).
  *   Other arguments as in qsa_forward.
+ *
+ * Gathered K/V rows are addressed as (ID) x (token stride) from each
+ * (batch, head) base: in 32 bits when the token stride is non-negative and
+ * (S_kv - 1) * stride * 2 + 2 * D < 2^32 bytes for both K and V, in 64 bits
+ * otherwise (flex_qsa page, `_membership_flat_offset`: offsets past 2^31).
  */
 int qsa_forward_preprocessed(const void *q, const int64_t q_strides[4], const void *k,
                              const int64_t k_strides[4], const void *v, const int64_t v_strides[4],
                              const int32_t *route_list, const int32_t *route_count, int64_t B,
                              int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,
-                             float scale, void *out, float *lse, void *stream);
+                             float scale, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /*
  * qsa_backward_workspace_size -- bytes of device workspace qsa_backward

@@ -15,7 +15,9 @@ runs in the library's HIP kernels; there is no other code path.
 * ``qsa_backward(q, k, v, out, dout, lse, route_list, route_count, scale=None)``
 * ``qsa_select_token_ids(index_queries, compressed_keys, sequence_lengths, token_budget, compress_ratio,
   query_position_offset=0, global_sequence_length=None, query_chunk_size=None)``
-* ``qsa_forward_workspace_size(B, S_q, K)``, ``qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)``,
+* ``qsa_forward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)``,
+  ``qsa_attention_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)``,
+  ``qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)``,
   ``qsa_select_workspace_size(B, S_q, H, q_offset, compress_ratio)``,
   ``qsa_select_chunk_workspace_size(B, S_q, H, q_offset, compress_ratio, query_chunk_size)``
 * ``qsa_status_string(status)``
@@ -67,15 +69,17 @@ def lib() -> ctypes.CDLL:
         P64 = ctypes.POINTER(ctypes.c_int64)
         L.qsa_status_string.argtypes = [i32]
         L.qsa_status_string.restype = ctypes.c_char_p
-        L.qsa_forward_workspace_size.argtypes = [i64, i64, i64]
+        L.qsa_forward_workspace_size.argtypes = [i64] * 7
         L.qsa_forward_workspace_size.restype = ctypes.c_size_t
+        L.qsa_attention_workspace_size.argtypes = [i64] * 7
+        L.qsa_attention_workspace_size.restype = ctypes.c_size_t
         L.qsa_preprocess.argtypes = [p, i32, i64, i64, i64, P64, i64, p, p, p, p, p]
         L.qsa_preprocess.restype = i32
         L.qsa_forward.argtypes = [p, P64, p, P64, p, P64, p, i32, P64, i64, i64, i64, i64, i64, i64, i64,
                                   ctypes.c_float, p, p, ctypes.c_size_t, p]
         L.qsa_forward.restype = i32
         L.qsa_forward_preprocessed.argtypes = [p, P64, p, P64, p, P64, p, p, i64, i64, i64, i64, i64, i64, i64,
-                                               ctypes.c_float, p, p, p]
+                                               ctypes.c_float, p, p, p, ctypes.c_size_t, p]
         L.qsa_forward_preprocessed.restype = i32
         L.qsa_tile_lists.argtypes = [p, i64, i64, i64, p, p, p, p, p, p, p, p, p]
         L.qsa_tile_lists.restype = i32
@@ -99,8 +103,12 @@ def qsa_status_string(status: int) -> str:
     return lib().qsa_status_string(int(status)).decode()
 
 
-def qsa_forward_workspace_size(B: int, S_q: int, K: int) -> int:
-    return int(lib().qsa_forward_workspace_size(int(B), int(S_q), int(K)))
+def qsa_forward_workspace_size(B: int, S_q: int, S_kv: int, Hq: int, Hkv: int, D: int, K: int) -> int:
+    return int(lib().qsa_forward_workspace_size(int(B), int(S_q), int(S_kv), int(Hq), int(Hkv), int(D), int(K)))
+
+
+def qsa_attention_workspace_size(B: int, S_q: int, S_kv: int, Hq: int, Hkv: int, D: int, K: int) -> int:
+    return int(lib().qsa_attention_workspace_size(int(B), int(S_q), int(S_kv), int(Hq), int(Hkv), int(D), int(K)))
 
 
 def qsa_backward_workspace_size(B: int, S_q: int, S_kv: int, Hq: int, Hkv: int, D: int, K: int) -> int:
@@ -262,7 +270,7 @@ def qsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, routes: torch
     K = routes.shape[2]
     dt = _route_dtype(routes)
     out = _output(out, (B, S_q, Hq, D), dev)
-    ws_bytes = qsa_forward_workspace_size(B, S_q, K)
+    ws_bytes = qsa_forward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     _on_device(workspace, dev, "workspace")
@@ -283,11 +291,14 @@ def _lists(route_list: torch.Tensor, route_count: torch.Tensor, B: int, S_q: int
 
 def qsa_forward_preprocessed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, route_list: torch.Tensor,
                              route_count: torch.Tensor, scale: Optional[float] = None,
-                             out: Optional[torch.Tensor] = None, return_lse: bool = False):
+                             out: Optional[torch.Tensor] = None, return_lse: bool = False,
+                             workspace: Optional[torch.Tensor] = None):
     """Gather-attention alone, on lists produced by ``qsa_preprocess(routes, S_kv)``.
 
     Returns ``out``, or ``(out, lse)`` with ``lse`` float32 [B,S_q,Hq] (natural-log
     log-sum-exp of each row's scaled scores, -inf for empty rows) when ``return_lse``.
+    ``workspace`` (uint8, on the inputs' device) defaults to the recommended
+    ``qsa_attention_workspace_size`` bytes; shapes that need none get none.
     """
     dev = _require_gpu(q, k, v, route_list, route_count)
     q, k, v = _bf16_operand(q, "query"), _bf16_operand(k, "key"), _bf16_operand(v, "value")
@@ -296,9 +307,16 @@ def qsa_forward_preprocessed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     K = route_list.shape[2]
     out = _output(out, (B, S_q, Hq, D), dev)
     lse = torch.empty((B, S_q, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    if workspace is None:
+        ws_bytes = qsa_attention_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
+    if workspace is not None:
+        _on_device(workspace, dev, "workspace")
     st = lib().qsa_forward_preprocessed(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
                                         _ptr(route_list), _ptr(route_count), B, S_q, S_kv, Hq, Hkv, D, K,
-                                        _scale(scale, D), _ptr(out), _ptr(lse), _stream(dev))
+                                        _scale(scale, D), _ptr(out), _ptr(lse), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                        _stream(dev))
     _check(st, "qsa_forward_preprocessed")
     return (out, lse) if return_lse else out
 
@@ -396,6 +414,7 @@ __all__ = [
     "qsa_forward_preprocessed",
     "qsa_backward",
     "qsa_forward_workspace_size",
+    "qsa_attention_workspace_size",
     "qsa_backward_workspace_size",
     "qsa_status_string",
     "lib",

@@ -34,7 +34,22 @@
 //    so the accumulator rescale is skipped once the max has settled.
 //    Probabilities are rounded to bf16 once; the same rounded values feed
 //    both the PV product and the normaliser.
+//
+// Key-range split (kSplit), for key ranges larger than an XCD's L2: a work
+// unit is (row, KV head, key range [pW, (p+1)W)); the unit's part of the
+// row's ascending list is [offs[p], offs[p+1]) of the range-start table.
+// Workgroups are ordered range-major, so at any time every XCD gathers from
+// one W-key range of one KV head (4 MiB of K and V).  A unit whose row has
+// routes in no other range writes the output itself; otherwise it writes
+// its normalised partial output (bf16) and the log2 of its softmax sum
+// against its own maximum, and `range_combine_kernel` merges the partials of
+// the row in ascending range order:
+//   out = sum_p 2^(s_p - M) o_p / sum_p 2^(s_p - M),  M = max_p s_p,
+// which is the softmax over the union of the ranges (the ranges partition
+// the row's route set).
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "device_common.h"
 #include "qsa_internal.h"
@@ -57,45 +72,104 @@ struct Geometry {
   static constexpr int kKStride = D + 8;                // K slab row stride in bf16 (2D + 16 bytes)
 };
 
-template <int D, bool kNarrow>
-__global__ void __launch_bounds__(64 * kWaves)
-    gather_attention_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                            const uint16_t* __restrict__ v, int64_t qs0, int64_t qs1, int64_t qs2,
-                            int64_t ks0, int64_t ks1, int64_t ks2, int64_t vs0, int64_t vs1, int64_t vs2,
-                            const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count,
-                            int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t K, int G,
-                            float scale_log2e, int64_t n_units, uint16_t* __restrict__ out,
-                            float* __restrict__ lse) {
+struct KernelArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2;
+  const int32_t* route_list;
+  const int32_t* route_count;
+  int64_t S_q, S_kv, Hq, Hkv, K;
+  int G;
+  float scale_log2e;
+  int64_t n_units;  // unsplit: B * S_q * Hkv
+  uint16_t* out;
+  float* lse;
+  // key-range split
+  const int32_t* offs;  // [B * S_q][P + 1] range starts within each row's list
+  int P;
+  int64_t row0, pass_rows, rowgroups;  // rows [row0, row0 + pass_rows) of this pass, ceil(pass_rows / 4)
+  uint16_t* part_o;                    // [pass_rows][Hkv][P][G][D] bf16
+  float* part_lse;                     // [pass_rows][Hkv][P][G] fp32, log2 domain
+};
+
+// Range starts of one row, one per lane: lane l < P gets its range's part
+// [lo, hi) of the list, clamped into [0, n], n = the row's count clamped into
+// [0, K] (stored at index P); returns the mask of lanes with a non-empty part.
+__device__ __forceinline__ uint64_t range_parts(const int32_t* __restrict__ offs_row, int P, int64_t K, int lane,
+                                                int* lo_out, int* hi_out) {
+  const int32_t o = lane <= P ? offs_row[lane] : 0;
+  const int n = min(max(__shfl(o, P), 0), static_cast<int>(K));
+  const int lo = min(max(o, 0), n);
+  const int hi = min(max(__shfl(o, min(lane + 1, 63)), lo), n);
+  *lo_out = lo;
+  *hi_out = hi;
+  return __ballot(lane < P && lo < hi);
+}
+
+template <int D, bool kNarrow, bool kSplit>
+__global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const KernelArgs a) {
   using Geo = Geometry<D>;
   __shared__ __attribute__((aligned(16))) uint16_t slab[kWaves][kChunk * Geo::kStride];
   __shared__ __attribute__((aligned(16))) uint16_t kslab[kWaves][kChunk * Geo::kKStride];
 
+  const int64_t S_q = a.S_q, Hq = a.Hq, Hkv = a.Hkv;
+  const int G = a.G;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));  // wave-uniform
-  // Workgroup x -> (KV head x % Hkv, four neighbouring rows): workgroups are
-  // dealt round-robin to the 8 XCDs, so when Hkv divides 8 each XCD serves a
-  // single KV head (half the K/V working set per L2 at Hkv = 2), while rows
-  // still spread evenly over the XCDs.  Rows are taken from the last to the
-  // first: with causal routes later rows route more keys, so the longest
-  // rows start first and the short ones fill the end of the launch.
   const int64_t x = blockIdx.x;
-  const int64_t hk = x % Hkv;
-  const int64_t row = n_units / Hkv - 1 - ((x / Hkv) * kWaves + wave);  // b * S_q + i
-  if (row < 0) return;  // the last workgroup's surplus waves; no workgroup barriers in this kernel
+  int64_t hk, row, local = 0;
+  int p = 0;
+  if constexpr (!kSplit) {
+    // Workgroup x -> (KV head x % Hkv, four neighbouring rows): workgroups are
+    // dealt round-robin to the 8 XCDs, so when Hkv divides 8 each XCD serves a
+    // single KV head (half the K/V working set per L2 at Hkv = 2), while rows
+    // still spread evenly over the XCDs.  Rows are taken from the last to the
+    // first: with causal routes later rows route more keys, so the longest
+    // rows start first and the short ones fill the end of the launch.
+    hk = x % Hkv;
+    row = a.n_units / Hkv - 1 - ((x / Hkv) * kWaves + wave);  // b * S_q + i
+    if (row < 0) return;  // the last workgroup's surplus waves; no workgroup barriers in this kernel
+  } else {
+    // Workgroup x -> phase x / rowgroups = (range p, KV head hk), then four
+    // rows of the pass, last rows first.  Consecutive workgroups go to all
+    // XCDs in turn, so the XCDs sweep the phases together.
+    const int64_t phase = x / a.rowgroups;
+    p = static_cast<int>(phase / Hkv);
+    hk = phase - static_cast<int64_t>(p) * Hkv;
+    local = a.pass_rows - 1 - ((x - phase * a.rowgroups) * kWaves + wave);
+    if (local < 0) return;
+    row = a.row0 + local;
+  }
   const int64_t b = row / S_q;
   const int64_t i = row % S_q;
   const int c = lane & 15;  // head column of this lane; also key/dim row within a 16-tile
   const int g = lane >> 4;  // k-group of this lane
   const bool head_ok = c < G;
-  uint16_t* out_row = out + (row * Hq + hk * G + c) * D;  // only dereferenced when head_ok
+  uint16_t* out_row = a.out + (row * Hq + hk * G + c) * D;  // only dereferenced when head_ok
 
-  const int n = static_cast<int>(min(max(static_cast<int64_t>(route_count[row]), int64_t{0}), K));
+  int first = 0, n;  // this unit's part of the row's list: [first, first + n)
+  bool direct = true;  // the unit writes the output (not a partial)
+  if constexpr (!kSplit) {
+    n = static_cast<int>(min(max(static_cast<int64_t>(a.route_count[row]), int64_t{0}), a.K));
+  } else {
+    int lo_l, hi_l;
+    const uint64_t parts = range_parts(a.offs + row * (a.P + 1), a.P, a.K, lane, &lo_l, &hi_l);
+    if (((parts >> p) & 1u) == 0) {
+      if (!(parts == 0 && p == 0)) return;  // nothing in this range; an empty row is written once, below
+      n = 0;
+    } else {
+      first = __shfl(lo_l, p);
+      n = __shfl(hi_l, p) - first;
+      direct = __builtin_popcountll(parts) == 1;
+    }
+  }
   if (n == 0) {  // empty route set: exactly +0.0 (and a log-sum-exp of -inf)
     if (head_ok) {
 #pragma unroll
       for (int t = 0; t < Geo::kDimTiles; ++t)
         *reinterpret_cast<u32x2*>(out_row + 16 * t + 4 * g) = u32x2{0u, 0u};
-      if (lse != nullptr && g == 0) lse[row * Hq + hk * G + c] = -INFINITY;
+      if (a.lse != nullptr && g == 0) a.lse[row * Hq + hk * G + c] = -INFINITY;
     }
     return;
   }
@@ -103,7 +177,7 @@ __global__ void __launch_bounds__(64 * kWaves)
   // Q^T as the MFMA B operand: lane (c, g) holds head c, dims 32s + 8g .. +7.
   bf16x8 qf[Geo::kSteps];
   {
-    const uint16_t* qp = q + b * qs0 + i * qs1 + (hk * G + (head_ok ? c : 0)) * qs2 + 8 * g;
+    const uint16_t* qp = a.q + b * a.qs0 + i * a.qs1 + (hk * G + (head_ok ? c : 0)) * a.qs2 + 8 * g;
 #pragma unroll
     for (int s = 0; s < Geo::kSteps; ++s)
       qf[s] = head_ok ? __builtin_bit_cast(bf16x8, load16(reinterpret_cast<const char*>(qp + 32 * s)))
@@ -116,13 +190,13 @@ __global__ void __launch_bounds__(64 * kWaves)
   float m_run = -INFINITY;  // reference max (log2 domain) of head c
   float l_run = 0.f;        // this lane's share of the running sum of head c
 
-  const int32_t* lst = route_list + row * K;
-  const int64_t ks1b = 2 * ks1, vs1b = 2 * vs1;  // row strides in bytes
-  const char* kb = reinterpret_cast<const char*>(k + b * ks0 + hk * ks2) + 16 * (lane % Geo::kLanesPerRow);
-  const char* vb = reinterpret_cast<const char*>(v + b * vs0 + hk * vs2) + 16 * (lane % Geo::kLanesPerRow);
+  const int32_t* lst = a.route_list + row * a.K + first;
+  const int64_t ks1b = 2 * a.ks1, vs1b = 2 * a.vs1;  // row strides in bytes
+  const char* kb = reinterpret_cast<const char*>(a.k + b * a.ks0 + hk * a.ks2) + 16 * (lane % Geo::kLanesPerRow);
+  const char* vb = reinterpret_cast<const char*>(a.v + b * a.vs0 + hk * a.vs2) + 16 * (lane % Geo::kLanesPerRow);
   uint16_t* my_slab = slab[wave];
   uint16_t* my_kslab = kslab[wave];
-  const int32_t id_max = static_cast<int32_t>(S_kv - 1);
+  const int32_t id_max = static_cast<int32_t>(a.S_kv - 1);
   auto clamp_id = [&](int32_t x) { return min(max(x, 0), id_max); };
   // Raw route ID of key base + c (tails repeat the last route; clamped later).
   auto load_id = [&](int base) { return lst[min(base + c, n - 1)]; };
@@ -190,7 +264,7 @@ __global__ void __launch_bounds__(64 * kWaves)
     // Online softmax (log2 domain) against a lazily raised reference max.
     float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = base + 4 * g + r < n ? st[r] * scale_log2e : -INFINITY;
+    for (int r = 0; r < 4; ++r) x[r] = base + 4 * g + r < n ? st[r] * a.scale_log2e : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));      // finite: the chunk holds at least one key
@@ -225,29 +299,174 @@ __global__ void __launch_bounds__(64 * kWaves)
   const float inv = 1.0f / l_tot;
   // Natural-log log-sum-exp of the scaled scores: the sum is taken against
   // the reference max m_run (log2 domain), from the same bf16-rounded
-  // probabilities as the output.
-  if (lse != nullptr && head_ok && g == 0) lse[row * Hq + hk * G + c] = (m_run + log2f(l_tot)) * kLn2;
+  // probabilities as the output.  A partial keeps it in the log2 domain.
+  if (direct) {
+    if (a.lse != nullptr && head_ok && g == 0) a.lse[row * Hq + hk * G + c] = (m_run + log2f(l_tot)) * kLn2;
+  } else if (head_ok && g == 0) {
+    a.part_lse[((local * Hkv + hk) * a.P + p) * G + c] = m_run + log2f(l_tot);
+  }
+  uint16_t* dst = direct ? out_row : a.part_o + (((local * Hkv + hk) * a.P + p) * G + c) * D;
   if (head_ok) {
 #pragma unroll
     for (int t = 0; t < Geo::kDimTiles; ++t) {
       bf16x4 o;
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(acc[t][r] * inv);
-      *reinterpret_cast<u32x2*>(out_row + 16 * t + 4 * g) = __builtin_bit_cast(u32x2, o);
+      *reinterpret_cast<u32x2*>(dst + 16 * t + 4 * g) = __builtin_bit_cast(u32x2, o);
     }
   }
 }
 
+// Merges the partial results of one (row, KV head) of a split pass: one
+// wavefront per unit; lane L takes the 8-element pieces L, L + 64, .. of the
+// unit's G x D outputs.  Rows with routes in at most one range were written
+// by the split kernel and are skipped.
+template <int D>
+__global__ void __launch_bounds__(64 * kWaves) range_combine_kernel(const KernelArgs a) {
+  constexpr int kPieces = D / 32;  // pieces per lane at G = 16: 16 * D / 8 / 64
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if (unit >= a.pass_rows * a.Hkv) return;
+  const int64_t local = unit / a.Hkv;
+  const int64_t hk = unit - local * a.Hkv;
+  const int64_t row = a.row0 + local;
+  const int G = a.G;
+  int lo_l, hi_l;
+  const uint64_t parts = range_parts(a.offs + row * (a.P + 1), a.P, a.K, lane, &lo_l, &hi_l);
+  if (__builtin_popcountll(parts) < 2) return;
+
+  const int n_pieces = G * D / 8;
+  const int64_t u0 = (local * a.Hkv + hk) * a.P;  // partial index of range 0 of this unit
+  float mx[kPieces], wsum[kPieces];
+  float acc[kPieces][8];
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) {
+    mx[k] = -INFINITY;
+    wsum[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+  }
+  // the largest log2-sum-exp of each head over the ranges
+  for (uint64_t m = parts; m != 0; m &= m - 1) {
+    const int p = __builtin_ctzll(m);
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const int piece = lane + 64 * k;
+      if (piece < n_pieces) mx[k] = fmaxf(mx[k], a.part_lse[(u0 + p) * G + piece * 8 / D]);
+    }
+  }
+  // weighted sum in ascending range order
+  for (uint64_t m = parts; m != 0; m &= m - 1) {
+    const int p = __builtin_ctzll(m);
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const int piece = lane + 64 * k;
+      if (piece < n_pieces) {
+        const float w = exp2f(a.part_lse[(u0 + p) * G + piece * 8 / D] - mx[k]);
+        const u32x4 v = load16(a.part_o + ((u0 + p) * G * D + piece * 8));
+        wsum[k] += w;
+        const uint32_t words[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[k][2 * e] += w * bf16_lo(words[e]);
+          acc[k][2 * e + 1] += w * bf16_hi(words[e]);
+        }
+      }
+    }
+  }
+  uint16_t* out_unit = a.out + (row * a.Hq + hk * G) * D;
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) {
+    const int piece = lane + 64 * k;
+    if (piece < n_pieces) {
+      const float inv = 1.0f / wsum[k];
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(acc[k][e] * inv);
+      *reinterpret_cast<u32x4*>(out_unit + piece * 8) = __builtin_bit_cast(u32x4, o);
+      if (a.lse != nullptr && (piece * 8) % D == 0)
+        a.lse[row * a.Hq + hk * G + piece * 8 / D] = (mx[k] + log2f(wsum[k])) * kLn2;
+    }
+  }
+}
+
+// Range starts of each row's list: offs[row][p] = the first position whose
+// ID (clamped into [0, S_kv)) lies in range p or a later one, offs[row][P] =
+// the row's count clamped into [0, K].  One wavefront per row; for an
+// ascending list every entry is written exactly once: by the position where
+// the range changes, or by the end for ranges past the last ID.
+__global__ void __launch_bounds__(64 * kWaves)
+    range_offsets_kernel(const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count,
+                         int64_t rows, int64_t K, int64_t S_kv, int w_shift, int P, int32_t* __restrict__ offs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int n = static_cast<int>(min(max(static_cast<int64_t>(route_count[row]), int64_t{0}), K));
+  const int32_t* lst = route_list + row * K;
+  int32_t* o = offs + row * (P + 1);
+  const int32_t id_max = static_cast<int32_t>(S_kv - 1);
+  auto range_of = [&](int32_t id) { return min(max(id, 0), id_max) >> w_shift; };
+  for (int j = lane; j < n; j += 64) {
+    const int r = range_of(lst[j]);
+    const int r_prev = j > 0 ? range_of(lst[j - 1]) : -1;
+    for (int q = r_prev + 1; q <= r; ++q) o[q] = j;
+  }
+  if (lane == 0) {
+    const int r_last = n > 0 ? range_of(lst[n - 1]) : -1;
+    for (int q = r_last + 1; q <= P; ++q) o[q] = n;
+  }
+}
+
+KernelArgs kernel_args(const AttnArgs& a) {
+  KernelArgs k{};
+  k.q = a.q; k.k = a.k; k.v = a.v;
+  k.qs0 = a.qs[0]; k.qs1 = a.qs[1]; k.qs2 = a.qs[2];
+  k.ks0 = a.ks[0]; k.ks1 = a.ks[1]; k.ks2 = a.ks[2];
+  k.vs0 = a.vs[0]; k.vs1 = a.vs[1]; k.vs2 = a.vs[2];
+  k.route_list = a.route_list;
+  k.route_count = a.route_count;
+  k.S_q = a.S_q; k.S_kv = a.S_kv; k.Hq = a.Hq; k.Hkv = a.Hkv; k.K = a.K;
+  k.G = static_cast<int>(a.Hq / a.Hkv);
+  k.scale_log2e = a.scale * kLog2e;
+  k.n_units = a.B * a.S_q * a.Hkv;
+  k.out = a.out;
+  k.lse = a.lse;
+  return k;
+}
+
 template <int D, bool kNarrow>
-hipError_t launch(const AttnArgs& a, hipStream_t stream) {
-  const int64_t n_units = a.B * a.S_q * a.Hkv;
-  const int64_t blocks = (a.B * a.S_q + kWaves - 1) / kWaves * a.Hkv;
-  const float scale_log2e = a.scale * kLog2e;
-  hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves),
-                     0, stream, a.q, a.k, a.v, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0],
-                     a.vs[1], a.vs[2], a.route_list, a.route_count, a.S_q, a.S_kv, a.Hq, a.Hkv, a.K,
-                     static_cast<int>(a.Hq / a.Hkv), scale_log2e, n_units, a.out, a.lse);
-  return hipGetLastError();
+hipError_t launch(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& w, hipStream_t stream) {
+  KernelArgs k = kernel_args(a);
+  const int64_t rows = a.B * a.S_q;
+  if (!plan.use) {
+    const int64_t blocks = (rows + kWaves - 1) / kWaves * a.Hkv;
+    hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow, false>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(64 * kWaves), 0, stream, k);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(range_offsets_kernel, dim3(static_cast<uint32_t>((rows + kWaves - 1) / kWaves)),
+                     dim3(64 * kWaves), 0, stream, a.route_list, a.route_count, rows, a.K, a.S_kv, plan.w_shift,
+                     plan.P, w.offs);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  k.offs = w.offs;
+  k.P = plan.P;
+  k.part_o = w.part_o;
+  k.part_lse = w.part_lse;
+  for (int64_t r0 = 0; r0 < rows; r0 += w.pass_rows) {
+    k.row0 = r0;
+    k.pass_rows = std::min(w.pass_rows, rows - r0);
+    k.rowgroups = (k.pass_rows + kWaves - 1) / kWaves;
+    const int64_t blocks = k.rowgroups * plan.P * a.Hkv;
+    hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow, true>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(64 * kWaves), 0, stream, k);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const int64_t units = k.pass_rows * a.Hkv;
+    hipLaunchKernelGGL((range_combine_kernel<D>), dim3(static_cast<uint32_t>((units + kWaves - 1) / kWaves)),
+                       dim3(64 * kWaves), 0, stream, k);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // True when (S_kv - 1) * row stride + one row fits in 32 bits for both K and V.
@@ -258,17 +477,39 @@ bool narrow_offsets(const AttnArgs& a) {
 }
 
 template <int D>
-hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
-  return narrow_offsets(a) ? launch<D, true>(a, stream) : launch<D, false>(a, stream);
+hipError_t launch_d(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& w, hipStream_t stream) {
+  return narrow_offsets(a) ? launch<D, true>(a, plan, w, stream) : launch<D, false>(a, plan, w, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gather_attention(const AttnArgs& a, hipStream_t stream) {
+SplitPlan split_plan(int64_t rows, int64_t S_kv, int64_t Hq, int64_t D) {
+  SplitPlan plan;
+  int w_shift = 0;
+  while ((int64_t{2} << w_shift) * 4 * D <= kRangeBytes) ++w_shift;  // largest W with W * 4D <= kRangeBytes
+  while ((S_kv + (int64_t{1} << w_shift) - 1) >> w_shift > kMaxRanges) ++w_shift;
+  plan.w_shift = w_shift;
+  plan.P = static_cast<int>((S_kv + (int64_t{1} << w_shift) - 1) >> w_shift);
+  plan.use = plan.P >= 2;
+  if (plan.use) {
+    plan.offs_bytes = (rows * (plan.P + 1) * 4 + 255) / 256 * 256;
+    plan.part_o_row_bytes = Hq * plan.P * 2 * D;
+    plan.part_lse_row_bytes = Hq * plan.P * 4;
+  }
+  return plan;
+}
+
+int64_t split_workspace_bytes(const SplitPlan& plan, int64_t pass_rows) {
+  auto r256 = [](int64_t x) { return (x + 255) / 256 * 256; };
+  return plan.offs_bytes + r256(pass_rows * plan.part_o_row_bytes) + r256(pass_rows * plan.part_lse_row_bytes);
+}
+
+hipError_t launch_gather_attention(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& w,
+                                   hipStream_t stream) {
   switch (a.D) {
-    case 64: return launch_d<64>(a, stream);
-    case 128: return launch_d<128>(a, stream);
-    case 256: return launch_d<256>(a, stream);
+    case 64: return launch_d<64>(a, plan, w, stream);
+    case 128: return launch_d<128>(a, plan, w, stream);
+    case 256: return launch_d<256>(a, plan, w, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -120,12 +120,57 @@ QSA_EXPORT const char* qsa_status_string(int status) {
   }
 }
 
-QSA_EXPORT size_t qsa_forward_workspace_size(int64_t B, int64_t S_q, int64_t K) {
+namespace {
+
+constexpr int64_t kPassRowsDefault = 16384;  // rows per pass of the key-range split at the recommended size
+
+// The attention's key-range split for these shapes; false when a size is out of range.
+bool attention_plan(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,
+                    qsa::SplitPlan* plan) {
+  int64_t rows = 0, tmp = 0;
+  if (B < 1 || S_q < 1 || S_kv < 1 || Hq < 1 || Hkv < 1 || K < 1) return false;
+  if (D != 64 && D != 128 && D != 256) return false;
+  if (!mul_ok(B, S_q, &rows) || rows > kMaxGrid || S_kv > kMaxKv || Hq % Hkv != 0 || Hq / Hkv > QSA_MAX_GROUP)
+    return false;
+  *plan = qsa::split_plan(rows, S_kv, Hq, D);
+  if (plan->use && (!mul_ok(rows, plan->P + 1, &tmp) || !mul_ok(Hq, plan->P * 2 * D, &tmp))) return false;
+  return true;
+}
+
+// Rows per pass that fit `bytes` of split workspace (every row when they all fit), or 0 when fewer than
+// min(rows, kMinPassRows) fit.
+int64_t split_pass_rows(const qsa::SplitPlan& plan, int64_t rows, int64_t Hkv, size_t bytes) {
+  const int64_t per_row = plan.part_o_row_bytes + plan.part_lse_row_bytes;
+  const int64_t fixed = plan.offs_bytes + 2 * static_cast<int64_t>(kWorkspaceAlign);
+  if (bytes < static_cast<size_t>(fixed)) return 0;
+  int64_t pass = std::min<int64_t>(rows, static_cast<int64_t>((bytes - fixed) / per_row));
+  pass = std::min(pass, kMaxGrid / (plan.P * Hkv) * 4);  // split grid: ceil(pass / 4) * P * Hkv workgroups
+  if (pass < rows) pass = pass / 4 * 4;
+  return pass >= std::min(rows, qsa::kMinPassRows) ? pass : 0;
+}
+
+size_t attention_ws(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K) {
+  qsa::SplitPlan plan;
+  if (!attention_plan(B, S_q, S_kv, Hq, Hkv, D, K, &plan) || !plan.use) return 0;
+  const int64_t rows = B * S_q;
+  return static_cast<size_t>(qsa::split_workspace_bytes(plan, std::min(rows, kPassRowsDefault)));
+}
+
+}  // namespace
+
+QSA_EXPORT size_t qsa_attention_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv,
+                                               int64_t D, int64_t K) {
+  return attention_ws(B, S_q, S_kv, Hq, Hkv, D, K);
+}
+
+QSA_EXPORT size_t qsa_forward_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv,
+                                             int64_t D, int64_t K) {
   Sizes s;
-  if (B < 1 || S_q < 1 || K < 1) return 0;
+  qsa::SplitPlan plan;
+  if (!attention_plan(B, S_q, S_kv, Hq, Hkv, D, K, &plan)) return 0;
   if (!mul_ok(B, S_q, &s.rows) || !mul_ok(s.rows, K, &s.list) || s.list > (INT64_MAX >> 3)) return 0;
   return round_up(static_cast<size_t>(4 * s.list), kWorkspaceAlign) +
-         round_up(static_cast<size_t>(4 * s.rows), kWorkspaceAlign);
+         round_up(static_cast<size_t>(4 * s.rows), kWorkspaceAlign) + attention_ws(B, S_q, S_kv, Hq, Hkv, D, K);
 }
 
 QSA_EXPORT int qsa_preprocess(const void* routes, int routes_dtype, int64_t B, int64_t S_q, int64_t K,
@@ -255,6 +300,33 @@ qsa::AttnArgs attn_args(const void* q, const int64_t q_strides[4], const void* k
   return a;
 }
 
+// Plans the key-range split, checks the workspace for it and launches the attention.
+int run_attention(const qsa::AttnArgs& a, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  qsa::SplitPlan plan;
+  if (!attention_plan(a.B, a.S_q, a.S_kv, a.Hq, a.Hkv, a.D, a.K, &plan)) return QSA_ERR_LIMIT;
+  qsa::SplitBuffers w{};
+  if (plan.use) {
+    const int64_t rows = a.B * a.S_q;
+    if (workspace == nullptr || !aligned(workspace, kWorkspaceAlign)) return QSA_ERR_WORKSPACE;
+    w.pass_rows = split_pass_rows(plan, rows, a.Hkv, workspace_bytes);
+    if (w.pass_rows == 0) return QSA_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    w.offs = reinterpret_cast<int32_t*>(ws);
+    w.part_o = reinterpret_cast<uint16_t*>(ws + plan.offs_bytes);
+    w.part_lse = reinterpret_cast<float*>(
+        ws + plan.offs_bytes + round_up(static_cast<size_t>(w.pass_rows * plan.part_o_row_bytes), kWorkspaceAlign));
+  }
+  return hip_status(qsa::launch_gather_attention(a, plan, w, stream));
+}
+
+// Bytes of the attention workspace a call uses (what the aliasing checks cover).
+size_t attention_ws_used(const qsa::AttnArgs& a, size_t workspace_bytes) {
+  qsa::SplitPlan plan;
+  if (!attention_plan(a.B, a.S_q, a.S_kv, a.Hq, a.Hkv, a.D, a.K, &plan) || !plan.use) return 0;
+  const int64_t pass = split_pass_rows(plan, a.B * a.S_q, a.Hkv, workspace_bytes);
+  return pass > 0 ? static_cast<size_t>(qsa::split_workspace_bytes(plan, pass)) : 0;
+}
+
 }  // namespace
 
 QSA_EXPORT int qsa_forward(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
@@ -271,35 +343,45 @@ QSA_EXPORT int qsa_forward(const void* q, const int64_t q_strides[4], const void
   if (routes_dtype != QSA_INT32 && routes_dtype != QSA_INT64) return QSA_ERR_ROUTE_DTYPE;
   const int64_t relem = routes_dtype == QSA_INT64 ? 8 : 4;
   if (!aligned(routes, relem)) return QSA_ERR_LAYOUT;
-  if (workspace == nullptr) return QSA_ERR_WORKSPACE;
-  const size_t need = qsa_forward_workspace_size(B, S_q, K);
-  if (need == 0 || workspace_bytes < need || !aligned(workspace, kWorkspaceAlign)) return QSA_ERR_WORKSPACE;
-  const int64_t rshape[3] = {B, S_q, K};
-  Range r_in;
-  if (!extent(routes, rshape, route_strides, 3, relem, &r_in)) return QSA_ERR_LIMIT;
-  const Range r_ws = dense(workspace, static_cast<int64_t>(need));
-  if (overlap(r_out, r_in) || overlap(r_out, r_ws) || overlap(r_ws, r_q) || overlap(r_ws, r_k) ||
-      overlap(r_ws, r_v) || overlap(r_ws, r_in))
-    return QSA_ERR_ALIAS;
-
+  if (workspace == nullptr || !aligned(workspace, kWorkspaceAlign)) return QSA_ERR_WORKSPACE;
+  // the lists and counts first, then the attention's own workspace
+  const size_t lists = round_up(static_cast<size_t>(s.list_bytes), kWorkspaceAlign) +
+                       round_up(static_cast<size_t>(s.count_bytes), kWorkspaceAlign);
+  if (workspace_bytes < lists) return QSA_ERR_WORKSPACE;
   int32_t* list = static_cast<int32_t*>(workspace);
   int32_t* count = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                               round_up(static_cast<size_t>(s.list_bytes), kWorkspaceAlign));
+  const qsa::AttnArgs a =
+      attn_args(q, q_strides, k, k_strides, v, v_strides, list, count, B, S_q, S_kv, Hq, Hkv, D, K, scale, out);
+  void* att_ws = static_cast<char*>(workspace) + lists;
+  const size_t att_bytes = workspace_bytes - lists;
+  const int64_t rshape[3] = {B, S_q, K};
+  Range r_in;
+  if (!extent(routes, rshape, route_strides, 3, relem, &r_in)) return QSA_ERR_LIMIT;
+  const Range r_ws = dense(workspace, static_cast<int64_t>(lists + attention_ws_used(a, att_bytes)));
+  if (overlap(r_out, r_in) || overlap(r_out, r_ws) || overlap(r_ws, r_q) || overlap(r_ws, r_k) ||
+      overlap(r_ws, r_v) || overlap(r_ws, r_in))
+    return QSA_ERR_ALIAS;
+  {  // the split's workspace is checked before anything is enqueued
+    qsa::SplitPlan plan;
+    if (!attention_plan(B, S_q, S_kv, Hq, Hkv, D, K, &plan)) return QSA_ERR_LIMIT;
+    if (plan.use && split_pass_rows(plan, s.rows, Hkv, att_bytes) == 0) return QSA_ERR_WORKSPACE;
+  }
+
   (void)hipGetLastError();
   hipStream_t st = as_stream(stream);
   int rc = hip_status(qsa::launch_route_normalize(routes, routes_dtype == QSA_INT64, B, S_q, K, route_strides,
                                                   S_kv, list, count, nullptr, 0, st));
   if (rc != QSA_OK) return rc;
-  const qsa::AttnArgs a =
-      attn_args(q, q_strides, k, k_strides, v, v_strides, list, count, B, S_q, S_kv, Hq, Hkv, D, K, scale, out);
-  return hip_status(qsa::launch_gather_attention(a, st));
+  return run_attention(a, att_ws, att_bytes, st);
 }
 
 QSA_EXPORT int qsa_forward_preprocessed(const void* q, const int64_t q_strides[4], const void* k,
                                         const int64_t k_strides[4], const void* v, const int64_t v_strides[4],
                                         const int32_t* route_list, const int32_t* route_count, int64_t B,
                                         int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,
-                                        float scale, void* out, float* lse, void* stream) {
+                                        float scale, void* out, float* lse, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
   Sizes s;
   Range r_q, r_k, r_v, r_out;
   if (int st = check_attention(q, q_strides, k, k_strides, v, v_strides, B, S_q, S_kv, Hq, Hkv, D, K, scale,
@@ -316,10 +398,18 @@ QSA_EXPORT int qsa_forward_preprocessed(const void* q, const int64_t q_strides[4
         overlap(r_lse, r_list) || overlap(r_lse, r_count))
       return QSA_ERR_ALIAS;
   }
-  (void)hipGetLastError();
   const qsa::AttnArgs a = attn_args(q, q_strides, k, k_strides, v, v_strides, route_list, route_count, B, S_q,
                                     S_kv, Hq, Hkv, D, K, scale, out, lse);
-  return hip_status(qsa::launch_gather_attention(a, as_stream(stream)));
+  const size_t used = workspace != nullptr ? attention_ws_used(a, workspace_bytes) : 0;
+  if (used > 0) {
+    const Range r_ws = dense(workspace, static_cast<int64_t>(used));
+    const Range r_lse = lse != nullptr ? dense(lse, 4 * s.rows * Hq) : Range{};
+    if (overlap(r_ws, r_out) || overlap(r_ws, r_q) || overlap(r_ws, r_k) || overlap(r_ws, r_v) ||
+        overlap(r_ws, r_list) || overlap(r_ws, r_count) || overlap(r_ws, r_lse))
+      return QSA_ERR_ALIAS;
+  }
+  (void)hipGetLastError();
+  return run_attention(a, workspace, workspace_bytes, as_stream(stream));
 }
 
 namespace {

@@ -44,8 +44,43 @@ struct AttnArgs {
   float* lse;  // nullable: [B*S_q*Hq] natural-log log-sum-exp
 };
 
-// Fused gather-attention over compacted lists.
-hipError_t launch_gather_attention(const AttnArgs& a, hipStream_t stream);
+// Key-range split of the attention (used when one KV head's K and V rows
+// exceed what one XCD's L2 holds): each row's sorted list is cut at
+// multiples of W = 2^w_shift key IDs into P ranges; the workgroups take the
+// ranges one after another for all rows of a pass, so every XCD's L2 holds
+// one range at a time; rows with routes in several ranges get one partial
+// result per range, merged by a combine pass.
+constexpr int64_t kRangeBytes = int64_t{4} << 20;  // K + V bytes of one KV head's range
+constexpr int kMaxRanges = 63;                      // ranges per row (one wavefront lane each, plus the end)
+constexpr int64_t kMinPassRows = 256;               // smallest pass the workspace must hold
+
+struct SplitPlan {
+  bool use = false;
+  int w_shift = 0;   // range width W = 2^w_shift key IDs
+  int P = 1;         // ranges: ceil(S_kv / W) <= kMaxRanges
+  int64_t offs_bytes = 0;          // [rows][P + 1] int32 range starts (256-B aligned size)
+  int64_t part_o_row_bytes = 0;    // partial outputs of one query row: Hq * P * D bf16
+  int64_t part_lse_row_bytes = 0;  // their log2-sum-exps: Hq * P fp32
+};
+
+SplitPlan split_plan(int64_t rows, int64_t S_kv, int64_t Hq, int64_t D);
+
+// Workspace of a split attention: range starts, then for each pass row the
+// partial outputs [Hkv][P][G][D] bf16 and their log2-sum-exps [Hkv][P][G] fp32.
+struct SplitBuffers {
+  int32_t* offs;
+  uint16_t* part_o;
+  float* part_lse;
+  int64_t pass_rows;  // rows per pass (a multiple of 4, or every row)
+};
+
+// Bytes of split workspace for passes of pass_rows rows (plan.use must hold).
+int64_t split_workspace_bytes(const SplitPlan& plan, int64_t pass_rows);
+
+// Fused gather-attention over compacted lists; with plan.use, the range
+// starts, then per pass the split attention and the combine.
+hipError_t launch_gather_attention(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& w,
+                                   hipStream_t stream);
 
 // Key segments (route lists regrouped by 64-key tile, rows ascending) and
 // their split into parts for the key-side backward kernel.

@@ -29,6 +29,7 @@ def _declared_constants():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "qsa_preprocess", "qsa_forward", "qsa_forward_preprocessed", "qsa_forward_workspace_size",
+        "qsa_attention_workspace_size",
         "qsa_backward", "qsa_backward_workspace_size", "qsa_tile_lists", "qsa_status_string",
         "qsa_select_token_ids", "qsa_select_workspace_size", "qsa_select_chunk_workspace_size"])
 
@@ -54,11 +55,47 @@ def test_status_strings():
 
 
 def test_workspace_size():
-    ws = qsa.qsa_forward_workspace_size
-    assert ws(2, 4096, 512) == 4 * 2 * 4096 * 512 + 4 * 2 * 4096
-    assert ws(1, 3, 5) == 256 + 256  # lists and counts each rounded to 256 bytes
-    assert ws(0, 10, 10) == 0 and ws(1, 1, 0) == 0
-    assert ws(1 << 40, 1 << 40, 1) == 0  # overflow
+    ws, att = qsa.qsa_forward_workspace_size, qsa.qsa_attention_workspace_size
+    # key ranges within one XCD's L2 (S_kv * 4 * D <= 4 MiB): lists and counts only
+    assert att(2, 4096, 4096, 16, 2, 256, 512) == 0
+    assert ws(2, 4096, 4096, 16, 2, 256, 512) == 4 * 2 * 4096 * 512 + 4 * 2 * 4096
+    assert ws(1, 3, 9, 2, 1, 64, 5) == 256 + 256  # lists and counts each rounded to 256 bytes
+    assert att(1, 10, 16384, 4, 1, 64, 8) == 0     # 16384 * 4 * 64 = 4 MiB
+    for bad in ((0, 10, 9, 2, 1, 64, 10), (1, 1, 9, 2, 1, 64, 0), (1, 1, 9, 2, 1, 96, 4), (1, 1, 9, 3, 2, 64, 4)):
+        assert ws(*bad) == 0 and att(*bad) == 0
+    assert ws(1 << 40, 1 << 40, 9, 2, 1, 64, 1) == 0  # overflow
+
+
+def _split_bytes(rows, S_kv, Hq, D, pass_rows):
+    """The layout of the attention workspace as include/qsa.h documents it."""
+    r256 = lambda x: -(-x // 256) * 256
+    W = 1
+    while 2 * W * 4 * D <= 4 << 20:
+        W *= 2
+    while -(-S_kv // W) > 63:
+        W *= 2
+    P = -(-S_kv // W)
+    return P, r256(4 * rows * (P + 1)) + r256(2 * pass_rows * Hq * P * D) + r256(4 * pass_rows * Hq * P)
+
+
+def test_attention_workspace_size():
+    att, fwd = qsa.qsa_attention_workspace_size, qsa.qsa_forward_workspace_size
+    cases = [  # (B, S_q, S_kv, Hq, Hkv, D, K): expected ranges
+        ((1, 65536, 65536, 16, 2, 256, 2048), 16),   # W = 4096
+        ((1, 8192, 32768, 16, 2, 256, 2048), 8),
+        ((1, 16384, 16384, 16, 2, 256, 1024), 4),
+        ((2, 100, 4097, 4, 1, 256, 64), 2),          # one key past a range
+        ((1, 50, 20000, 8, 2, 128, 300), 3),         # W = 8192
+        ((1, 30, 40000, 4, 2, 64, 300), 3),          # W = 16384
+        ((1, 10, 1 << 31, 4, 2, 256, 64), 32),       # W doubled until at most 63 ranges: 2^26
+    ]
+    for (B, S_q, S_kv, Hq, Hkv, D, K), P in cases:
+        rows = B * S_q
+        got_P, want = _split_bytes(rows, S_kv, Hq, D, min(rows, 16384))
+        assert got_P == P
+        assert att(B, S_q, S_kv, Hq, Hkv, D, K) == want, (B, S_q, S_kv)
+        lists = -(-4 * rows * K // 256) * 256 + -(-4 * rows // 256) * 256
+        assert fwd(B, S_q, S_kv, Hq, Hkv, D, K) == lists + want
 
 
 def _call_forward(B=1, S_q=4, S_kv=4, Hq=2, Hkv=1, D=64, K=2, scale=0.1, null_routes=False):

@@ -38,7 +38,8 @@ def _raw_forward(q, k, v, r, *, dims=None, scale=0.125, out=None, ws=None, ws_by
         B, S_q, S_kv, Hq, Hkv, D, K = dims
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    need = qsa.qsa_forward_workspace_size(q.shape[0], q.shape[1], r.shape[2])
+    need = qsa.qsa_forward_workspace_size(q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2], q.shape[3],
+                                          r.shape[2])
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = lambda t: (ctypes.c_int64 * t.dim())(*t.stride())
@@ -94,7 +95,7 @@ def test_empty_dims():
 
 def test_workspace_too_small_or_missing():
     q, k, v, r = _inputs()
-    need = qsa.qsa_forward_workspace_size(1, 8, 4)
+    need = qsa.qsa_forward_workspace_size(1, 8, 16, 4, 2, 64, 4)
     assert _raw_forward(q, k, v, r, ws_bytes=need - 1) == ERR["WORKSPACE"]
 
 

@@ -91,7 +91,7 @@ def _forward(q, kl: KVLayout, vl: KVLayout, lst, cnt, shape, scale, lse=None):
     st = qsa.lib().qsa_forward_preprocessed(
         _p(q.data_ptr()), _strides(q.stride()), _p(kl.ptr), _strides(kl.strides), _p(vl.ptr), _strides(vl.strides),
         _p(lst.data_ptr()), _p(cnt.data_ptr()), B, S_q, S_kv, Hq, Hkv, D, K, ctypes.c_float(scale),
-        _p(out.data_ptr()), _p(lse.data_ptr()) if lse is not None else None, None)
+        _p(out.data_ptr()), _p(lse.data_ptr()) if lse is not None else None, None, 0, None)
     assert st == 0, qsa.qsa_status_string(st)
     return out
 

@@ -131,6 +131,23 @@ def random_dout(seed: int, shape) -> np.ndarray:
     return float32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
 
 
+def random_windowed_routes(seed: int, B: int, S_q: int, S_kv: int, K: int, p_invalid: float = 0.1,
+                           p_empty: float = 0.05) -> np.ndarray:
+    """int64 routes [B,S_q,K] whose valid IDs lie in one window per row: the window's width is drawn
+    log-uniformly from [1, S_kv] and its start uniformly, so rows range from a few neighbouring keys
+    to the whole key range; then invalid slots (-1, S_kv, 2**40), and a fraction of empty rows.
+    Repeats come from drawing with replacement."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    width = np.exp(rng.uniform(0.0, np.log(S_kv), size=(B, S_q))).astype(np.int64).clip(1, S_kv)
+    start = (rng.random((B, S_q)) * (S_kv - width + 1)).astype(np.int64)
+    routes = start[:, :, None] + (rng.random((B, S_q, K)) * width[:, :, None]).astype(np.int64)
+    bad = rng.random((B, S_q, K)) < p_invalid
+    pool = np.array([-1, S_kv, 1 << 40], dtype=np.int64)
+    routes[bad] = pool[rng.integers(0, pool.size, size=int(bad.sum()))]
+    routes[rng.random((B, S_q)) < p_empty] = -1
+    return routes
+
+
 # --------------------------------------------------------------------------
 # route recipes
 # --------------------------------------------------------------------------

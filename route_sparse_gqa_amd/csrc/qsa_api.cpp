@@ -140,12 +140,13 @@ bool attention_plan(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hk
 // Rows per pass that fit `bytes` of split workspace (every row when they all fit), or 0 when fewer than
 // min(rows, kMinPassRows) fit.
 int64_t split_pass_rows(const qsa::SplitPlan& plan, int64_t rows, int64_t Hkv, size_t bytes) {
+  if (bytes < static_cast<size_t>(plan.offs_bytes)) return 0;
+  const int64_t grid_rows = kMaxGrid / (plan.P * Hkv) * 4;  // split grid: ceil(pass / 4) * P * Hkv workgroups
+  auto fits = [&](int64_t pass) { return static_cast<size_t>(qsa::split_workspace_bytes(plan, pass)) <= bytes; };
+  if (rows <= grid_rows && fits(rows)) return rows;
   const int64_t per_row = plan.part_o_row_bytes + plan.part_lse_row_bytes;
-  const int64_t fixed = plan.offs_bytes + 2 * static_cast<int64_t>(kWorkspaceAlign);
-  if (bytes < static_cast<size_t>(fixed)) return 0;
-  int64_t pass = std::min<int64_t>(rows, static_cast<int64_t>((bytes - fixed) / per_row));
-  pass = std::min(pass, kMaxGrid / (plan.P * Hkv) * 4);  // split grid: ceil(pass / 4) * P * Hkv workgroups
-  if (pass < rows) pass = pass / 4 * 4;
+  int64_t pass = std::min(static_cast<int64_t>((bytes - plan.offs_bytes) / per_row), grid_rows) / 4 * 4;
+  while (pass > 0 && !fits(pass)) pass -= 4;  // the 256-byte rounding of each part takes a few rows at most
   return pass >= std::min(rows, qsa::kMinPassRows) ? pass : 0;
 }
 

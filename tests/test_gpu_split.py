@@ -60,6 +60,8 @@ def _case(seed, case):
     B, S_q, S_kv, Hq, Hkv, D, K = case
     q, k, v, _ = random_small_case(seed, B, S_q, S_kv, Hq, Hkv, D, 1)
     r = random_windowed_routes(seed + 1, B, S_q, S_kv, K)
+    r[:, 1::2, 0] = S_kv - 1  # every other row also routes the last key (the last, ragged range)
+    r[:, ::5] = -1  # and every fifth row is empty
     return q, k, v, r
 
 

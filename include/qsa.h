@@ -58,6 +58,8 @@ extern "C" {
 #define QSA_ERR_HIP -12         /* a HIP launch reported an error                      */
 #define QSA_ERR_SELECTION -13   /* token_budget or compress_ratio < 1, or query rows   */
                                 /* outside [0, S_global) (route selection)             */
+#define QSA_ERR_SCRATCH_LIMIT -14 /* qsa_forward_noalloc: the call needs more than its  */
+                                  /* fixed scratch (QSA_NOALLOC_SCRATCH_BYTES)          */
 
 /* ---- constants --------------------------------------------------------- */
 #define QSA_INT32 0          /* routes are int32_t (sign-extended before the checks) */
@@ -68,6 +70,7 @@ extern "C" {
 #define QSA_MAX_SELECT_BLOCKS 4096   /* largest token_budget / compress_ratio          */
 #define QSA_MAX_VISIBLE_BLOCKS 65536 /* largest floor(S_global / compress_ratio)       */
 #define QSA_MAX_INDEX_HEADS 64       /* largest H (index heads) of route selection     */
+#define QSA_NOALLOC_SCRATCH_BYTES (64u << 20) /* device scratch of qsa_forward_noalloc (64 MiB) */
 
 /*
  * qsa_preprocess -- validate, deduplicate and compact the routes; optionally
@@ -199,6 +202,32 @@ int qsa_forward(const void *q, const int64_t q_strides[4], const void *k, const 
                 const int64_t route_strides[3], int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq,
                 int64_t Hkv, int64_t D, int64_t K, float scale, void *out, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/*
+ * qsa_forward_noalloc -- qsa_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid hipMalloc.  It takes no workspace and calls no allocating
+ * routine: its workspace is a device array of QSA_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) built into the library, which each GPU the library runs on holds
+ * until the process ends (its address is looked up on the first call on
+ * each device).
+ *
+ * Arguments, results and errors as for qsa_forward (the same kernels run,
+ * with identical results), except:
+ *   - the call must fit the scratch: the compacted lists and counts
+ *     (4*B*S_q*K + 4*B*S_q bytes, each 256-B aligned) plus, when the
+ *     attention splits its key range, the range starts and one pass of at
+ *     least min(B*S_q, 256) rows (qsa_attention_workspace_size); larger calls
+ *     return QSA_ERR_SCRATCH_LIMIT before anything is enqueued;
+ *   - `stream` must belong to the current device (QSA_ERR_HIP otherwise).
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents: calls that overlap on one GPU (several host threads, or
+ * several streams) race and must be serialised by the caller.
+ */
+int qsa_forward_noalloc(const void *q, const int64_t q_strides[4], const void *k, const int64_t k_strides[4],
+                        const void *v, const int64_t v_strides[4], const void *routes, int routes_dtype,
+                        const int64_t route_strides[3], int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq,
+                        int64_t Hkv, int64_t D, int64_t K, float scale, void *out, void *stream);
 
 /*
  * qsa_forward_preprocessed -- the gather-attention kernel alone, on lists

@@ -11,6 +11,7 @@ runs in the library's HIP kernels; there is no other code path.
 * ``qsa_preprocess(routes, kv_length, membership=False, tile_class=False)``
 * ``qsa_tile_lists(tile_class)``
 * ``qsa_forward(q, k, v, routes, scale=None)``
+* ``qsa_forward_noalloc(q, k, v, routes, scale=None, out=None)`` (no workspace: the library's fixed scratch)
 * ``qsa_forward_preprocessed(q, k, v, route_list, route_count, scale=None, return_lse=False)``
 * ``qsa_backward(q, k, v, out, dout, lse, route_list, route_count, scale=None)``
 * ``qsa_select_token_ids(index_queries, compressed_keys, sequence_lengths, token_budget, compress_ratio,
@@ -39,6 +40,7 @@ QSA_INT32, QSA_INT64 = 0, 1
 TILE = 128
 MAX_ROUTES = 16384
 MAX_GROUP = 16
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # argument-error statuses raise ValueError; HIP errors raise RuntimeError
 _HIP_ERROR = -12
@@ -78,6 +80,9 @@ def lib() -> ctypes.CDLL:
         L.qsa_forward.argtypes = [p, P64, p, P64, p, P64, p, i32, P64, i64, i64, i64, i64, i64, i64, i64,
                                   ctypes.c_float, p, p, ctypes.c_size_t, p]
         L.qsa_forward.restype = i32
+        L.qsa_forward_noalloc.argtypes = [p, P64, p, P64, p, P64, p, i32, P64, i64, i64, i64, i64, i64, i64, i64,
+                                          ctypes.c_float, p, p]
+        L.qsa_forward_noalloc.restype = i32
         L.qsa_forward_preprocessed.argtypes = [p, P64, p, P64, p, P64, p, p, i64, i64, i64, i64, i64, i64, i64,
                                                ctypes.c_float, p, p, p, ctypes.c_size_t, p]
         L.qsa_forward_preprocessed.restype = i32
@@ -281,6 +286,26 @@ def qsa_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, routes: torch
     return out
 
 
+def qsa_forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, routes: torch.Tensor,
+                        scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``qsa_forward`` without a workspace: the library's fixed device scratch (64 MiB per GPU) holds it.
+    For callers that cannot allocate; calls that overlap on one GPU race.  ``out`` is allocated when not
+    given (pass it to allocate nothing here either)."""
+    dev = _require_gpu(q, k, v, routes)
+    q, k, v = _bf16_operand(q, "query"), _bf16_operand(k, "key"), _bf16_operand(v, "value")
+    B, S_q, Hq, D, S_kv, Hkv = _attention_shapes(q, k, v)
+    if routes.dim() != 3 or routes.shape[0] != B or routes.shape[1] != S_q:
+        raise ValueError(f"routes must be [B, S_q, K] = [{B}, {S_q}, K], got {tuple(routes.shape)}")
+    K = routes.shape[2]
+    dt = _route_dtype(routes)
+    out = _output(out, (B, S_q, Hq, D), dev)
+    st = lib().qsa_forward_noalloc(_ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v), _ptr(routes),
+                                   dt, _strides(routes), B, S_q, S_kv, Hq, Hkv, D, K, _scale(scale, D), _ptr(out),
+                                   _stream(dev))
+    _check(st, "qsa_forward_noalloc")
+    return out
+
+
 def _lists(route_list: torch.Tensor, route_count: torch.Tensor, B: int, S_q: int):
     if route_list.dtype != torch.int32 or route_count.dtype != torch.int32:
         raise ValueError("route_list and route_count must be int32")
@@ -411,6 +436,7 @@ __all__ = [
     "qsa_preprocess",
     "qsa_tile_lists",
     "qsa_forward",
+    "qsa_forward_noalloc",
     "qsa_forward_preprocessed",
     "qsa_backward",
     "qsa_forward_workspace_size",

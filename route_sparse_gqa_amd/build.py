@@ -31,6 +31,7 @@ SOURCES = [
     "tile_lists.hip",
     "route_select.hip",
     "qsa_api.cpp",
+    "noalloc.hip",
 ]
 
 COMMON_FLAGS = [

@@ -12,7 +12,7 @@
 #include <algorithm>
 #include <cstring>
 
-#include "../../include/qsa.h"
+#include "qsa.h"
 #include "qsa_internal.h"
 
 #define QSA_EXPORT extern "C" __attribute__((visibility("default")))
@@ -116,6 +116,9 @@ QSA_EXPORT const char* qsa_status_string(int status) {
     case QSA_ERR_SELECTION:
       return "selection arguments out of range (token_budget >= 1, compress_ratio >= 1, "
              "0 <= q_offset, q_offset + S_q <= S_global)";
+    case QSA_ERR_SCRATCH_LIMIT:
+      return "the call needs more scratch than qsa_forward_noalloc's fixed device array holds "
+             "(QSA_NOALLOC_SCRATCH_BYTES); use qsa_forward with a workspace";
     default: return "unknown status";
   }
 }
@@ -330,11 +333,13 @@ size_t attention_ws_used(const qsa::AttnArgs& a, size_t workspace_bytes) {
 
 }  // namespace
 
-QSA_EXPORT int qsa_forward(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
-                           const void* v, const int64_t v_strides[4], const void* routes, int routes_dtype,
-                           const int64_t route_strides[3], int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq,
-                           int64_t Hkv, int64_t D, int64_t K, float scale, void* out, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+namespace qsa {
+
+int forward_entry(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
+                  const void* v, const int64_t v_strides[4], const void* routes, int routes_dtype,
+                  const int64_t route_strides[3], int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv,
+                  int64_t D, int64_t K, float scale, void* out, void* workspace, size_t workspace_bytes,
+                  ScratchFn scratch, void* stream) {
   Sizes s;
   Range r_q, r_k, r_v, r_out;
   if (int st = check_attention(q, q_strides, k, k_strides, v, v_strides, B, S_q, S_kv, Hq, Hkv, D, K, scale,
@@ -344,10 +349,18 @@ QSA_EXPORT int qsa_forward(const void* q, const int64_t q_strides[4], const void
   if (routes_dtype != QSA_INT32 && routes_dtype != QSA_INT64) return QSA_ERR_ROUTE_DTYPE;
   const int64_t relem = routes_dtype == QSA_INT64 ? 8 : 4;
   if (!aligned(routes, relem)) return QSA_ERR_LAYOUT;
-  if (workspace == nullptr || !aligned(workspace, kWorkspaceAlign)) return QSA_ERR_WORKSPACE;
   // the lists and counts first, then the attention's own workspace
   const size_t lists = round_up(static_cast<size_t>(s.list_bytes), kWorkspaceAlign) +
                        round_up(static_cast<size_t>(s.count_bytes), kWorkspaceAlign);
+  qsa::SplitPlan plan;
+  if (!attention_plan(B, S_q, S_kv, Hq, Hkv, D, K, &plan)) return QSA_ERR_LIMIT;
+  if (scratch != nullptr) {  // the caller's fixed scratch replaces the workspace
+    const size_t need = lists + (plan.use ? static_cast<size_t>(qsa::split_workspace_bytes(
+                                                plan, std::min(s.rows, qsa::kMinPassRows)))
+                                          : 0);
+    if (int st = scratch(need, stream, &workspace, &workspace_bytes)) return st;
+  }
+  if (workspace == nullptr || !aligned(workspace, kWorkspaceAlign)) return QSA_ERR_WORKSPACE;
   if (workspace_bytes < lists) return QSA_ERR_WORKSPACE;
   int32_t* list = static_cast<int32_t*>(workspace);
   int32_t* count = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
@@ -363,11 +376,8 @@ QSA_EXPORT int qsa_forward(const void* q, const int64_t q_strides[4], const void
   if (overlap(r_out, r_in) || overlap(r_out, r_ws) || overlap(r_ws, r_q) || overlap(r_ws, r_k) ||
       overlap(r_ws, r_v) || overlap(r_ws, r_in))
     return QSA_ERR_ALIAS;
-  {  // the split's workspace is checked before anything is enqueued
-    qsa::SplitPlan plan;
-    if (!attention_plan(B, S_q, S_kv, Hq, Hkv, D, K, &plan)) return QSA_ERR_LIMIT;
-    if (plan.use && split_pass_rows(plan, s.rows, Hkv, att_bytes) == 0) return QSA_ERR_WORKSPACE;
-  }
+  // the split's workspace is checked before anything is enqueued
+  if (plan.use && split_pass_rows(plan, s.rows, Hkv, att_bytes) == 0) return QSA_ERR_WORKSPACE;
 
   (void)hipGetLastError();
   hipStream_t st = as_stream(stream);
@@ -375,6 +385,17 @@ QSA_EXPORT int qsa_forward(const void* q, const int64_t q_strides[4], const void
                                                   S_kv, list, count, nullptr, 0, st));
   if (rc != QSA_OK) return rc;
   return run_attention(a, att_ws, att_bytes, st);
+}
+
+}  // namespace qsa
+
+QSA_EXPORT int qsa_forward(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
+                           const void* v, const int64_t v_strides[4], const void* routes, int routes_dtype,
+                           const int64_t route_strides[3], int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq,
+                           int64_t Hkv, int64_t D, int64_t K, float scale, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return qsa::forward_entry(q, q_strides, k, k_strides, v, v_strides, routes, routes_dtype, route_strides, B, S_q,
+                            S_kv, Hq, Hkv, D, K, scale, out, workspace, workspace_bytes, nullptr, stream);
 }
 
 QSA_EXPORT int qsa_forward_preprocessed(const void* q, const int64_t q_strides[4], const void* k,

@@ -77,6 +77,17 @@ struct SplitBuffers {
 // Bytes of split workspace for passes of pass_rows rows (plan.use must hold).
 int64_t split_workspace_bytes(const SplitPlan& plan, int64_t pass_rows);
 
+// qsa_forward's checks and launches.  When `scratch` is non-null it is
+// called after the argument checks with the smallest workspace the call can
+// run in (lists plus the split's smallest pass) and the stream, and supplies
+// the workspace pointer and size in place of the arguments (or an error).
+typedef int (*ScratchFn)(size_t need, void* stream, void** workspace, size_t* workspace_bytes);
+int forward_entry(const void* q, const int64_t q_strides[4], const void* k, const int64_t k_strides[4],
+                  const void* v, const int64_t v_strides[4], const void* routes, int routes_dtype,
+                  const int64_t route_strides[3], int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv,
+                  int64_t D, int64_t K, float scale, void* out, void* workspace, size_t workspace_bytes,
+                  ScratchFn scratch, void* stream);
+
 // Fused gather-attention over compacted lists; with plan.use, the range
 // starts, then per pass the split attention and the combine.
 hipError_t launch_gather_attention(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& w,

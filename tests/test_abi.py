@@ -29,7 +29,7 @@ def _declared_constants():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted([
         "qsa_preprocess", "qsa_forward", "qsa_forward_preprocessed", "qsa_forward_workspace_size",
-        "qsa_attention_workspace_size",
+        "qsa_attention_workspace_size", "qsa_forward_noalloc",
         "qsa_backward", "qsa_backward_workspace_size", "qsa_tile_lists", "qsa_status_string",
         "qsa_select_token_ids", "qsa_select_workspace_size", "qsa_select_chunk_workspace_size"])
 
@@ -45,6 +45,9 @@ def test_python_constants_match_header():
     assert c["QSA_INT32"] == qsa.QSA_INT32 and c["QSA_INT64"] == qsa.QSA_INT64
     assert c["QSA_TILE"] == qsa.TILE and c["QSA_MAX_ROUTES"] == qsa.MAX_ROUTES
     assert c["QSA_MAX_GROUP"] == qsa.MAX_GROUP and c["QSA_ERR_HIP"] == qsa._HIP_ERROR
+    text = open(HEADER).read()
+    assert re.search(r"#define\s+QSA_NOALLOC_SCRATCH_BYTES\s+\(64u << 20\)", text)
+    assert qsa.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_status_strings():
@@ -251,3 +254,21 @@ def test_select_host_checks():
     assert _call_select(ws_bytes=16) == -10          # smaller than one 16-row tile of scores
     assert _call_select(misaligned_ws=True) == -10
     assert _call_select(q_row_stride=1 << 60) == -11        # the query tensor's extent overflows 64 bits
+
+
+def test_noalloc_refuses_calls_beyond_its_scratch():
+    """Host checks only: these calls need more than the 64 MiB scratch and return before any HIP call."""
+    L = qsa.lib()
+    fq, fk, fv, fr, fo = (ctypes.c_void_p(n << 32) for n in range(1, 6))  # distinct, never dereferenced
+
+    def call(B, S_q, S_kv, Hq, Hkv, D, K):
+        sq = (ctypes.c_int64 * 4)(S_q * Hq * D, Hq * D, D, 1)
+        sk = (ctypes.c_int64 * 4)(S_kv * Hkv * D, Hkv * D, D, 1)
+        s3 = (ctypes.c_int64 * 3)(S_q * K, K, 1)
+        return L.qsa_forward_noalloc(fq, sq, fk, sk, fv, sk, fr, 1, s3, B, S_q, S_kv, Hq, Hkv, D, K,
+                                     ctypes.c_float(0.1), fo, None)
+
+    assert call(1, 8192, 4096, 16, 2, 256, 2048) == -14   # lists alone are 64 MiB, plus the counts
+    assert call(1, 300, 1 << 20, 16, 2, 256, 64) == -14   # split: 256 rows x 16 heads x 32 ranges x 516 B
+    assert call(1, 300, 1 << 20, 16, 2, 96, 64) == -5     # argument errors come first
+    assert "QSA_NOALLOC_SCRATCH_BYTES" in qsa.qsa_status_string(-14)

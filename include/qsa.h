@@ -140,11 +140,12 @@ int qsa_tile_lists(const int32_t *tile_class, int64_t B, int64_t n_rows, int64_t
  * the attention kernels (qsa_forward_preprocessed), 0 when these shapes need
  * none.
  *
- * When one KV head's K and V rows span more than 4 MiB (S_kv * 4 * D bytes;
- * one XCD's L2), the attention splits each row's ascending route list at
- * multiples of W key IDs, W = the largest power of two with W * 4 * D <=
- * 4 MiB (doubled until P = ceil(S_kv / W) <= 63), and gathers one key range
- * at a time on every XCD.  Its workspace holds, 256-B aligned each:
+ * When one KV head's K and V rows span more than 16 MiB (S_kv * 4 * D
+ * bytes, four times one XCD's L2), the attention splits each row's ascending
+ * route list at multiples of W key IDs, W = the largest power of two with
+ * W * 4 * D <= 4 MiB (doubled until P = ceil(S_kv / W) <= 63; the split
+ * runs when P >= 5), and gathers one key range at a time on every XCD.  Its
+ * workspace holds, 256-B aligned each:
  *   range starts     int32 [B*S_q][P + 1]: for row r, entry p is the first
  *                    list position whose ID lies in range p or later, and
  *                    entry P the row's count;

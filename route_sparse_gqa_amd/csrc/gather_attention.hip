@@ -490,7 +490,10 @@ SplitPlan split_plan(int64_t rows, int64_t S_kv, int64_t Hq, int64_t D) {
   while ((S_kv + (int64_t{1} << w_shift) - 1) >> w_shift > kMaxRanges) ++w_shift;
   plan.w_shift = w_shift;
   plan.P = static_cast<int>((S_kv + (int64_t{1} << w_shift) - 1) >> w_shift);
-  plan.use = plan.P >= 2;
+  // Up to 4 ranges (16 MiB of K and V per KV head) the unsplit kernel, which gives each XCD one KV head,
+  // keeps routes that stay within a document or window in the L2 well enough that the split's extra
+  // work units and partial results cost more than they save (measured on packed THD rows).
+  plan.use = plan.P >= kMinRanges;
   if (plan.use) {
     plan.offs_bytes = (rows * (plan.P + 1) * 4 + 255) / 256 * 256;
     plan.part_o_row_bytes = Hq * plan.P * 2 * D;

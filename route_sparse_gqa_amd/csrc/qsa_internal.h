@@ -51,6 +51,7 @@ struct AttnArgs {
 // one range at a time; rows with routes in several ranges get one partial
 // result per range, merged by a combine pass.
 constexpr int64_t kRangeBytes = int64_t{4} << 20;  // K + V bytes of one KV head's range
+constexpr int kMinRanges = 5;                       // fewer ranges (<= 16 MiB per KV head): no split
 constexpr int kMaxRanges = 63;                      // ranges per row (one wavefront lane each, plus the end)
 constexpr int64_t kMinPassRows = 256;               // smallest pass the workspace must hold
 

@@ -63,7 +63,8 @@ def test_workspace_size():
     assert att(2, 4096, 4096, 16, 2, 256, 512) == 0
     assert ws(2, 4096, 4096, 16, 2, 256, 512) == 4 * 2 * 4096 * 512 + 4 * 2 * 4096
     assert ws(1, 3, 9, 2, 1, 64, 5) == 256 + 256  # lists and counts each rounded to 256 bytes
-    assert att(1, 10, 16384, 4, 1, 64, 8) == 0     # 16384 * 4 * 64 = 4 MiB
+    assert att(1, 10, 65536, 4, 1, 64, 8) == 0     # 65536 * 4 * 64 = 16 MiB: four ranges, no split
+    assert att(1, 16384, 16384, 16, 2, 256, 1024) == 0
     for bad in ((0, 10, 9, 2, 1, 64, 10), (1, 1, 9, 2, 1, 64, 0), (1, 1, 9, 2, 1, 96, 4), (1, 1, 9, 3, 2, 64, 4)):
         assert ws(*bad) == 0 and att(*bad) == 0
     assert ws(1 << 40, 1 << 40, 9, 2, 1, 64, 1) == 0  # overflow
@@ -86,10 +87,9 @@ def test_attention_workspace_size():
     cases = [  # (B, S_q, S_kv, Hq, Hkv, D, K): expected ranges
         ((1, 65536, 65536, 16, 2, 256, 2048), 16),   # W = 4096
         ((1, 8192, 32768, 16, 2, 256, 2048), 8),
-        ((1, 16384, 16384, 16, 2, 256, 1024), 4),
-        ((2, 100, 4097, 4, 1, 256, 64), 2),          # one key past a range
-        ((1, 50, 20000, 8, 2, 128, 300), 3),         # W = 8192
-        ((1, 30, 40000, 4, 2, 64, 300), 3),          # W = 16384
+        ((2, 100, 16385, 4, 1, 256, 64), 5),         # one key past four ranges
+        ((1, 50, 40000, 8, 2, 128, 300), 5),         # W = 8192
+        ((1, 30, 90000, 4, 2, 64, 300), 6),          # W = 16384
         ((1, 10, 1 << 31, 4, 2, 256, 64), 32),       # W doubled until at most 63 ranges: 2^26
     ]
     for (B, S_q, S_kv, Hq, Hkv, D, K), P in cases:

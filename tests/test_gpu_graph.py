@@ -49,7 +49,7 @@ def _attention_inputs(seed, case):
 
 
 @pytest.mark.parametrize("case", [(1, 256, 256, 4, 1, 64, 32), (2, 130, 300, 16, 2, 256, 77),
-                                  (1, 64, 9000, 16, 2, 256, 300)],  # the last one takes the key-range split
+                                  (1, 64, 20000, 16, 2, 256, 300)],  # the last one takes the key-range split
                          ids=lambda c: "B{}_Sq{}_Skv{}_Hq{}_Hkv{}_D{}_K{}".format(*c))
 def test_forward_and_backward_graph_replays_equal_eager(case):
     print(f"graph forward/backward {case}", flush=True)

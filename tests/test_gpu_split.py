@@ -1,6 +1,6 @@
 """GPU parity of the attention's key-range split.
 
-When one KV head's K and V rows exceed 4 MiB (S_kv * 4 * D bytes), the
+When one KV head's K and V rows exceed 16 MiB (S_kv * 4 * D bytes), the
 attention cuts each row's list into key ranges of W IDs, computes one
 partial result per range that holds routes, and merges the partials
 (include/qsa.h, qsa_attention_workspace_size).  Checked here:
@@ -32,12 +32,12 @@ from workloads.generators import random_small_case, random_windowed_routes
 
 pytestmark = pytest.mark.gpu
 
-CASES = [  # (B, S_q, S_kv, Hq, Hkv, D, K): S_kv * 4 * D > 4 MiB
-    (1, 40, 9000, 16, 2, 256, 600),   # W = 4096: 3 ranges, the last ragged
-    (2, 33, 17000, 8, 1, 128, 900),   # W = 8192: 3 ranges
-    (1, 50, 40000, 4, 2, 64, 2000),   # W = 16384: 3 ranges
-    (1, 60, 4097, 16, 2, 256, 40),    # one key past the first range
-    (3, 70, 13000, 12, 3, 256, 300),  # G = 4, 4 ranges
+CASES = [  # (B, S_q, S_kv, Hq, Hkv, D, K): S_kv * 4 * D > 16 MiB
+    (1, 40, 20000, 16, 2, 256, 600),   # W = 4096: 5 ranges, the last ragged
+    (2, 33, 45000, 8, 1, 128, 900),    # W = 8192: 6 ranges
+    (1, 50, 90000, 4, 2, 64, 2000),    # W = 16384: 6 ranges
+    (1, 60, 16385, 16, 2, 256, 40),    # one key past four ranges
+    (3, 70, 26000, 12, 3, 256, 300),   # G = 4, 7 ranges
     (1, 30, 33000, 16, 1, 256, 1500),  # G = 16, 9 ranges
 ]
 
@@ -53,7 +53,7 @@ def _ranges(S_kv: int, D: int):
         W *= 2
     while -(-S_kv // W) > 63:
         W *= 2
-    return W, -(-S_kv // W)
+    return W, -(-S_kv // W)  # the split runs when there are at least 5 ranges
 
 
 def _case(seed, case):
@@ -77,7 +77,7 @@ def _attention(qg, kg, vg, lst, cnt, case, scale, ws_bytes=None, lse=True):
 def test_split_matches_oracle(case):
     B, S_q, S_kv, Hq, Hkv, D, K = case
     W, P = _ranges(S_kv, D)
-    assert P >= 2 and qsa.qsa_attention_workspace_size(*case) > 0
+    assert P >= 5 and qsa.qsa_attention_workspace_size(*case) > 0
     print(f"split forward {case}: W={W} P={P}", flush=True)
     q, k, v, r = _case(3000 + sum(case), case)
     scale = 1.0 / math.sqrt(D)
@@ -101,7 +101,7 @@ def test_split_matches_oracle(case):
 
 
 def test_split_passes_are_bit_identical():
-    case = (2, 700, 9000, 16, 2, 256, 300)
+    case = (2, 700, 20000, 16, 2, 256, 300)
     B, S_q, S_kv, Hq, Hkv, D, K = case
     W, P = _ranges(S_kv, D)
     print(f"split passes {case}", flush=True)
@@ -114,7 +114,7 @@ def test_split_passes_are_bit_identical():
     per_pass = lambda pr: r256(4 * rows * (P + 1)) + r256(2 * pr * Hq * P * D) + r256(4 * pr * Hq * P)
     assert full == per_pass(rows)  # every row fits the recommended size: one pass
     one, lse1, _ = _attention(qg, kg, vg, lst, cnt, case, 0.0625)
-    for pass_rows in (256, 300, 1000):  # 6, 5 and 2 passes
+    for pass_rows in (256, 300, 1000):  # 6, 5 and 2 passes of the 1400 rows
         got, lse2, _ = _attention(qg, kg, vg, lst, cnt, case, 0.0625, ws_bytes=per_pass(pass_rows) + 512)
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), one.view(torch.int16)), f"passes of {pass_rows} rows differ"
@@ -124,7 +124,7 @@ def test_split_passes_are_bit_identical():
 
 
 def test_split_range_start_table():
-    case = (1, 90, 13000, 8, 2, 256, 500)
+    case = (1, 90, 26000, 8, 2, 256, 500)
     B, S_q, S_kv, Hq, Hkv, D, K = case
     W, P = _ranges(S_kv, D)
     q, k, v, r = _case(11, case)
@@ -141,7 +141,7 @@ def test_split_range_start_table():
 
 
 def test_split_workspace_refused():
-    case = (1, 300, 9000, 16, 2, 256, 64)
+    case = (1, 300, 20000, 16, 2, 256, 64)
     B, S_q, S_kv, Hq, Hkv, D, K = case
     q, k, v, r = _case(5, case)
     qg, kg, vg = bf16_to_gpu(q), bf16_to_gpu(k), bf16_to_gpu(v)

@@ -33,8 +33,8 @@ def _raw_noalloc(qg, kg, vg, rg, scale, out):
 
 
 def test_noalloc_matches_qsa_forward_twice():
-    cases = [  # (B, S_q, S_kv, Hq, Hkv, D, K): the split (3 ranges), then a smaller call
-        (2, 500, 9000, 16, 2, 256, 400),
+    cases = [  # (B, S_q, S_kv, Hq, Hkv, D, K): the split (5 ranges), then a smaller call
+        (2, 500, 20000, 16, 2, 256, 400),
         (1, 70, 500, 8, 1, 128, 60),
     ]
     for n, case in enumerate(cases):

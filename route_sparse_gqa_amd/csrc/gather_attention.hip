@@ -407,12 +407,17 @@ __global__ void __launch_bounds__(64 * kWaves)
   int32_t* o = offs + row * (P + 1);
   const int32_t id_max = static_cast<int32_t>(S_kv - 1);
   auto range_of = [&](int32_t id) { return min(max(id, 0), id_max) >> w_shift; };
-  for (int j = lane; j < n; j += 64) {
-    const int r = range_of(lst[j]);
-    const int r_prev = j > 0 ? range_of(lst[j - 1]) : -1;
-    for (int q = r_prev + 1; q <= r; ++q) o[q] = j;
+  int r_carry = -1;  // range of the entry before this 64-entry block (-1 before the first)
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    const int r = j < n ? range_of(lst[j]) : P;  // past the end: the end sentinel, written below
+    const int r_up = __shfl(r, (lane + 63) & 63);
+    const int r_prev = lane == 0 ? r_carry : r_up;  // the previous entry's range, from the lane before
+    if (j < n)
+      for (int q = r_prev + 1; q <= r; ++q) o[q] = j;
+    r_carry = __shfl(r, 63);
   }
-  if (lane == 0) {
+  if (lane == 0) {  // ranges past the last entry start at the end
     const int r_last = n > 0 ? range_of(lst[n - 1]) : -1;
     for (int q = r_last + 1; q <= P; ++q) o[q] = n;
   }

@@ -273,6 +273,10 @@ int qsa_forward_preprocessed(const void *q, const int64_t q_strides[4], const vo
  *   part starts, slots    about 8 * B*T, plus 8 bytes
  *   partial sums          512*D * Hkv * 2*min(P, ceil(B*S_q*min(K, T)/64)),
  *                         P = max(1, 4096 / Hkv)  (at most 1 GiB at D = 256)
+ *   when dq takes the key-range split (the forward's rule, see
+ *   qsa_attention_workspace_size, with Pr ranges):
+ *   range starts          4 * B*S_q*(Pr + 1)
+ *   dq partial sums       4 * R*Hq*Pr*D, R = min(B*S_q, 8192) rows per pass
  * Returns 0 when a size is < 1 or beyond the library's int32 segment
  * indexing (more than 2^31 - 1 segments or chunk prefixes).
  */

@@ -36,6 +36,8 @@
 //    dkdv_reduce_kernel adds in part order.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "qsa_internal.h"
 
@@ -61,79 +63,163 @@ struct Geo {
 // dq (and delta)
 // ---------------------------------------------------------------------------
 
-template <int D, bool kNarrow>
-__global__ void __launch_bounds__(64 * kWaves)
-    dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-              const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, int64_t qs0, int64_t qs1,
-              int64_t qs2, int64_t ks0, int64_t ks1, int64_t ks2, int64_t vs0, int64_t vs1, int64_t vs2,
-              int64_t gs0, int64_t gs1, int64_t gs2, const float* __restrict__ lse,
-              const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count, int64_t S_q,
-              int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t K, int G, float scale_log2e, float scale,
-              int64_t n_rows, uint16_t* __restrict__ dq, float* __restrict__ delta) {
+struct DqArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, gs0, gs1, gs2;
+  const float* lse;
+  const int32_t* route_list;
+  const int32_t* route_count;
+  int64_t S_q, S_kv, Hq, Hkv, K;
+  int G;
+  float scale_log2e, scale;
+  int64_t n_rows;
+  uint16_t* dq;
+  float* delta;
+  // key-range split (as the forward's): range starts, this pass's rows and fp32 partial sums
+  const int32_t* offs;
+  int P;
+  int64_t row0, pass_rows, rowgroups;
+  float* part;  // [pass_rows][Hkv][P][G][D]
+};
+
+// delta = <dO, O> per (row, head), for the split dq kernel (whose units each
+// see only part of a row) and the dk/dv kernel: one wavefront per (row, KV
+// head), lane (c, g) summing dims 32s + 8g .. +7 of head c.
+template <int D>
+__global__ void __launch_bounds__(64 * kWaves) delta_kernel(const DqArgs a) {
+  using Gm = Geo<D>;
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (unit >= a.n_rows * a.Hkv) return;
+  const int64_t row = unit / a.Hkv, hk = unit - row * a.Hkv;
+  const int64_t b = row / a.S_q, i = row - b * a.S_q;
+  const int c = lane & 15, g = lane >> 4;
+  const bool head_ok = c < a.G;
+  const int64_t hq = hk * a.G + (head_ok ? c : 0);
+  const uint16_t* gp = a.dout + b * a.gs0 + i * a.gs1 + hq * a.gs2 + 8 * g;
+  const uint16_t* op = a.o + (row * a.Hq + hq) * D + 8 * g;
+  float dl = 0.f;
+#pragma unroll
+  for (int s = 0; s < Gm::kSteps; ++s) {
+    const u32x4 gw = head_ok ? load16(gp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 ow = head_ok ? load16(op + 32 * s) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dl += bf16_lo(gw[e]) * bf16_lo(ow[e]) + bf16_hi(gw[e]) * bf16_hi(ow[e]);
+  }
+  dl += __shfl_xor(dl, 16);
+  dl += __shfl_xor(dl, 32);
+  if (head_ok && g == 0) a.delta[row * a.Hq + hq] = dl;
+}
+
+// dq over a row's routes (unsplit: one unit per (row, KV head), which also
+// forms delta), or over one key range of them (kSplit: units ordered range by
+// range as in the forward's split, delta from delta_kernel; a unit whose row
+// has routes in no other range writes dq, otherwise an fp32 partial sum that
+// dq_combine_kernel adds in ascending range order).
+template <int D, bool kNarrow, bool kSplit>
+__global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
   using Gm = Geo<D>;
   __shared__ __attribute__((aligned(16))) uint16_t kslab[kWaves][kChunk * Gm::kTrStride];
   __shared__ __attribute__((aligned(16))) uint16_t vslab[kWaves][kChunk * Gm::kRowStride];
 
+  const int64_t S_q = a.S_q, Hq = a.Hq, Hkv = a.Hkv;
+  const int G = a.G;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t x = blockIdx.x;
-  const int64_t hk = x % Hkv;  // one KV head per XCD, as in the forward
-  // Rows from the last to the first, as in the forward: with causal routes the longest start first.
-  const int64_t row = n_rows - 1 - ((x / Hkv) * kWaves + wave);
-  if (row < 0) return;  // the last workgroup's surplus waves; no workgroup barriers in this kernel
+  int64_t hk, row, local = 0;
+  int p = 0;
+  if constexpr (!kSplit) {
+    hk = x % Hkv;  // one KV head per XCD, as in the forward
+    // Rows from the last to the first, as in the forward: with causal routes the longest start first.
+    row = a.n_rows - 1 - ((x / Hkv) * kWaves + wave);
+    if (row < 0) return;  // the last workgroup's surplus waves; no workgroup barriers in this kernel
+  } else {
+    const int64_t phase = x / a.rowgroups;  // (range p, KV head hk), rows last to first
+    p = static_cast<int>(phase / Hkv);
+    hk = phase - static_cast<int64_t>(p) * Hkv;
+    local = a.pass_rows - 1 - ((x - phase * a.rowgroups) * kWaves + wave);
+    if (local < 0) return;
+    row = a.row0 + local;
+  }
   const int64_t b = row / S_q;
   const int64_t i = row % S_q;
   const int c = lane & 15;  // head column (N side); key / dim row within a 16-tile
   const int g = lane >> 4;
   const bool head_ok = c < G;
   const int64_t hq = hk * G + (head_ok ? c : 0);
-  uint16_t* dq_row = dq + (row * Hq + hk * G + c) * D;  // only dereferenced when head_ok
+  uint16_t* dq_row = a.dq + (row * Hq + hk * G + c) * D;  // only dereferenced when head_ok
 
-  const int n = static_cast<int>(min(max(static_cast<int64_t>(route_count[row]), int64_t{0}), K));
+  int first = 0, n;
+  bool direct = true;
+  if constexpr (!kSplit) {
+    n = static_cast<int>(min(max(static_cast<int64_t>(a.route_count[row]), int64_t{0}), a.K));
+  } else {
+    int lo_l, hi_l;
+    const uint64_t parts = range_parts(a.offs + row * (a.P + 1), a.P, a.K, lane, &lo_l, &hi_l);
+    if (((parts >> p) & 1u) == 0) {
+      if (!(parts == 0 && p == 0)) return;  // nothing in this range; an empty row is written once, below
+      n = 0;
+    } else {
+      first = __shfl(lo_l, p);
+      n = __shfl(hi_l, p) - first;
+      direct = __builtin_popcountll(parts) == 1;
+    }
+  }
   if (n == 0) {  // empty route set: zero gradient, nothing reaches dk / dv
     if (head_ok) {
 #pragma unroll
       for (int t = 0; t < Gm::kDimTiles; ++t)
         *reinterpret_cast<u32x2*>(dq_row + 16 * t + 4 * g) = u32x2{0u, 0u};
-      if (g == 0) delta[row * Hq + hk * G + c] = 0.f;
+      if (!kSplit && g == 0) a.delta[row * Hq + hk * G + c] = 0.f;
     }
     return;
   }
 
   // Q^T and dO^T as MFMA B operands: lane (c, g) holds head c, dims 32s + 8g .. +7.
   bf16x8 qf[Gm::kSteps], gf[Gm::kSteps];
-  float dl = 0.f;  // this lane's share of delta = <dO, O> for head c
+  float dl = 0.f;  // delta = <dO, O> for head c
   {
-    const uint16_t* qp = q + b * qs0 + i * qs1 + hq * qs2 + 8 * g;
-    const uint16_t* gp = dout + b * gs0 + i * gs1 + hq * gs2 + 8 * g;
-    const uint16_t* op = o + (row * Hq + hq) * D + 8 * g;
+    const uint16_t* qp = a.q + b * a.qs0 + i * a.qs1 + hq * a.qs2 + 8 * g;
+    const uint16_t* gp = a.dout + b * a.gs0 + i * a.gs1 + hq * a.gs2 + 8 * g;
+    const uint16_t* op = a.o + (row * Hq + hq) * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < Gm::kSteps; ++s) {
       const u32x4 qw = head_ok ? load16(qp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
       const u32x4 gw = head_ok ? load16(gp + 32 * s) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 ow = head_ok ? load16(op + 32 * s) : u32x4{0u, 0u, 0u, 0u};
       qf[s] = __builtin_bit_cast(bf16x8, qw);
       gf[s] = __builtin_bit_cast(bf16x8, gw);
+      if constexpr (!kSplit) {
+        const u32x4 ow = head_ok ? load16(op + 32 * s) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dl += bf16_lo(gw[e]) * bf16_lo(ow[e]) + bf16_hi(gw[e]) * bf16_hi(ow[e]);
+        for (int e = 0; e < 4; ++e) dl += bf16_lo(gw[e]) * bf16_lo(ow[e]) + bf16_hi(gw[e]) * bf16_hi(ow[e]);
+      }
     }
   }
-  dl += __shfl_xor(dl, 16);
-  dl += __shfl_xor(dl, 32);
-  const float lse2 = head_ok ? lse[row * Hq + hq] * kLog2e : 0.f;
-  if (head_ok && g == 0) delta[row * Hq + hq] = dl;
+  if constexpr (!kSplit) {
+    dl += __shfl_xor(dl, 16);
+    dl += __shfl_xor(dl, 32);
+    if (head_ok && g == 0) a.delta[row * Hq + hq] = dl;
+  } else {
+    dl = head_ok ? a.delta[row * Hq + hq] : 0.f;
+  }
+  const float lse2 = head_ok ? a.lse[row * Hq + hq] * kLog2e : 0.f;
 
   f32x4 acc[Gm::kDimTiles];
 #pragma unroll
   for (int t = 0; t < Gm::kDimTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* lst = route_list + row * K;
-  const int64_t ks1b = 2 * ks1, vs1b = 2 * vs1;
-  const char* kb = reinterpret_cast<const char*>(k + b * ks0 + hk * ks2) + 16 * (lane % Gm::kLanesPerRow);
-  const char* vb = reinterpret_cast<const char*>(v + b * vs0 + hk * vs2) + 16 * (lane % Gm::kLanesPerRow);
+  const int32_t* lst = a.route_list + row * a.K + first;
+  const int64_t ks1b = 2 * a.ks1, vs1b = 2 * a.vs1;
+  const char* kb = reinterpret_cast<const char*>(a.k + b * a.ks0 + hk * a.ks2) + 16 * (lane % Gm::kLanesPerRow);
+  const char* vb = reinterpret_cast<const char*>(a.v + b * a.vs0 + hk * a.vs2) + 16 * (lane % Gm::kLanesPerRow);
   uint16_t* my_k = kslab[wave];
   uint16_t* my_v = vslab[wave];
-  const int32_t id_max = static_cast<int32_t>(S_kv - 1);
+  const int32_t id_max = static_cast<int32_t>(a.S_kv - 1);
   auto clamp_id = [&](int32_t xid) { return min(max(xid, 0), id_max); };
   auto load_id = [&](int base) { return lst[min(base + c, n - 1)]; };
   auto load_rows = [&](const char* base, int64_t stride_b, int32_t id, u32x4* r) {
@@ -191,8 +277,8 @@ __global__ void __launch_bounds__(64 * kWaves)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool on = head_ok && base + 4 * g + r < n;
-      const float p = on ? exp2f(st[r] * scale_log2e - lse2) : 0.f;
-      dsb[r] = static_cast<__bf16>(p * (dpt[r] - dl));
+      const float pr = on ? exp2f(st[r] * a.scale_log2e - lse2) : 0.f;
+      dsb[r] = static_cast<__bf16>(pr * (dpt[r] - dl));
     }
     const i16x4 db = __builtin_bit_cast(i16x4, dsb);
 
@@ -205,12 +291,59 @@ __global__ void __launch_bounds__(64 * kWaves)
   }
 
   if (head_ok) {
+    if (direct) {
 #pragma unroll
-    for (int t = 0; t < Gm::kDimTiles; ++t) {
+      for (int t = 0; t < Gm::kDimTiles; ++t) {
+        bf16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = static_cast<__bf16>(acc[t][r] * a.scale);
+        *reinterpret_cast<u32x2*>(dq_row + 16 * t + 4 * g) = __builtin_bit_cast(u32x2, w);
+      }
+    } else {  // fp32 partial sum [G][D] of this range, unscaled
+      float* dst = a.part + (((local * Hkv + hk) * a.P + p) * G + c) * D;
+#pragma unroll
+      for (int t = 0; t < Gm::kDimTiles; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t + 4 * g) = acc[t];
+    }
+  }
+}
+
+// Sums the fp32 partial dq of a row's ranges in ascending range order and
+// writes scale x the sum as bf16: one wavefront per (row, KV head); lane L
+// takes the 4-element pieces L, L + 64, .. of the unit's G x D values.  Rows
+// with routes in at most one range were written by dq_kernel.
+template <int D>
+__global__ void __launch_bounds__(64 * kWaves) dq_combine_kernel(const DqArgs a) {
+  constexpr int kPieces = D / 16;  // pieces per lane at G = 16: 16 * D / 4 / 64
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (unit >= a.pass_rows * a.Hkv) return;
+  const int64_t local = unit / a.Hkv, hk = unit - local * a.Hkv;
+  const int64_t row = a.row0 + local;
+  int lo_l, hi_l;
+  const uint64_t parts = range_parts(a.offs + row * (a.P + 1), a.P, a.K, lane, &lo_l, &hi_l);
+  if (__builtin_popcountll(parts) < 2) return;
+  const int n_pieces = a.G * D / 4;
+  const float* base = a.part + (local * a.Hkv + hk) * a.P * a.G * D;
+  f32x4 acc[kPieces];
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (uint64_t m = parts; m != 0; m &= m - 1) {
+    const float* src = base + static_cast<int64_t>(__builtin_ctzll(m)) * a.G * D;
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const int piece = lane + 64 * k;
+      if (piece < n_pieces) acc[k] += *reinterpret_cast<const f32x4*>(src + 4 * piece);
+    }
+  }
+  uint16_t* dst = a.dq + (row * a.Hq + hk * a.G) * D;
+#pragma unroll
+  for (int k = 0; k < kPieces; ++k) {
+    const int piece = lane + 64 * k;
+    if (piece < n_pieces) {
       bf16x4 w;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = static_cast<__bf16>(acc[t][r] * scale);
-      *reinterpret_cast<u32x2*>(dq_row + 16 * t + 4 * g) = __builtin_bit_cast(u32x2, w);
+      for (int r = 0; r < 4; ++r) w[r] = static_cast<__bf16>(acc[k][r] * a.scale);
+      *reinterpret_cast<u32x2*>(dst + 4 * piece) = __builtin_bit_cast(u32x2, w);
     }
   }
 }
@@ -519,13 +652,50 @@ bool narrow_offsets(const BwdArgs& a) {
 template <int D, bool kNarrow>
 hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = a.B * a.S_q;
-  const int64_t blocks = (rows + kWaves - 1) / kWaves * a.Hkv;
-  hipLaunchKernelGGL((dq_kernel<D, kNarrow>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0, stream,
-                     a.q, a.k, a.v, a.out, a.dout, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0],
-                     a.vs[1], a.vs[2], a.gs[0], a.gs[1], a.gs[2], a.lse, a.route_list, a.route_count, a.S_q, a.S_kv,
-                     a.Hq, a.Hkv, a.K, static_cast<int>(a.Hq / a.Hkv), a.scale * kLog2e, a.scale, rows, a.dq,
-                     a.delta);
-  return hipGetLastError();
+  DqArgs k{};
+  k.q = a.q; k.k = a.k; k.v = a.v; k.o = a.out; k.dout = a.dout;
+  k.qs0 = a.qs[0]; k.qs1 = a.qs[1]; k.qs2 = a.qs[2];
+  k.ks0 = a.ks[0]; k.ks1 = a.ks[1]; k.ks2 = a.ks[2];
+  k.vs0 = a.vs[0]; k.vs1 = a.vs[1]; k.vs2 = a.vs[2];
+  k.gs0 = a.gs[0]; k.gs1 = a.gs[1]; k.gs2 = a.gs[2];
+  k.lse = a.lse;
+  k.route_list = a.route_list;
+  k.route_count = a.route_count;
+  k.S_q = a.S_q; k.S_kv = a.S_kv; k.Hq = a.Hq; k.Hkv = a.Hkv; k.K = a.K;
+  k.G = static_cast<int>(a.Hq / a.Hkv);
+  k.scale_log2e = a.scale * kLog2e;
+  k.scale = a.scale;
+  k.n_rows = rows;
+  k.dq = a.dq;
+  k.delta = a.delta;
+  if (!a.split.use) {
+    const int64_t blocks = (rows + kWaves - 1) / kWaves * a.Hkv;
+    hipLaunchKernelGGL((dq_kernel<D, kNarrow, false>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0,
+                       stream, k);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_range_offsets(a.route_list, a.route_count, rows, a.K, a.S_kv, a.split, a.offs, stream);
+  if (e != hipSuccess) return e;
+  const uint32_t unit_blocks = static_cast<uint32_t>((rows * a.Hkv + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL((delta_kernel<D>), dim3(unit_blocks), dim3(64 * kWaves), 0, stream, k);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  k.offs = a.offs;
+  k.P = a.split.P;
+  k.part = a.dq_part;
+  for (int64_t r0 = 0; r0 < rows; r0 += a.dq_pass_rows) {
+    k.row0 = r0;
+    k.pass_rows = std::min(a.dq_pass_rows, rows - r0);
+    k.rowgroups = (k.pass_rows + kWaves - 1) / kWaves;
+    const int64_t blocks = k.rowgroups * a.split.P * a.Hkv;
+    hipLaunchKernelGGL((dq_kernel<D, kNarrow, true>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0,
+                       stream, k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t units = k.pass_rows * a.Hkv;
+    hipLaunchKernelGGL((dq_combine_kernel<D>), dim3(static_cast<uint32_t>((units + kWaves - 1) / kWaves)),
+                       dim3(64 * kWaves), 0, stream, k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int D>

@@ -84,6 +84,20 @@ struct RowOffset<false> {
   }
 };
 
+// Range starts of one row, one per lane: lane l < P gets its range's part
+// [lo, hi) of the list, clamped into [0, n], n = the row's count clamped into
+// [0, K] (stored at index P); returns the mask of lanes with a non-empty part.
+__device__ __forceinline__ uint64_t range_parts(const int32_t* __restrict__ offs_row, int P, int64_t K, int lane,
+                                                int* lo_out, int* hi_out) {
+  const int32_t o = lane <= P ? offs_row[lane] : 0;
+  const int n = min(max(__shfl(o, P), 0), static_cast<int>(K));
+  const int lo = min(max(o, 0), n);
+  const int hi = min(max(__shfl(o, min(lane + 1, 63)), lo), n);
+  *lo_out = lo;
+  *hi_out = hi;
+  return __ballot(lane < P && lo < hi);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -93,20 +93,6 @@ struct KernelArgs {
   float* part_lse;                     // [pass_rows][Hkv][P][G] fp32, log2 domain
 };
 
-// Range starts of one row, one per lane: lane l < P gets its range's part
-// [lo, hi) of the list, clamped into [0, n], n = the row's count clamped into
-// [0, K] (stored at index P); returns the mask of lanes with a non-empty part.
-__device__ __forceinline__ uint64_t range_parts(const int32_t* __restrict__ offs_row, int P, int64_t K, int lane,
-                                                int* lo_out, int* hi_out) {
-  const int32_t o = lane <= P ? offs_row[lane] : 0;
-  const int n = min(max(__shfl(o, P), 0), static_cast<int>(K));
-  const int lo = min(max(o, 0), n);
-  const int hi = min(max(__shfl(o, min(lane + 1, 63)), lo), n);
-  *lo_out = lo;
-  *hi_out = hi;
-  return __ballot(lane < P && lo < hi);
-}
-
 template <int D, bool kNarrow, bool kSplit>
 __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const KernelArgs a) {
   using Geo = Geometry<D>;
@@ -450,10 +436,9 @@ hipError_t launch(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& 
                        dim3(64 * kWaves), 0, stream, k);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(range_offsets_kernel, dim3(static_cast<uint32_t>((rows + kWaves - 1) / kWaves)),
-                     dim3(64 * kWaves), 0, stream, a.route_list, a.route_count, rows, a.K, a.S_kv, plan.w_shift,
-                     plan.P, w.offs);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (hipError_t e = launch_range_offsets(a.route_list, a.route_count, rows, a.K, a.S_kv, plan, w.offs, stream);
+      e != hipSuccess)
+    return e;
   k.offs = w.offs;
   k.P = plan.P;
   k.part_o = w.part_o;
@@ -487,6 +472,14 @@ hipError_t launch_d(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers
 }
 
 }  // namespace
+
+hipError_t launch_range_offsets(const int32_t* route_list, const int32_t* route_count, int64_t rows, int64_t K,
+                                int64_t S_kv, const SplitPlan& plan, int32_t* offs, hipStream_t stream) {
+  hipLaunchKernelGGL(range_offsets_kernel, dim3(static_cast<uint32_t>((rows + kWaves - 1) / kWaves)),
+                     dim3(64 * kWaves), 0, stream, route_list, route_count, rows, K, S_kv, plan.w_shift, plan.P,
+                     offs);
+  return hipGetLastError();
+}
 
 SplitPlan split_plan(int64_t rows, int64_t S_kv, int64_t Hq, int64_t D) {
   SplitPlan plan;

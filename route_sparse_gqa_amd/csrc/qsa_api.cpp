@@ -440,8 +440,9 @@ namespace {
 // sums of split tiles, each 256-B aligned.
 struct BwdLayout {
   size_t delta = 0, bits = 0, chunk_prefix = 0, totals = 0, tile_start = 0, segs = 0, part_start = 0,
-         slot_start = 0, plan = 0, partial = 0, total = 0;
-  int64_t n_kt = 0, capacity = 0, max_parts = 0;
+         slot_start = 0, plan = 0, partial = 0, offs = 0, dq_part = 0, total = 0;
+  int64_t n_kt = 0, capacity = 0, max_parts = 0, dq_pass_rows = 0;
+  qsa::SplitPlan split;
 };
 
 bool bwd_layout(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K, BwdLayout* l) {
@@ -477,6 +478,15 @@ bool bwd_layout(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, i
   take(&l->slot_start, 4 * tiles);
   take(&l->plan, 8);
   take(&l->partial, partial);
+  // the key-range split of dq (when the forward would split): range starts and one pass of fp32 partial sums
+  l->split = qsa::split_plan(rows, S_kv, Hq, D);
+  if (l->split.use) {
+    int64_t part_bytes = 0;
+    l->dq_pass_rows = rows < qsa::kDqPassRows ? rows : qsa::kDqPassRows;
+    if (!mul_ok(l->dq_pass_rows * Hq, static_cast<int64_t>(l->split.P) * D * 4, &part_bytes)) return false;
+    take(&l->offs, 4 * rows * (l->split.P + 1));
+    take(&l->dq_part, part_bytes);
+  }
   l->total = off;
   return true;
 }
@@ -573,6 +583,10 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
+  a.split = l.split;
+  a.offs = l.split.use ? reinterpret_cast<int32_t*>(ws + l.offs) : nullptr;
+  a.dq_part = l.split.use ? reinterpret_cast<float*>(ws + l.dq_part) : nullptr;
+  a.dq_pass_rows = l.dq_pass_rows;
 
   (void)hipGetLastError();
   hipStream_t st = as_stream(stream);

@@ -89,6 +89,10 @@ int forward_entry(const void* q, const int64_t q_strides[4], const void* k, cons
                   int64_t D, int64_t K, float scale, void* out, void* workspace, size_t workspace_bytes,
                   ScratchFn scratch, void* stream);
 
+// Range starts of each row's list for a split plan: offs [rows][P + 1].
+hipError_t launch_range_offsets(const int32_t* route_list, const int32_t* route_count, int64_t rows, int64_t K,
+                                int64_t S_kv, const SplitPlan& plan, int32_t* offs, hipStream_t stream);
+
 // Fused gather-attention over compacted lists; with plan.use, the range
 // starts, then per pass the split attention and the combine.
 hipError_t launch_gather_attention(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& w,
@@ -140,7 +144,14 @@ struct BwdArgs {
   uint16_t* dq;  // [B, S_q, Hq, D] contiguous
   uint16_t* dk;  // [B, S_kv, Hkv, D] contiguous
   uint16_t* dv;  // [B, S_kv, Hkv, D] contiguous
+  // key-range split of dq (the forward's plan): range starts and fp32 partial sums of one pass
+  SplitPlan split;
+  int32_t* offs;         // [B * S_q][P + 1]
+  float* dq_part;        // [dq_pass_rows][Hkv][P][G][D]
+  int64_t dq_pass_rows;
 };
+
+constexpr int64_t kDqPassRows = 8192;  // rows per pass of the split dq
 
 // dq and delta (one wavefront per (b, i, hk)); then dk and dv (one wavefront
 // workgroup per (part of a 64-key tile, hk)) over the key segments.

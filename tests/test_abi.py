@@ -147,8 +147,12 @@ def _bwd_ws(B, S_q, S_kv, Hq, Hkv, D, K):
     cap = B * S_q * min(K, T)
     P = max(1, 4096 // Hkv)
     slots = 2 * min(P, -(-cap // 64))
-    return (r(4 * B * S_q * Hq) + r(4 * B * n_w * T) + r(4 * B * n_c * T) + r(4 * B * T) + r(4 * (B * T + 1)) +
-            r(16 * cap) + r(4 * (B * T + 1)) + r(4 * B * T) + r(8) + r(512 * D * Hkv * slots))
+    total = (r(4 * B * S_q * Hq) + r(4 * B * n_w * T) + r(4 * B * n_c * T) + r(4 * B * T) + r(4 * (B * T + 1)) +
+             r(16 * cap) + r(4 * (B * T + 1)) + r(4 * B * T) + r(8) + r(512 * D * Hkv * slots))
+    Pr, _ = _split_bytes(B * S_q, S_kv, Hq, D, 0)
+    if Pr >= 5:  # dq's key-range split: range starts, then fp32 partial sums of passes of up to 8192 rows
+        total += r(4 * B * S_q * (Pr + 1)) + r(4 * min(B * S_q, 8192) * Hq * Pr * D)
+    return total
 
 
 def test_backward_workspace_size():
@@ -156,7 +160,8 @@ def test_backward_workspace_size():
     for args in [(2, 4096, 4096, 16, 2, 256, 512), (1, 10, 17, 2, 1, 64, 100), (1, 65536, 65536, 16, 2, 256, 2048),
                  (3, 257, 513, 8, 1, 128, 129)]:
         assert ws(*args) == _bwd_ws(*args), args
-    assert ws(1, 65536, 65536, 16, 2, 256, 2048) < 3 << 30  # long sequences fit in a few GiB
+    assert ws(1, 65536, 65536, 16, 2, 256, 2048) < 6 << 30  # long sequences fit in a few GiB
+    assert ws(1, 8192, 32768, 16, 2, 256, 2048) > ws(1, 8192, 16384, 16, 2, 256, 2048) + (1 << 30)  # split dq
     assert ws(0, 1, 1, 1, 1, 64, 1) == 0 and ws(1, 1, 1, 1, 1, 64, 0) == 0
     assert ws(1, 1 << 21, 1 << 24, 16, 2, 256, 2048) == 0  # more than 2^31 - 1 segments
 

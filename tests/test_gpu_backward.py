@@ -198,6 +198,7 @@ def test_backward_strided_inputs():
 BACKWARD_SAMPLES = {  # workload: (dq row ranges, dk/dv key ranges), every batch row
     "right_padded": ([(0, 128), (2990, 3010), (3968, 4096)], [(2048, 2112), (3968, 4096)]),
     "packed_thd": ([(0, 64), (16000, 16384)], [(16256, 16384)]),
+    "cp_slice": ([(0, 64), (8128, 8192)], [(32704, 32768)]),
     "long_int64": ([(65024, 65536)], [(65472, 65536)]),
 }
 

@@ -166,3 +166,41 @@ def test_split_workspace_refused():
     out = ws[:2 * B * S_q * Hq * D].view(torch.bfloat16)  # the output inside the workspace: refused
     assert call(p(ws), smallest) == -9
     torch.cuda.synchronize()
+
+
+BACKWARD_CASES = [  # (B, S_q, S_kv, Hq, Hkv, D, K): the backward's dq takes the same key-range split
+    (1, 40, 20000, 16, 2, 256, 600),
+    (2, 33, 45000, 8, 1, 128, 900),
+    (1, 50, 90000, 4, 2, 64, 2000),
+    (1, 8200, 16400, 2, 1, 256, 4),   # more than 8192 rows: dq in two passes
+]
+
+
+@pytest.mark.parametrize("case", BACKWARD_CASES, ids=_ids)
+def test_split_backward_matches_oracle(case):
+    from test_gpu_backward import check_grad
+    from workloads import random_dout
+
+    B, S_q, S_kv, Hq, Hkv, D, K = case
+    W, P = _ranges(S_kv, D)
+    assert P >= 5
+    print(f"split backward {case}: W={W} P={P}", flush=True)
+    q, k, v, r = _case(7000 + sum(case), case)
+    dout = random_dout(8000 + sum(case), q.shape)
+    scale = 1.0 / math.sqrt(D)
+    qg, kg, vg, gg = bf16_to_gpu(q), bf16_to_gpu(k), bf16_to_gpu(v), bf16_to_gpu(dout)
+    lst, cnt, _, _ = qsa.qsa_preprocess(torch.from_numpy(r).to(device()), S_kv)
+    out, lse = qsa.qsa_forward_preprocessed(qg, kg, vg, lst, cnt, scale, return_lse=True)
+    dq, dk, dv = qsa.qsa_backward(qg, kg, vg, out, gg, lse, lst, cnt, scale)
+    dq2, dk2, dv2 = qsa.qsa_backward(qg, kg, vg, out, gg, lse, lst, cnt, scale)
+    torch.cuda.synchronize()
+    for a, b2, name in ((dq, dq2, "dq"), (dk, dk2, "dk"), (dv, dv2, "dv")):
+        assert torch.equal(a.view(torch.int16), b2.view(torch.int16)), f"{name} differs between two calls"
+    _, ocnt = oracle.route_lists(r, S_kv)
+    rq, rk, rv = oracle.backward(q, k, v, dout, r, scale)
+    floor = 1e-3 * float(np.abs(rv).max())
+    dq_b = gpu_bf16_bits(dq)
+    check_grad(dq_b, rq, f"split {case} dq", floor)
+    check_grad(gpu_bf16_bits(dk), rk, f"split {case} dk", floor)
+    check_grad(gpu_bf16_bits(dv), rv, f"split {case} dv")
+    assert not np.any(dq_b[ocnt == 0]), "empty rows must have dq exactly +0.0"

@@ -111,3 +111,53 @@ def test_random_shape_preprocess(c):
     np.testing.assert_array_equal(lst.cpu().numpy(), olst)
     np.testing.assert_array_equal(mem.cpu().numpy(), oracle.membership(r, S_kv))
     np.testing.assert_array_equal(tc.cpu().numpy(), oracle.tile_class(r, S_kv))
+
+
+def _draw_split_cases(n: int, seed: int = 20261203):
+    """Shapes whose K/V exceed 16 MiB per KV head (the attention and dq split their key range), with
+    windowed routes so that rows span one, several or all ranges."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for _ in range(n):
+        D = int(rng.choice([64, 128, 256]))
+        W = (4 << 20) // (4 * D)  # keys per range
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.integers(1, 3 if G == 16 else 4))
+        cases.append(dict(
+            B=int(rng.integers(1, 3)), S_q=int(rng.integers(1, 90)), S_kv=int(rng.integers(4 * W + 1, 12 * W)),
+            Hq=G * Hkv, Hkv=Hkv, D=D, K=int(rng.integers(1, 1500)), scale=float(rng.uniform(0.02, 0.3)),
+            seed=int(rng.integers(1, 1 << 30))))
+    return cases
+
+
+SPLIT_CASES = _draw_split_cases(10)
+
+
+def _sid(c):
+    return "B{B}_Sq{S_q}_Skv{S_kv}_Hq{Hq}_Hkv{Hkv}_D{D}_K{K}".format(**c)
+
+
+@pytest.mark.parametrize("c", SPLIT_CASES, ids=_sid)
+def test_random_split_shape_forward_backward(c):
+    from workloads.generators import random_windowed_routes
+
+    B, S_q, S_kv, Hq, Hkv, D, K = (c[x] for x in ("B", "S_q", "S_kv", "Hq", "Hkv", "D", "K"))
+    print(f"random split shape {_sid(c)} scale={c['scale']:.4f}", flush=True)
+    assert qsa.qsa_attention_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K) > 0  # the split runs
+    q, k, v, _ = random_small_case(c["seed"], B, S_q, S_kv, Hq, Hkv, D, 1)
+    r = random_windowed_routes(c["seed"] + 2, B, S_q, S_kv, K)
+    dout = random_dout(c["seed"] + 1, q.shape)
+    scale = c["scale"]
+    qg, kg, vg, gg = bf16_to_gpu(q), bf16_to_gpu(k), bf16_to_gpu(v), bf16_to_gpu(dout)
+    lst, cnt, _, _ = qsa.qsa_preprocess(torch.from_numpy(r).to(device()), S_kv)
+    out, lse = qsa.qsa_forward_preprocessed(qg, kg, vg, lst, cnt, scale, return_lse=True)
+    dq, dk, dv = qsa.qsa_backward(qg, kg, vg, out, gg, lse, lst, cnt, scale)
+    torch.cuda.synchronize()
+    _, ocnt = oracle.route_lists(r, S_kv)
+    check_forward(gpu_bf16_bits(out), oracle.forward(q, k, v, r, scale), ocnt, v, f"split {_sid(c)}")
+    check_lse(lse.cpu().numpy().astype(np.float64), oracle.lse(q, k, r, scale), f"split lse {_sid(c)}")
+    rq, rk, rv = oracle.backward(q, k, v, dout, r, scale)
+    floor = 1e-3 * float(np.abs(rv).max()) if rv.size else 0.0
+    check_grad(gpu_bf16_bits(dq), rq, f"split dq {_sid(c)}", floor)
+    check_grad(gpu_bf16_bits(dk), rk, f"split dk {_sid(c)}", floor)
+    check_grad(gpu_bf16_bits(dv), rv, f"split dv {_sid(c)}")

@@ -393,15 +393,41 @@ __global__ void __launch_bounds__(64 * kWaves)
   int32_t* o = offs + row * (P + 1);
   const int32_t id_max = static_cast<int32_t>(S_kv - 1);
   auto range_of = [&](int32_t id) { return min(max(id, 0), id_max) >> w_shift; };
-  int r_carry = -1;  // range of the entry before this 64-entry block (-1 before the first)
-  for (int j0 = 0; j0 < n; j0 += 64) {
-    const int j = j0 + lane;
-    const int r = j < n ? range_of(lst[j]) : P;  // past the end: the end sentinel, written below
-    const int r_up = __shfl(r, (lane + 63) & 63);
-    const int r_prev = lane == 0 ? r_carry : r_up;  // the previous entry's range, from the lane before
-    if (j < n)
-      for (int q = r_prev + 1; q <= r; ++q) o[q] = j;
-    r_carry = __shfl(r, 63);
+  int r_carry = -1;  // range of the entry before this block (-1 before the first)
+  if ((K & 3) == 0 && (reinterpret_cast<uintptr_t>(route_list) & 15) == 0) {
+    // Every row 16-byte aligned: lane L takes entries 4L .. 4L+3 of each 256-entry block with one load
+    // (in bounds: an entry below n <= K starts a group of four that ends at K - 1 at most).
+    for (int j0 = 0; j0 < n; j0 += 256) {
+      const int j = j0 + 4 * lane;
+      int r[4] = {P, P, P, P};  // past the end: the end sentinel, written below
+      if (j < n) {
+        const u32x4 w = load16(lst + j);
+        const int32_t ids[4] = {static_cast<int32_t>(w.x), static_cast<int32_t>(w.y), static_cast<int32_t>(w.z),
+                                static_cast<int32_t>(w.w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j + e < n) r[e] = range_of(ids[e]);
+      }
+      const int r_up = __shfl(r[3], (lane + 63) & 63);
+      int r_prev = lane == 0 ? r_carry : r_up;  // the previous entry's range, from the lane before
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (j + e < n)
+          for (int q = r_prev + 1; q <= r[e]; ++q) o[q] = j + e;
+        r_prev = r[e];
+      }
+      r_carry = __shfl(r[3], 63);
+    }
+  } else {
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      const int j = j0 + lane;
+      const int r = j < n ? range_of(lst[j]) : P;  // past the end: the end sentinel, written below
+      const int r_up = __shfl(r, (lane + 63) & 63);
+      const int r_prev = lane == 0 ? r_carry : r_up;  // the previous entry's range, from the lane before
+      if (j < n)
+        for (int q = r_prev + 1; q <= r; ++q) o[q] = j;
+      r_carry = __shfl(r, 63);
+    }
   }
   if (lane == 0) {  // ranges past the last entry start at the end
     const int r_last = n > 0 ? range_of(lst[n - 1]) : -1;

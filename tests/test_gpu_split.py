@@ -123,8 +123,9 @@ def test_split_passes_are_bit_identical():
     check_forward(gpu_bf16_bits(one), ref, oracle.route_lists(r, S_kv)[1], v, "split one pass")
 
 
-def test_split_range_start_table():
-    case = (1, 90, 26000, 8, 2, 256, 500)
+@pytest.mark.parametrize("K", [500, 501], ids=["K500_rows16B", "K501_rows4B"])  # one load per 4 entries, or per 1
+def test_split_range_start_table(K):
+    case = (1, 90, 26000, 8, 2, 256, K)
     B, S_q, S_kv, Hq, Hkv, D, K = case
     W, P = _ranges(S_kv, D)
     q, k, v, r = _case(11, case)

@@ -151,10 +151,14 @@ int qsa_tile_lists(const int32_t *tile_class, int64_t B, int64_t n_rows, int64_t
  *                    entry P the row's count;
  *   partial outputs  bf16 [R][Hkv][P][G][D], R = rows per pass;
  *   partial sums     fp32 [R][Hkv][P][G] (log2 of each partial's softmax
- *                    sum against its maximum score, log2 domain).
- * The rows are processed in passes of R rows, R = every row or as many
- * multiples of 4 as fit (at least min(B*S_q, 256)); the recommended size
- * takes R = min(B*S_q, 16384).  Results do not depend on R.
+ *                    sum against its maximum score, log2 domain);
+ *   with more than one pass, a second set of partial outputs and sums
+ *   (each pass's partials are merged while the next pass gathers into the
+ *   other set).
+ * The rows are processed in passes of R rows, from the last rows to the
+ * first: R = every row when one set for all of them fits, else as many
+ * multiples of 4 as two sets fit (at least 256); the recommended size takes
+ * R = min(B*S_q, 16384).  Results do not depend on R.
  * Returns 0 as well when a size is out of range.
  */
 size_t qsa_attention_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D,
@@ -217,9 +221,10 @@ int qsa_forward(const void *q, const int64_t q_strides[4], const void *k, const 
  * with identical results), except:
  *   - the call must fit the scratch: the compacted lists and counts
  *     (4*B*S_q*K + 4*B*S_q bytes, each 256-B aligned) plus, when the
- *     attention splits its key range, the range starts and one pass of at
- *     least min(B*S_q, 256) rows (qsa_attention_workspace_size); larger calls
- *     return QSA_ERR_SCRATCH_LIMIT before anything is enqueued;
+ *     attention splits its key range, the range starts and the partial
+ *     results of its smallest pass (one pass of every row, or two sets of
+ *     256 rows: qsa_attention_workspace_size); larger calls return
+ *     QSA_ERR_SCRATCH_LIMIT before anything is enqueued;
  *   - `stream` must belong to the current device (QSA_ERR_HIP otherwise).
  * Every call on one GPU uses that GPU's one array, which keeps the last
  * call's contents: calls that overlap on one GPU (several host threads, or

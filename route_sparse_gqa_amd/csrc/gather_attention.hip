@@ -42,11 +42,14 @@
 // one W-key range of one KV head (4 MiB of K and V).  A unit whose row has
 // routes in no other range writes the output itself; otherwise it writes
 // its normalised partial output (bf16) and the log2 of its softmax sum
-// against its own maximum, and `range_combine_kernel` merges the partials of
-// the row in ascending range order:
+// against its own maximum, and `combine_unit` merges the partials of the row
+// in ascending range order:
 //   out = sum_p 2^(s_p - M) o_p / sum_p 2^(s_p - M),  M = max_p s_p,
 // which is the softmax over the union of the ranges (the ranges partition
-// the row's route set).
+// the row's route set).  The rows go in passes (partials of one pass in
+// workspace), last rows first; the workgroups merging a pass are spread
+// through the next pass's split launch, which writes the other of two
+// partial buffers, and `range_combine_kernel` merges the last pass.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -91,7 +94,125 @@ struct KernelArgs {
   int64_t row0, pass_rows, rowgroups;  // rows [row0, row0 + pass_rows) of this pass, ceil(pass_rows / 4)
   uint16_t* part_o;                    // [pass_rows][Hkv][P][G][D] bf16
   float* part_lse;                     // [pass_rows][Hkv][P][G] fp32, log2 domain
+  // the pass whose partials are merged (by the combine kernel, or by the
+  // combine workgroups interleaved into the next pass's split launch)
+  int64_t comb_row0, comb_pass_rows;
+  const uint16_t* comb_part_o;
+  const float* comb_part_lse;
+  int64_t comb_blocks, comb_stride;  // split launch: workgroup comb_stride * k - 1 merges units 4(k-1) ..
 };
+
+// Merges the partial results of one (row, KV head) unit of a split pass
+// (one wavefront): lane L takes the 8-element pieces L, L + 64, .. (kP of
+// them) of the unit's G x D outputs.  The unit's ranges are taken in
+// ascending order, kB at a time with all their loads in flight together (16
+// 16-byte loads per lane at D = 256, 4 below: the split kernel then needs no
+// more registers than its gather), and folded into a running sum against
+// the largest log2-sum-exp seen so far:
+//   out = sum_p 2^(s_p - M) o_p / sum_p 2^(s_p - M),  M = max_p s_p.
+// Rows with routes in at most one range were written by the split kernel and
+// are skipped.
+template <int D, int kP>
+__device__ __forceinline__ void combine_unit(const KernelArgs& a, int64_t unit, int lane) {
+  constexpr int kB = (D == 256 ? 16 : 4) / kP;  // ranges per batch
+  const int64_t local = unit / a.Hkv;
+  const int64_t hk = unit - local * a.Hkv;
+  const int64_t row = a.comb_row0 + local;
+  const int G = a.G;
+  int lo_l, hi_l;
+  uint64_t parts = range_parts(a.offs + row * (a.P + 1), a.P, a.K, lane, &lo_l, &hi_l);
+  if (__builtin_popcountll(parts) < 2) return;
+
+  const int n_pieces = G * D / 8;
+  const int64_t u0 = (local * a.Hkv + hk) * a.P;  // partial index of range 0 of this unit
+  float mx[kP], wsum[kP];
+  float acc[kP][8];
+#pragma unroll
+  for (int k = 0; k < kP; ++k) {
+    mx[k] = -INFINITY;
+    wsum[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+  }
+  while (parts != 0) {  // wave-uniform
+    int pr[kB];  // this batch's ranges, ascending; -1 past the unit's last
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      pr[j] = parts != 0 ? __builtin_ctzll(parts) : -1;
+      parts &= parts - 1;
+    }
+    float ls[kB][kP];
+    u32x4 v[kB][kP];
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+#pragma unroll
+      for (int k = 0; k < kP; ++k) {
+        const int piece = lane + 64 * k;
+        if (pr[j] >= 0 && piece < n_pieces) {
+          const int64_t u = u0 + pr[j];
+          ls[j][k] = a.comb_part_lse[u * G + piece * 8 / D];
+          const u32x4* src = reinterpret_cast<const u32x4*>(a.comb_part_o + (u * G * D + piece * 8));
+          v[j][k] = __builtin_nontemporal_load(src);  // read once: streamed
+        }
+      }
+#pragma unroll
+    for (int k = 0; k < kP; ++k) {
+      if (lane + 64 * k >= n_pieces) continue;
+      float bm = ls[0][k];  // pr[0] >= 0: the batch holds at least one range
+#pragma unroll
+      for (int j = 1; j < kB; ++j)
+        if (pr[j] >= 0) bm = fmaxf(bm, ls[j][k]);
+      const float m_new = fmaxf(mx[k], bm);
+      const float alpha = exp2f(mx[k] - m_new);  // 0 on the first batch
+      mx[k] = m_new;
+      wsum[k] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[k][e] *= alpha;
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        if (pr[j] < 0) continue;
+        const float w = exp2f(ls[j][k] - m_new);
+        wsum[k] += w;
+        const uint32_t words[4] = {v[j][k].x, v[j][k].y, v[j][k].z, v[j][k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[k][2 * e] += w * bf16_lo(words[e]);
+          acc[k][2 * e + 1] += w * bf16_hi(words[e]);
+        }
+      }
+    }
+  }
+  uint16_t* out_unit = a.out + (row * a.Hq + hk * G) * D;
+#pragma unroll
+  for (int k = 0; k < kP; ++k) {
+    const int piece = lane + 64 * k;
+    if (piece < n_pieces) {
+      const float inv = 1.0f / wsum[k];
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(acc[k][e] * inv);
+      *reinterpret_cast<u32x4*>(out_unit + piece * 8) = __builtin_bit_cast(u32x4, o);
+      if (a.lse != nullptr && (piece * 8) % D == 0)
+        a.lse[row * a.Hq + hk * G + piece * 8 / D] = (mx[k] + log2f(wsum[k])) * kLn2;
+    }
+  }
+}
+
+// combine_unit with kP = the pieces each lane needs, G * D / 512 rounded up
+// to a power of two (at most D / 32, at G = 16).
+template <int D>
+__device__ __forceinline__ void combine_unit(const KernelArgs& a, int64_t unit, int lane) {
+  if (unit >= a.comb_pass_rows * a.Hkv) return;
+  const int per_lane = (a.G * D / 8 + 63) / 64;
+  if constexpr (D / 32 >= 8) {
+    if (per_lane > 4) return combine_unit<D, 8>(a, unit, lane);
+  }
+  if constexpr (D / 32 >= 4) {
+    if (per_lane > 2) return combine_unit<D, 4>(a, unit, lane);
+  }
+  if (per_lane > 1) return combine_unit<D, 2>(a, unit, lane);
+  combine_unit<D, 1>(a, unit, lane);
+}
 
 template <int D, bool kNarrow, bool kSplit>
 __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const KernelArgs a) {
@@ -103,9 +224,21 @@ __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const Ker
   const int G = a.G;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));  // wave-uniform
-  const int64_t x = blockIdx.x;
+  int64_t x = blockIdx.x;
   int64_t hk, row, local = 0;
   int p = 0;
+  if constexpr (kSplit) {
+    // Every comb_stride-th workgroup merges four units of the previous pass
+    // instead, spread evenly over the launch; the others keep their order.
+    if (a.comb_blocks > 0) {
+      const int64_t k1 = (x + 1) / a.comb_stride;
+      if (k1 * a.comb_stride == x + 1 && k1 <= a.comb_blocks) {
+        combine_unit<D>(a, (k1 - 1) * kWaves + wave, lane);
+        return;
+      }
+      x -= min(x / a.comb_stride, a.comb_blocks);
+    }
+  }
   if constexpr (!kSplit) {
     // Workgroup x -> (KV head x % Hkv, four neighbouring rows): workgroups are
     // dealt round-robin to the 8 XCDs, so when Hkv divides 8 each XCD serves a
@@ -298,83 +431,19 @@ __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const Ker
       bf16x4 o;
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(acc[t][r] * inv);
-      *reinterpret_cast<u32x2*>(dst + 16 * t + 4 * g) = __builtin_bit_cast(u32x2, o);
+      if (direct)
+        *reinterpret_cast<u32x2*>(dst + 16 * t + 4 * g) = __builtin_bit_cast(u32x2, o);
+      else  // read once, by the combine: streamed past the caches (keeps the L2 for K and V)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, o), reinterpret_cast<u32x2*>(dst + 16 * t + 4 * g));
     }
   }
 }
 
-// Merges the partial results of one (row, KV head) of a split pass: one
-// wavefront per unit; lane L takes the 8-element pieces L, L + 64, .. of the
-// unit's G x D outputs.  Rows with routes in at most one range were written
-// by the split kernel and are skipped.
+// The combine of one pass on its own: one wavefront per (row, KV head) unit.
 template <int D>
 __global__ void __launch_bounds__(64 * kWaves) range_combine_kernel(const KernelArgs a) {
-  constexpr int kPieces = D / 32;  // pieces per lane at G = 16: 16 * D / 8 / 64
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  if (unit >= a.pass_rows * a.Hkv) return;
-  const int64_t local = unit / a.Hkv;
-  const int64_t hk = unit - local * a.Hkv;
-  const int64_t row = a.row0 + local;
-  const int G = a.G;
-  int lo_l, hi_l;
-  const uint64_t parts = range_parts(a.offs + row * (a.P + 1), a.P, a.K, lane, &lo_l, &hi_l);
-  if (__builtin_popcountll(parts) < 2) return;
-
-  const int n_pieces = G * D / 8;
-  const int64_t u0 = (local * a.Hkv + hk) * a.P;  // partial index of range 0 of this unit
-  float mx[kPieces], wsum[kPieces];
-  float acc[kPieces][8];
-#pragma unroll
-  for (int k = 0; k < kPieces; ++k) {
-    mx[k] = -INFINITY;
-    wsum[k] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
-  }
-  // the largest log2-sum-exp of each head over the ranges
-  for (uint64_t m = parts; m != 0; m &= m - 1) {
-    const int p = __builtin_ctzll(m);
-#pragma unroll
-    for (int k = 0; k < kPieces; ++k) {
-      const int piece = lane + 64 * k;
-      if (piece < n_pieces) mx[k] = fmaxf(mx[k], a.part_lse[(u0 + p) * G + piece * 8 / D]);
-    }
-  }
-  // weighted sum in ascending range order
-  for (uint64_t m = parts; m != 0; m &= m - 1) {
-    const int p = __builtin_ctzll(m);
-#pragma unroll
-    for (int k = 0; k < kPieces; ++k) {
-      const int piece = lane + 64 * k;
-      if (piece < n_pieces) {
-        const float w = exp2f(a.part_lse[(u0 + p) * G + piece * 8 / D] - mx[k]);
-        const u32x4 v = load16(a.part_o + ((u0 + p) * G * D + piece * 8));
-        wsum[k] += w;
-        const uint32_t words[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[k][2 * e] += w * bf16_lo(words[e]);
-          acc[k][2 * e + 1] += w * bf16_hi(words[e]);
-        }
-      }
-    }
-  }
-  uint16_t* out_unit = a.out + (row * a.Hq + hk * G) * D;
-#pragma unroll
-  for (int k = 0; k < kPieces; ++k) {
-    const int piece = lane + 64 * k;
-    if (piece < n_pieces) {
-      const float inv = 1.0f / wsum[k];
-      bf16x8 o;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(acc[k][e] * inv);
-      *reinterpret_cast<u32x4*>(out_unit + piece * 8) = __builtin_bit_cast(u32x4, o);
-      if (a.lse != nullptr && (piece * 8) % D == 0)
-        a.lse[row * a.Hq + hk * G + piece * 8 / D] = (mx[k] + log2f(wsum[k])) * kLn2;
-    }
-  }
+  combine_unit<D>(a, static_cast<int64_t>(blockIdx.x) * kWaves + wave, threadIdx.x & 63);
 }
 
 // Range starts of each row's list: offs[row][p] = the first position whose
@@ -467,19 +536,35 @@ hipError_t launch(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& 
     return e;
   k.offs = w.offs;
   k.P = plan.P;
-  k.part_o = w.part_o;
-  k.part_lse = w.part_lse;
-  for (int64_t r0 = 0; r0 < rows; r0 += w.pass_rows) {
-    k.row0 = r0;
-    k.pass_rows = std::min(w.pass_rows, rows - r0);
+  // Passes from the last rows to the first (with causal routes the later
+  // rows reach more ranges, so the combine left for the end is the smallest).
+  // Each pass's split launch also merges the previous pass's partials, from
+  // the other of the two partial buffers; the last pass is merged on its own.
+  const int64_t n_pass = (rows + w.pass_rows - 1) / w.pass_rows;
+  for (int64_t i = 0; i <= n_pass; ++i) {
+    if (i > 0) {  // the previous pass, to be merged
+      k.comb_row0 = k.row0;
+      k.comb_pass_rows = k.pass_rows;
+      k.comb_part_o = k.part_o;
+      k.comb_part_lse = k.part_lse;
+    }
+    const int64_t comb_blocks = i > 0 ? (k.comb_pass_rows * a.Hkv + kWaves - 1) / kWaves : 0;
+    if (i == n_pass) {
+      hipLaunchKernelGGL((range_combine_kernel<D>), dim3(static_cast<uint32_t>(comb_blocks)), dim3(64 * kWaves), 0,
+                         stream, k);
+      return hipGetLastError();
+    }
+    const int64_t r_end = rows - i * w.pass_rows;
+    k.row0 = std::max<int64_t>(r_end - w.pass_rows, 0);
+    k.pass_rows = r_end - k.row0;
     k.rowgroups = (k.pass_rows + kWaves - 1) / kWaves;
-    const int64_t blocks = k.rowgroups * plan.P * a.Hkv;
-    hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow, true>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(64 * kWaves), 0, stream, k);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    const int64_t units = k.pass_rows * a.Hkv;
-    hipLaunchKernelGGL((range_combine_kernel<D>), dim3(static_cast<uint32_t>((units + kWaves - 1) / kWaves)),
-                       dim3(64 * kWaves), 0, stream, k);
+    k.part_o = w.part_o[i & 1];
+    k.part_lse = w.part_lse[i & 1];
+    const int64_t gather_blocks = k.rowgroups * plan.P * a.Hkv;
+    k.comb_blocks = comb_blocks;
+    k.comb_stride = comb_blocks > 0 ? (gather_blocks + comb_blocks) / comb_blocks : 0;
+    hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow, true>),
+                       dim3(static_cast<uint32_t>(gather_blocks + comb_blocks)), dim3(64 * kWaves), 0, stream, k);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -526,9 +611,11 @@ SplitPlan split_plan(int64_t rows, int64_t S_kv, int64_t Hq, int64_t D) {
   return plan;
 }
 
-int64_t split_workspace_bytes(const SplitPlan& plan, int64_t pass_rows) {
+int64_t split_workspace_bytes(const SplitPlan& plan, int64_t pass_rows, int64_t rows) {
   auto r256 = [](int64_t x) { return (x + 255) / 256 * 256; };
-  return plan.offs_bytes + r256(pass_rows * plan.part_o_row_bytes) + r256(pass_rows * plan.part_lse_row_bytes);
+  const int64_t buffers = pass_rows < rows ? 2 : 1;
+  return plan.offs_bytes +
+         buffers * (r256(pass_rows * plan.part_o_row_bytes) + r256(pass_rows * plan.part_lse_row_bytes));
 }
 
 hipError_t launch_gather_attention(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& w,

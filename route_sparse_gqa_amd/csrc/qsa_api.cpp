@@ -140,24 +140,36 @@ bool attention_plan(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hk
   return true;
 }
 
-// Rows per pass that fit `bytes` of split workspace (every row when they all fit), or 0 when fewer than
-// min(rows, kMinPassRows) fit.
+// Rows per pass that fit `bytes` of split workspace (every row when they all fit in one pass, whose
+// partials need one buffer; else two buffers of a pass), or 0 when fewer than min(rows, kMinPassRows) fit.
 int64_t split_pass_rows(const qsa::SplitPlan& plan, int64_t rows, int64_t Hkv, size_t bytes) {
   if (bytes < static_cast<size_t>(plan.offs_bytes)) return 0;
-  const int64_t grid_rows = kMaxGrid / (plan.P * Hkv) * 4;  // split grid: ceil(pass / 4) * P * Hkv workgroups
-  auto fits = [&](int64_t pass) { return static_cast<size_t>(qsa::split_workspace_bytes(plan, pass)) <= bytes; };
+  // split launch: ceil(pass / 4) * P * Hkv workgroups, plus ceil(previous pass * Hkv / 4) merging the previous pass
+  const int64_t grid_rows = kMaxGrid / ((plan.P + 1) * Hkv) * 4;
+  auto fits = [&](int64_t pass) {
+    return static_cast<size_t>(qsa::split_workspace_bytes(plan, pass, rows)) <= bytes;
+  };
   if (rows <= grid_rows && fits(rows)) return rows;
   const int64_t per_row = plan.part_o_row_bytes + plan.part_lse_row_bytes;
-  int64_t pass = std::min(static_cast<int64_t>((bytes - plan.offs_bytes) / per_row), grid_rows) / 4 * 4;
+  int64_t pass =
+      std::min({static_cast<int64_t>((bytes - plan.offs_bytes) / (2 * per_row)), grid_rows, rows - 1}) / 4 * 4;
   while (pass > 0 && !fits(pass)) pass -= 4;  // the 256-byte rounding of each part takes a few rows at most
   return pass >= std::min(rows, qsa::kMinPassRows) ? pass : 0;
+}
+
+// The smallest split workspace a call can run in: one pass of every row (one partial buffer), or two
+// buffers of the smallest pass, whichever is smaller.
+size_t split_min_bytes(const qsa::SplitPlan& plan, int64_t rows) {
+  const int64_t one_pass = qsa::split_workspace_bytes(plan, rows, rows);
+  if (rows <= qsa::kMinPassRows) return static_cast<size_t>(one_pass);
+  return static_cast<size_t>(std::min(one_pass, qsa::split_workspace_bytes(plan, qsa::kMinPassRows, rows)));
 }
 
 size_t attention_ws(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K) {
   qsa::SplitPlan plan;
   if (!attention_plan(B, S_q, S_kv, Hq, Hkv, D, K, &plan) || !plan.use) return 0;
   const int64_t rows = B * S_q;
-  return static_cast<size_t>(qsa::split_workspace_bytes(plan, std::min(rows, kPassRowsDefault)));
+  return static_cast<size_t>(qsa::split_workspace_bytes(plan, std::min(rows, kPassRowsDefault), rows));
 }
 
 }  // namespace
@@ -316,9 +328,13 @@ int run_attention(const qsa::AttnArgs& a, void* workspace, size_t workspace_byte
     if (w.pass_rows == 0) return QSA_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
     w.offs = reinterpret_cast<int32_t*>(ws);
-    w.part_o = reinterpret_cast<uint16_t*>(ws + plan.offs_bytes);
-    w.part_lse = reinterpret_cast<float*>(
-        ws + plan.offs_bytes + round_up(static_cast<size_t>(w.pass_rows * plan.part_o_row_bytes), kWorkspaceAlign));
+    const size_t o_bytes = round_up(static_cast<size_t>(w.pass_rows * plan.part_o_row_bytes), kWorkspaceAlign);
+    const size_t lse_bytes = round_up(static_cast<size_t>(w.pass_rows * plan.part_lse_row_bytes), kWorkspaceAlign);
+    for (int j = 0; j < 2; ++j) {  // the second buffer is used only when there is more than one pass
+      char* buf = ws + plan.offs_bytes + (w.pass_rows < rows ? j : 0) * (o_bytes + lse_bytes);
+      w.part_o[j] = reinterpret_cast<uint16_t*>(buf);
+      w.part_lse[j] = reinterpret_cast<float*>(buf + o_bytes);
+    }
   }
   return hip_status(qsa::launch_gather_attention(a, plan, w, stream));
 }
@@ -328,7 +344,7 @@ size_t attention_ws_used(const qsa::AttnArgs& a, size_t workspace_bytes) {
   qsa::SplitPlan plan;
   if (!attention_plan(a.B, a.S_q, a.S_kv, a.Hq, a.Hkv, a.D, a.K, &plan) || !plan.use) return 0;
   const int64_t pass = split_pass_rows(plan, a.B * a.S_q, a.Hkv, workspace_bytes);
-  return pass > 0 ? static_cast<size_t>(qsa::split_workspace_bytes(plan, pass)) : 0;
+  return pass > 0 ? static_cast<size_t>(qsa::split_workspace_bytes(plan, pass, a.B * a.S_q)) : 0;
 }
 
 }  // namespace
@@ -355,9 +371,7 @@ int forward_entry(const void* q, const int64_t q_strides[4], const void* k, cons
   qsa::SplitPlan plan;
   if (!attention_plan(B, S_q, S_kv, Hq, Hkv, D, K, &plan)) return QSA_ERR_LIMIT;
   if (scratch != nullptr) {  // the caller's fixed scratch replaces the workspace
-    const size_t need = lists + (plan.use ? static_cast<size_t>(qsa::split_workspace_bytes(
-                                                plan, std::min(s.rows, qsa::kMinPassRows)))
-                                          : 0);
+    const size_t need = lists + (plan.use ? split_min_bytes(plan, s.rows) : 0);
     if (int st = scratch(need, stream, &workspace, &workspace_bytes)) return st;
   }
   if (workspace == nullptr || !aligned(workspace, kWorkspaceAlign)) return QSA_ERR_WORKSPACE;

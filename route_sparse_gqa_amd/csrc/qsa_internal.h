@@ -67,16 +67,18 @@ struct SplitPlan {
 SplitPlan split_plan(int64_t rows, int64_t S_kv, int64_t Hq, int64_t D);
 
 // Workspace of a split attention: range starts, then for each pass row the
-// partial outputs [Hkv][P][G][D] bf16 and their log2-sum-exps [Hkv][P][G] fp32.
+// partial outputs [Hkv][P][G][D] bf16 and their log2-sum-exps [Hkv][P][G]
+// fp32, twice when there is more than one pass (a pass's partials are merged
+// while the next pass gathers into the other buffer).
 struct SplitBuffers {
   int32_t* offs;
-  uint16_t* part_o;
-  float* part_lse;
+  uint16_t* part_o[2];
+  float* part_lse[2];
   int64_t pass_rows;  // rows per pass (a multiple of 4, or every row)
 };
 
-// Bytes of split workspace for passes of pass_rows rows (plan.use must hold).
-int64_t split_workspace_bytes(const SplitPlan& plan, int64_t pass_rows);
+// Bytes of split workspace for passes of pass_rows of the call's rows (plan.use must hold).
+int64_t split_workspace_bytes(const SplitPlan& plan, int64_t pass_rows, int64_t rows);
 
 // qsa_forward's checks and launches.  When `scratch` is non-null it is
 // called after the argument checks with the smallest workspace the call can

@@ -79,7 +79,8 @@ def _split_bytes(rows, S_kv, Hq, D, pass_rows):
     while -(-S_kv // W) > 63:
         W *= 2
     P = -(-S_kv // W)
-    return P, r256(4 * rows * (P + 1)) + r256(2 * pass_rows * Hq * P * D) + r256(4 * pass_rows * Hq * P)
+    buffers = 2 if pass_rows < rows else 1  # a pass's partials are merged while the next pass fills the other
+    return P, r256(4 * rows * (P + 1)) + buffers * (r256(2 * pass_rows * Hq * P * D) + r256(4 * pass_rows * Hq * P))
 
 
 def test_attention_workspace_size():

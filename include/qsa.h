@@ -52,9 +52,11 @@ extern "C" {
 #define QSA_ERR_ALIAS -9        /* an output overlaps an input or another output       */
 #define QSA_ERR_WORKSPACE -10   /* workspace NULL or smaller than required             */
 #define QSA_ERR_LIMIT -11       /* a size beyond a library limit: K > QSA_MAX_ROUTES,  */
-                                /* G > QSA_MAX_GROUP, B*S_q >= 2^31, more index heads, */
+                                /* G > QSA_MAX_GROUP, B*S_q >= 2^24, more index heads, */
                                 /* kept or visible blocks than the selection limits,   */
-                                /* or strides whose element offsets overflow 64 bits   */
+                                /* a launch of 2^32 or more work-items (one grid       */
+                                /* dimension holds fewer), or strides whose element    */
+                                /* offsets overflow 64 bits                            */
 #define QSA_ERR_HIP -12         /* a HIP launch reported an error                      */
 #define QSA_ERR_SELECTION -13   /* token_budget or compress_ratio < 1, or query rows   */
                                 /* outside [0, S_global) (route selection)             */

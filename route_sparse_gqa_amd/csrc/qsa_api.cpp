@@ -20,7 +20,8 @@
 namespace {
 
 constexpr int64_t kMaxKv = int64_t{1} << 31;  // IDs are stored as int32
-constexpr int64_t kMaxGrid = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxGrid = qsa::kMaxBlocks;  // 256-thread workgroups per launch; also the largest B * S_q
+constexpr int64_t kMaxIndex = (int64_t{1} << 31) - 1;  // counts and positions stored as int32
 
 struct Range {
   uintptr_t lo = 0, hi = 0;  // [lo, hi) bytes; empty when lo == hi
@@ -75,6 +76,11 @@ struct Sizes {
   int64_t list_bytes = 0;
   int64_t count_bytes = 0;
 };
+
+// The route normalisation launch for rows of K slots over kv_length keys fits one grid.
+bool route_launch_fits(int64_t rows, int64_t K, int64_t kv_length) {
+  return (rows + 3) * qsa::route_normalize_items_per_row(K, kv_length) <= qsa::kMaxLaunchItems;  // 4-row groups
+}
 
 int check_route_dims(int64_t B, int64_t S_q, int64_t K, Sizes* s) {
   if (B < 1 || S_q < 1 || K < 1) return QSA_ERR_EMPTY_DIM;
@@ -197,6 +203,7 @@ QSA_EXPORT int qsa_preprocess(const void* routes, int routes_dtype, int64_t B, i
   if (routes == nullptr || route_strides == nullptr || route_list == nullptr || route_count == nullptr)
     return QSA_ERR_NULL_POINTER;
   if (kv_length < 1 || kv_length > kMaxKv) return QSA_ERR_KV_LENGTH;
+  if (!route_launch_fits(s.rows, K, kv_length)) return QSA_ERR_LIMIT;
   if (routes_dtype != QSA_INT32 && routes_dtype != QSA_INT64) return QSA_ERR_ROUTE_DTYPE;
   const int64_t relem = routes_dtype == QSA_INT64 ? 8 : 4;
   if (!aligned(routes, relem) || !aligned(route_list, 4) || !aligned(route_count, 4)) return QSA_ERR_LAYOUT;
@@ -242,7 +249,7 @@ QSA_EXPORT int qsa_tile_lists(const int32_t* tile_class, int64_t B, int64_t n_ro
   if (B < 1 || n_rows < 1 || n_cols < 1) return QSA_ERR_EMPTY_DIM;
   if (tile_class == nullptr) return QSA_ERR_NULL_POINTER;
   int64_t tiles = 0, rows = 0, cols = 0;
-  if (n_rows > kMaxGrid || n_cols > kMaxGrid || !mul_ok(B, n_rows, &rows) || !mul_ok(B, n_cols, &cols) ||
+  if (n_rows > kMaxIndex || n_cols > kMaxIndex || !mul_ok(B, n_rows, &rows) || !mul_ok(B, n_cols, &cols) ||
       !mul_ok(rows, n_cols, &tiles) || tiles > (INT64_MAX >> 3) || (rows + cols + 3) / 4 > kMaxGrid)
     return QSA_ERR_LIMIT;
   int32_t* const out[8] = {partial_count, partial_idx, full_count, full_idx,
@@ -363,6 +370,7 @@ int forward_entry(const void* q, const int64_t q_strides[4], const void* k, cons
     return st;
   if (routes == nullptr || route_strides == nullptr) return QSA_ERR_NULL_POINTER;
   if (routes_dtype != QSA_INT32 && routes_dtype != QSA_INT64) return QSA_ERR_ROUTE_DTYPE;
+  if (!route_launch_fits(s.rows, K, S_kv)) return QSA_ERR_LIMIT;
   const int64_t relem = routes_dtype == QSA_INT64 ? 8 : 4;
   if (!aligned(routes, relem)) return QSA_ERR_LAYOUT;
   // the lists and counts first, then the attention's own workspace
@@ -470,7 +478,7 @@ bool bwd_layout(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, i
       !mul_ok(rows, K < l->n_kt ? K : l->n_kt, &cap))
     return false;
   // segment positions, chunk prefixes, tile and part starts are int32
-  if (cap > kMaxGrid || chunks > kMaxGrid || tiles + 1 > kMaxGrid / 2 || heads > (INT64_MAX >> 3) ||
+  if (cap > kMaxIndex || chunks > kMaxIndex || tiles + 1 > kMaxIndex / 2 || heads > (INT64_MAX >> 3) ||
       words > (INT64_MAX >> 3))
     return false;
   l->capacity = cap;
@@ -535,7 +543,10 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
   if (!bwd_layout(B, S_q, S_kv, Hq, Hkv, D, K, &l)) return QSA_ERR_LIMIT;
   int64_t kv_elems = 0;
   if (!mul_ok(B * S_kv, Hkv * D, &kv_elems) || kv_elems > (INT64_MAX >> 2)) return QSA_ERR_LIMIT;
-  if ((l.n_kt * B + l.max_parts) * Hkv > kMaxGrid || l.n_kt * B * 4 * Hkv > kMaxGrid || (s.rows + 3) / 4 > kMaxGrid ||
+  // grids: dk/dv and its reduction, dq (and delta and its combine) per (row, KV head) group of four, the
+  // split dq per (range, KV head, four rows of a pass), the segment counts
+  if ((l.n_kt * B + l.max_parts) * Hkv > kMaxGrid || l.n_kt * B * 4 * Hkv > kMaxGrid ||
+      (s.rows + 3) / 4 * Hkv > kMaxGrid || (l.split.use && (l.dq_pass_rows + 3) / 4 * l.split.P * Hkv > kMaxGrid) ||
       (B * ((S_q + qsa::kSegChunkRows - 1) / qsa::kSegChunkRows) * l.n_kt + 255) / 256 > kMaxGrid)
     return QSA_ERR_LIMIT;
   if (workspace == nullptr || workspace_bytes < l.total || !aligned(workspace, kWorkspaceAlign))
@@ -624,11 +635,13 @@ int check_select_dims(int64_t B, int64_t S_q, int64_t H, int64_t D, int64_t S_gl
   if (token_budget < 1 || c < 1 || q_offset < 0 || q_offset > S_global || S_q > S_global - q_offset)
     return QSA_ERR_SELECTION;
   if (D != 64 && D != 128 && D != 256) return QSA_ERR_HEAD_DIM;
-  if (H > QSA_MAX_INDEX_HEADS || S_global > kMaxGrid || token_budget / c > QSA_MAX_SELECT_BLOCKS ||
-      S_global / c > QSA_MAX_VISIBLE_BLOCKS || token_budget > kMaxGrid - c)
+  if (H > QSA_MAX_INDEX_HEADS || S_global > kMaxIndex || token_budget / c > QSA_MAX_SELECT_BLOCKS ||
+      S_global / c > QSA_MAX_VISIBLE_BLOCKS || token_budget > kMaxIndex - c)
     return QSA_ERR_LIMIT;
   z->width = token_budget + c - 1;
   if (!mul_ok(B, S_q, &z->rows) || z->rows > kMaxGrid) return QSA_ERR_LIMIT;
+  // the top-k takes one workgroup per row: 1024 threads when a row can see more than 256 * 64 blocks
+  if ((q_offset + S_q) / c > 256 * 64 && z->rows > qsa::kMaxLaunchItems / 1024) return QSA_ERR_LIMIT;
   int64_t outs = 0;
   if (!mul_ok(z->rows, z->width, &outs) || outs > (INT64_MAX >> 3)) return QSA_ERR_LIMIT;
   z->tile_rows = qsa::select_rows_per_tile(H);

@@ -7,6 +7,16 @@
 
 namespace qsa {
 
+// One launch holds fewer than 2^32 work-items per grid dimension
+// (gridDim.x * blockDim.x); kMaxBlocks is that limit in 256-thread
+// workgroups, the size of most launches here.
+constexpr int64_t kMaxLaunchItems = (int64_t{1} << 32) - 1;
+constexpr int64_t kMaxBlocks = kMaxLaunchItems / 256;
+
+// Work-items per query row of the route normalisation launch that K and
+// kv_length select (the host checks B * S_q times it against kMaxLaunchItems).
+int64_t route_normalize_items_per_row(int64_t K, int64_t kv_length);
+
 // Route normalisation: [B*S_q rows, K slots] -> ascending distinct valid IDs.
 // When zero_buf is non-null the same launch also sets its zero_count int32
 // entries to 0 (the tile member counters of the membership pass).

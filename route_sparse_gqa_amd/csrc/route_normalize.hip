@@ -383,15 +383,29 @@ __global__ void __launch_bounds__(64 * kWaveRows)
   }
 }
 
+// The launch that normalises rows of K slots over kv_length keys.
+enum class RoutePath { kWave8, kWave16, kBitmapHalf, kBitmap, kSorted };
+
+RoutePath route_path(int64_t K, int64_t kv_length) {
+  if (kv_length <= 32 * kWaveWords && K <= 1024) return K <= 512 ? RoutePath::kWave8 : RoutePath::kWave16;
+  if (kv_length <= 32 * int64_t{kBitmapWordsHalf} && K <= kBitmapWordsHalf) return RoutePath::kBitmapHalf;
+  if (kv_length <= 32 * int64_t{kBitmapWords} && K <= kBitmapWords) return RoutePath::kBitmap;
+  return RoutePath::kSorted;
+}
+
+// Wavefronts per row of the sorting path (the W of launch_sorted).
+int64_t sorted_waves(int64_t K) { return K <= 512 ? 1 : K <= 1024 ? 2 : K <= 2048 ? 4 : K <= 4096 ? 8 : 16; }
+
 template <typename RouteT>
 hipError_t dispatch(const RouteT* routes, const int64_t* st, int64_t B, int64_t S_q, int64_t K,
                     int64_t kv_length, int32_t* list, int32_t* count, int32_t* zb, int64_t zn,
                     hipStream_t stream) {
   const dim3 rows(static_cast<uint32_t>(B * S_q)), threads(kBitmapThreads);
-  if (kv_length <= 32 * kWaveWords && K <= 1024) {  // small rows: one wavefront each
+  const RoutePath path = route_path(K, kv_length);
+  if (path == RoutePath::kWave8 || path == RoutePath::kWave16) {  // small rows: one wavefront each
     const int64_t n_rows = B * S_q;
     const dim3 groups(static_cast<uint32_t>((n_rows + kWaveRows - 1) / kWaveRows)), wave_threads(64 * kWaveRows);
-    if (K <= 512)
+    if (path == RoutePath::kWave8)
       hipLaunchKernelGGL((route_wave_kernel<8, RouteT>), groups, wave_threads, 0, stream, routes, st[0], st[1], st[2],
                          S_q, n_rows, K, kv_length, list, count, zb, zn);
     else
@@ -399,12 +413,12 @@ hipError_t dispatch(const RouteT* routes, const int64_t* st, int64_t B, int64_t 
                          st[2], S_q, n_rows, K, kv_length, list, count, zb, zn);
     return hipGetLastError();
   }
-  if (kv_length <= 32 * int64_t{kBitmapWordsHalf} && K <= kBitmapWordsHalf) {
+  if (path == RoutePath::kBitmapHalf) {
     hipLaunchKernelGGL((route_bitmap_kernel<kBitmapWordsHalf, RouteT>), rows, threads, 0, stream, routes, st[0],
                        st[1], st[2], S_q, K, kv_length, list, count, zb, zn);
     return hipGetLastError();
   }
-  if (kv_length <= 32 * int64_t{kBitmapWords} && K <= kBitmapWords) {
+  if (path == RoutePath::kBitmap) {
     hipLaunchKernelGGL((route_bitmap_kernel<kBitmapWords, RouteT>), rows, threads, 0, stream, routes, st[0], st[1],
                        st[2], S_q, K, kv_length, list, count, zb, zn);
     return hipGetLastError();
@@ -421,6 +435,16 @@ hipError_t dispatch(const RouteT* routes, const int64_t* st, int64_t B, int64_t 
 }
 
 }  // namespace
+
+int64_t route_normalize_items_per_row(int64_t K, int64_t kv_length) {
+  switch (route_path(K, kv_length)) {
+    case RoutePath::kWave8:
+    case RoutePath::kWave16: return 64;
+    case RoutePath::kBitmapHalf:
+    case RoutePath::kBitmap: return kBitmapThreads;
+    default: return 64 * sorted_waves(K);  // 64 * W * ROWS threads per ROWS rows
+  }
+}
 
 hipError_t launch_route_normalize(const void* routes, bool routes_int64, int64_t B, int64_t S_q,
                                   int64_t K, const int64_t route_strides[3], int64_t kv_length,

@@ -141,6 +141,25 @@ def test_other_host_checks():
                             None) == -11
 
 
+def test_launches_beyond_one_grid_are_refused():
+    """One launch holds fewer than 2^32 work-items per grid dimension; calls whose grids would not fit return
+    QSA_ERR_LIMIT before anything runs (fake pointers never reach a launch)."""
+    L = qsa.lib()
+    fake = [ctypes.c_void_p(n << 32) for n in range(1, 4)]
+    s3 = (ctypes.c_int64 * 3)(1, 1, 1)
+    # 2^24 rows: route normalisation's bitmap path runs one 256-thread workgroup per row
+    assert L.qsa_preprocess(fake[0], 1, 1, 1 << 24, 1, s3, 5, fake[1], fake[2], None, None, None) == -11
+    # K = 8193 over 2^20 keys sorts each row with 16 wavefronts (1024 work-items): 2^22 rows do not fit
+    sk = (ctypes.c_int64 * 3)((1 << 22) * 8193, 8193, 1)
+    assert L.qsa_preprocess(fake[0], 1, 1, 1 << 22, 8193, sk, 1 << 20, fake[1], fake[2], None, None, None) == -11
+    assert _call_forward(S_q=1 << 24) == -11
+    assert _call_forward(S_q=1 << 22, K=8193, S_kv=1 << 20) == -11
+    assert _call_forward(S_q=1 << 22, Hq=16, Hkv=16) == -11          # ceil(rows / 4) * Hkv = 2^24 workgroups
+    assert _call_backward(S_q=1 << 22, Hq=16, Hkv=16) == -11
+    # a top-k row that sees more than 16384 blocks takes a 1024-thread workgroup: at most 2^22 - 1 rows
+    assert _call_select(S_q=1 << 22, S_global=1 << 22, c=64, budget=64) == -11
+
+
 def _bwd_ws(B, S_q, S_kv, Hq, Hkv, D, K):
     """The layout the header documents, from its formula."""
     r = lambda x: -(-x // 256) * 256

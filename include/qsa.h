@@ -283,7 +283,9 @@ int qsa_forward_preprocessed(const void *q, const int64_t q_strides[4], const vo
  *   when dq takes the key-range split (the forward's rule, see
  *   qsa_attention_workspace_size, with Pr ranges):
  *   range starts          4 * B*S_q*(Pr + 1)
- *   dq partial sums       4 * R*Hq*Pr*D, R = min(B*S_q, 8192) rows per pass
+ *   dq partial sums       4 * R*Hq*Pr*D, R = min(B*S_q, 4096) rows per pass,
+ *                         twice when R < B*S_q (a pass's sums are added up
+ *                         while the next pass fills the other buffer)
  * Returns 0 when a size is < 1 or beyond the library's int32 segment
  * indexing (more than 2^31 - 1 segments or chunk prefixes).
  */

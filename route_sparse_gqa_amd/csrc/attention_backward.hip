@@ -84,7 +84,87 @@ struct DqArgs {
   int P;
   int64_t row0, pass_rows, rowgroups;
   float* part;  // [pass_rows][Hkv][P][G][D]
+  // the pass whose partial sums are added up (by dq_combine_kernel, or by the
+  // combine workgroups interleaved into the next pass's split launch)
+  int64_t comb_row0, comb_pass_rows;
+  const float* comb_part;
+  int64_t comb_blocks, comb_stride;  // split launch: workgroup comb_stride * k - 1 adds units 4(k-1) ..
 };
+
+// Adds the fp32 partial dq of one (row, KV head) unit's ranges in ascending
+// range order and writes scale x the sum as bf16 (one wavefront): lane L
+// takes the 4-element pieces L, L + 64, .. (kP of them) of the unit's G x D
+// values; the ranges are read kB at a time with all their loads in flight
+// together (16 16-byte loads per lane at D = 256, fewer below, which keeps
+// the split dq kernel within the registers it needs anyway).  Rows with
+// routes in at most one range were written by dq_kernel.
+template <int D, int kP>
+__device__ __forceinline__ void dq_combine_unit(const DqArgs& a, int64_t unit, int lane) {
+  constexpr int kSlots = D == 256 ? 16 : D == 128 ? 8 : 4;  // 16-byte loads per lane per batch
+  constexpr int kB = kSlots / kP > 0 ? kSlots / kP : 1;        // ranges per batch
+  const int64_t local = unit / a.Hkv, hk = unit - local * a.Hkv;
+  const int64_t row = a.comb_row0 + local;
+  int lo_l, hi_l;
+  uint64_t parts = range_parts(a.offs + row * (a.P + 1), a.P, a.K, lane, &lo_l, &hi_l);
+  if (__builtin_popcountll(parts) < 2) return;
+  const int n_pieces = a.G * D / 4;
+  const float* base = a.comb_part + (local * a.Hkv + hk) * a.P * a.G * D;
+  f32x4 acc[kP];
+#pragma unroll
+  for (int k = 0; k < kP; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  while (parts != 0) {  // wave-uniform
+    int pr[kB];  // this batch's ranges, ascending; -1 past the unit's last
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      pr[j] = parts != 0 ? __builtin_ctzll(parts) : -1;
+      parts &= parts - 1;
+    }
+    f32x4 v[kB][kP];
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+#pragma unroll
+      for (int k = 0; k < kP; ++k) {
+        const int piece = lane + 64 * k;
+        if (pr[j] >= 0 && piece < n_pieces) {
+          const f32x4* src = reinterpret_cast<const f32x4*>(base + static_cast<int64_t>(pr[j]) * a.G * D + 4 * piece);
+          v[j][k] = __builtin_nontemporal_load(src);  // read once: streamed
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+#pragma unroll
+      for (int k = 0; k < kP; ++k)
+        if (pr[j] >= 0 && lane + 64 * k < n_pieces) acc[k] += v[j][k];
+  }
+  uint16_t* dst = a.dq + (row * a.Hq + hk * a.G) * D;
+#pragma unroll
+  for (int k = 0; k < kP; ++k) {
+    const int piece = lane + 64 * k;
+    if (piece < n_pieces) {
+      bf16x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = static_cast<__bf16>(acc[k][r] * a.scale);
+      *reinterpret_cast<u32x2*>(dst + 4 * piece) = __builtin_bit_cast(u32x2, w);
+    }
+  }
+}
+
+// dq_combine_unit with kP = the pieces each lane needs, G * D / 256 rounded
+// up to a power of two (at most D / 16, at G = 16).
+template <int D>
+__device__ __forceinline__ void dq_combine_unit(const DqArgs& a, int64_t unit, int lane) {
+  if (unit >= a.comb_pass_rows * a.Hkv) return;
+  const int per_lane = (a.G * D / 4 + 63) / 64;
+  if constexpr (D / 16 >= 16) {
+    if (per_lane > 8) return dq_combine_unit<D, 16>(a, unit, lane);
+  }
+  if constexpr (D / 16 >= 8) {
+    if (per_lane > 4) return dq_combine_unit<D, 8>(a, unit, lane);
+  }
+  if (per_lane > 2) return dq_combine_unit<D, 4>(a, unit, lane);
+  if (per_lane > 1) return dq_combine_unit<D, 2>(a, unit, lane);
+  dq_combine_unit<D, 1>(a, unit, lane);
+}
 
 // delta = <dO, O> per (row, head), for the split dq kernel (whose units each
 // see only part of a row) and the dk/dv kernel: one wavefront per (row, KV
@@ -119,7 +199,8 @@ __global__ void __launch_bounds__(64 * kWaves) delta_kernel(const DqArgs a) {
 // forms delta), or over one key range of them (kSplit: units ordered range by
 // range as in the forward's split, delta from delta_kernel; a unit whose row
 // has routes in no other range writes dq, otherwise an fp32 partial sum that
-// dq_combine_kernel adds in ascending range order).
+// dq_combine_unit adds in ascending range order, in the next pass's launch or
+// on its own after the last pass).
 template <int D, bool kNarrow, bool kSplit>
 __global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
   using Gm = Geo<D>;
@@ -130,9 +211,21 @@ __global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
   const int G = a.G;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int64_t x = blockIdx.x;
+  int64_t x = blockIdx.x;
   int64_t hk, row, local = 0;
   int p = 0;
+  if constexpr (kSplit) {
+    // Every comb_stride-th workgroup adds up four units of the previous pass
+    // instead, spread evenly over the launch; the others keep their order.
+    if (a.comb_blocks > 0) {
+      const int64_t k1 = (x + 1) / a.comb_stride;
+      if (k1 * a.comb_stride == x + 1 && k1 <= a.comb_blocks) {
+        dq_combine_unit<D>(a, (k1 - 1) * kWaves + wave, lane);
+        return;
+      }
+      x -= min(x / a.comb_stride, a.comb_blocks);
+    }
+  }
   if constexpr (!kSplit) {
     hk = x % Hkv;  // one KV head per XCD, as in the forward
     // Rows from the last to the first, as in the forward: with causal routes the longest start first.
@@ -307,45 +400,11 @@ __global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
   }
 }
 
-// Sums the fp32 partial dq of a row's ranges in ascending range order and
-// writes scale x the sum as bf16: one wavefront per (row, KV head); lane L
-// takes the 4-element pieces L, L + 64, .. of the unit's G x D values.  Rows
-// with routes in at most one range were written by dq_kernel.
+// The combine of one pass on its own: one wavefront per (row, KV head) unit.
 template <int D>
 __global__ void __launch_bounds__(64 * kWaves) dq_combine_kernel(const DqArgs a) {
-  constexpr int kPieces = D / 16;  // pieces per lane at G = 16: 16 * D / 4 / 64
-  const int lane = threadIdx.x & 63;
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  if (unit >= a.pass_rows * a.Hkv) return;
-  const int64_t local = unit / a.Hkv, hk = unit - local * a.Hkv;
-  const int64_t row = a.row0 + local;
-  int lo_l, hi_l;
-  const uint64_t parts = range_parts(a.offs + row * (a.P + 1), a.P, a.K, lane, &lo_l, &hi_l);
-  if (__builtin_popcountll(parts) < 2) return;
-  const int n_pieces = a.G * D / 4;
-  const float* base = a.part + (local * a.Hkv + hk) * a.P * a.G * D;
-  f32x4 acc[kPieces];
-#pragma unroll
-  for (int k = 0; k < kPieces; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (uint64_t m = parts; m != 0; m &= m - 1) {
-    const float* src = base + static_cast<int64_t>(__builtin_ctzll(m)) * a.G * D;
-#pragma unroll
-    for (int k = 0; k < kPieces; ++k) {
-      const int piece = lane + 64 * k;
-      if (piece < n_pieces) acc[k] += *reinterpret_cast<const f32x4*>(src + 4 * piece);
-    }
-  }
-  uint16_t* dst = a.dq + (row * a.Hq + hk * a.G) * D;
-#pragma unroll
-  for (int k = 0; k < kPieces; ++k) {
-    const int piece = lane + 64 * k;
-    if (piece < n_pieces) {
-      bf16x4 w;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = static_cast<__bf16>(acc[k][r] * a.scale);
-      *reinterpret_cast<u32x2*>(dst + 4 * piece) = __builtin_bit_cast(u32x2, w);
-    }
-  }
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  dq_combine_unit<D>(a, static_cast<int64_t>(blockIdx.x) * kWaves + wave, threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------------------
@@ -681,17 +740,31 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   k.offs = a.offs;
   k.P = a.split.P;
-  k.part = a.dq_part;
-  for (int64_t r0 = 0; r0 < rows; r0 += a.dq_pass_rows) {
-    k.row0 = r0;
-    k.pass_rows = std::min(a.dq_pass_rows, rows - r0);
+  // Passes from the last rows to the first; each pass's split launch also
+  // adds up the previous pass's partial sums, from the other of the two
+  // partial buffers, and the last pass is added up on its own.
+  const int64_t n_pass = (rows + a.dq_pass_rows - 1) / a.dq_pass_rows;
+  for (int64_t i = 0; i <= n_pass; ++i) {
+    if (i > 0) {  // the previous pass, to be added up
+      k.comb_row0 = k.row0;
+      k.comb_pass_rows = k.pass_rows;
+      k.comb_part = k.part;
+    }
+    const int64_t comb_blocks = i > 0 ? (k.comb_pass_rows * a.Hkv + kWaves - 1) / kWaves : 0;
+    if (i == n_pass) {
+      hipLaunchKernelGGL((dq_combine_kernel<D>), dim3(static_cast<uint32_t>(comb_blocks)), dim3(64 * kWaves), 0,
+                         stream, k);
+      return hipGetLastError();
+    }
+    const int64_t r_end = rows - i * a.dq_pass_rows;
+    k.row0 = std::max<int64_t>(r_end - a.dq_pass_rows, 0);
+    k.pass_rows = r_end - k.row0;
     k.rowgroups = (k.pass_rows + kWaves - 1) / kWaves;
-    const int64_t blocks = k.rowgroups * a.split.P * a.Hkv;
-    hipLaunchKernelGGL((dq_kernel<D, kNarrow, true>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0,
-                       stream, k);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t units = k.pass_rows * a.Hkv;
-    hipLaunchKernelGGL((dq_combine_kernel<D>), dim3(static_cast<uint32_t>((units + kWaves - 1) / kWaves)),
+    k.part = a.dq_part[i & 1];
+    const int64_t split_blocks = k.rowgroups * a.split.P * a.Hkv;
+    k.comb_blocks = comb_blocks;
+    k.comb_stride = comb_blocks > 0 ? (split_blocks + comb_blocks) / comb_blocks : 0;
+    hipLaunchKernelGGL((dq_kernel<D, kNarrow, true>), dim3(static_cast<uint32_t>(split_blocks + comb_blocks)),
                        dim3(64 * kWaves), 0, stream, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -462,7 +462,7 @@ namespace {
 // sums of split tiles, each 256-B aligned.
 struct BwdLayout {
   size_t delta = 0, bits = 0, chunk_prefix = 0, totals = 0, tile_start = 0, segs = 0, part_start = 0,
-         slot_start = 0, plan = 0, partial = 0, offs = 0, dq_part = 0, total = 0;
+         slot_start = 0, plan = 0, partial = 0, offs = 0, dq_part = 0, dq_part2 = 0, total = 0;
   int64_t n_kt = 0, capacity = 0, max_parts = 0, dq_pass_rows = 0;
   qsa::SplitPlan split;
 };
@@ -508,6 +508,8 @@ bool bwd_layout(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, i
     if (!mul_ok(l->dq_pass_rows * Hq, static_cast<int64_t>(l->split.P) * D * 4, &part_bytes)) return false;
     take(&l->offs, 4 * rows * (l->split.P + 1));
     take(&l->dq_part, part_bytes);
+    l->dq_part2 = l->dq_part;
+    if (l->dq_pass_rows < rows) take(&l->dq_part2, part_bytes);  // a pass's sums are added during the next
   }
   l->total = off;
   return true;
@@ -610,7 +612,8 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
   a.dv = static_cast<uint16_t*>(dv);
   a.split = l.split;
   a.offs = l.split.use ? reinterpret_cast<int32_t*>(ws + l.offs) : nullptr;
-  a.dq_part = l.split.use ? reinterpret_cast<float*>(ws + l.dq_part) : nullptr;
+  a.dq_part[0] = l.split.use ? reinterpret_cast<float*>(ws + l.dq_part) : nullptr;
+  a.dq_part[1] = l.split.use ? reinterpret_cast<float*>(ws + l.dq_part2) : nullptr;
   a.dq_pass_rows = l.dq_pass_rows;
 
   (void)hipGetLastError();

@@ -156,14 +156,15 @@ struct BwdArgs {
   uint16_t* dq;  // [B, S_q, Hq, D] contiguous
   uint16_t* dk;  // [B, S_kv, Hkv, D] contiguous
   uint16_t* dv;  // [B, S_kv, Hkv, D] contiguous
-  // key-range split of dq (the forward's plan): range starts and fp32 partial sums of one pass
+  // key-range split of dq (the forward's plan): range starts and fp32 partial sums of a pass, in two
+  // buffers when there is more than one pass (the same buffer twice otherwise)
   SplitPlan split;
   int32_t* offs;         // [B * S_q][P + 1]
-  float* dq_part;        // [dq_pass_rows][Hkv][P][G][D]
+  float* dq_part[2];     // [dq_pass_rows][Hkv][P][G][D] each
   int64_t dq_pass_rows;
 };
 
-constexpr int64_t kDqPassRows = 8192;  // rows per pass of the split dq
+constexpr int64_t kDqPassRows = 4096;  // rows per pass of the split dq (two partial buffers of them)
 
 // dq and delta (one wavefront per (b, i, hk)); then dk and dv (one wavefront
 // workgroup per (part of a 64-key tile, hk)) over the key segments.

@@ -170,8 +170,9 @@ def _bwd_ws(B, S_q, S_kv, Hq, Hkv, D, K):
     total = (r(4 * B * S_q * Hq) + r(4 * B * n_w * T) + r(4 * B * n_c * T) + r(4 * B * T) + r(4 * (B * T + 1)) +
              r(16 * cap) + r(4 * (B * T + 1)) + r(4 * B * T) + r(8) + r(512 * D * Hkv * slots))
     Pr, _ = _split_bytes(B * S_q, S_kv, Hq, D, 0)
-    if Pr >= 5:  # dq's key-range split: range starts, then fp32 partial sums of passes of up to 8192 rows
-        total += r(4 * B * S_q * (Pr + 1)) + r(4 * min(B * S_q, 8192) * Hq * Pr * D)
+    if Pr >= 5:  # dq's key-range split: range starts, then fp32 partial sums of passes of up to 4096 rows,
+        R = min(B * S_q, 4096)  # in two buffers when there is more than one pass
+        total += r(4 * B * S_q * (Pr + 1)) + (2 if R < B * S_q else 1) * r(4 * R * Hq * Pr * D)
     return total
 
 

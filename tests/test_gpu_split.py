@@ -175,7 +175,7 @@ BACKWARD_CASES = [  # (B, S_q, S_kv, Hq, Hkv, D, K): the backward's dq takes the
     (1, 40, 20000, 16, 2, 256, 600),
     (2, 33, 45000, 8, 1, 128, 900),
     (1, 50, 90000, 4, 2, 64, 2000),
-    (1, 8200, 16400, 2, 1, 256, 4),   # more than 8192 rows: dq in two passes
+    (1, 8200, 16400, 2, 1, 256, 4),   # more than 8192 rows: dq in three passes of up to 4096 (the last of 8)
 ]
 
 

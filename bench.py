@@ -226,7 +226,8 @@ class Plan:
 
     def kernel_name(self) -> str:
         if self.split:
-            return "range_offsets_kernel + gather_attention_kernel (key-range split) + range_combine_kernel"
+            return ("range_offsets_kernel + gather_attention_kernel (key-range split; from the second pass on "
+                    "each launch also merges the previous pass) + range_combine_kernel (the last pass)")
         return "gather_attention_kernel"
 
 
@@ -733,7 +734,7 @@ def run_select(args):
     }), flush=True)
 
 
-ATTENTION_SOURCES = ("gather_attention.hip", "device_common.h", "qsa_internal.h")
+ATTENTION_SOURCES = ("gather_attention.hip", "device_common.h", "qsa_internal.h", "qsa_api.cpp")  # qsa_api: passes
 
 
 def _kernel_sha() -> str:

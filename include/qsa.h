@@ -160,7 +160,7 @@ int qsa_tile_lists(const int32_t *tile_class, int64_t B, int64_t n_rows, int64_t
  * The rows are processed in passes of R rows, from the last rows to the
  * first: R = every row when one set for all of them fits, else as many
  * multiples of 4 as two sets fit (at least 256); the recommended size takes
- * R = min(B*S_q, 16384).  Results do not depend on R.
+ * R = min(B*S_q, 8192).  Results do not depend on R.
  * Returns 0 as well when a size is out of range.
  */
 size_t qsa_attention_workspace_size(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D,

@@ -131,7 +131,7 @@ QSA_EXPORT const char* qsa_status_string(int status) {
 
 namespace {
 
-constexpr int64_t kPassRowsDefault = 16384;  // rows per pass of the key-range split at the recommended size
+constexpr int64_t kPassRowsDefault = 8192;  // rows per pass of the key-range split at the recommended size
 
 // The attention's key-range split for these shapes; false when a size is out of range.
 bool attention_plan(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hkv, int64_t D, int64_t K,

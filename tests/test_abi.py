@@ -95,7 +95,7 @@ def test_attention_workspace_size():
     ]
     for (B, S_q, S_kv, Hq, Hkv, D, K), P in cases:
         rows = B * S_q
-        got_P, want = _split_bytes(rows, S_kv, Hq, D, min(rows, 16384))
+        got_P, want = _split_bytes(rows, S_kv, Hq, D, min(rows, 8192))
         assert got_P == P
         assert att(B, S_q, S_kv, Hq, Hkv, D, K) == want, (B, S_q, S_kv)
         lists = -(-4 * rows * K // 256) * 256 + -(-4 * rows // 256) * 256

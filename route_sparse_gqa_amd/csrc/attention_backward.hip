@@ -483,13 +483,19 @@ __global__ void __launch_bounds__(64 * kWaves)
   // global load.  Batches then flow through two register stages (loads of
   // batches i + 1 and i + 2 in flight while batch i is computed) into a
   // double-buffered LDS slab.
+  // Every load is issued unconditionally from an in-range address (a column
+  // past the batch reads the chunk's last record's row) and masked when the
+  // stage is written to LDS: a load under a divergent branch would make the
+  // compiler wait for it at the branch's join, i.e. at once.
   struct Stage {
     u32x4 pre[kPer];
     float2 stat;
     uint2 mask;
+    uint32_t ok;  // bit u: pre[u] is a batch column; bit kPer: stat and mask are
   };
-  int32_t n_rec = 0;  // records staged for the current chunk
+  int32_t n_rec = 0;  // records staged for the current chunk (>= 1 while batches run)
   auto fetch = [&](Stage& S, int32_t sb) {  // sb: first record of the batch, within the chunk
+    uint32_t ok_bits = 0;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int pc = tid + kThreads * u;
@@ -498,24 +504,23 @@ __global__ void __launch_bounds__(64 * kWaves)
       const int piece = 8 * (pc % Gm::kLanesPerRow);
       const int slot = col / G;
       const bool ok = col < cols && sb + slot < n_rec;
-      const int32_t ir = ok ? min(max(recs[sb + slot].x, 0), row_max) : 0;
-      const int64_t h = q_head0 + (ok ? col % G : 0);
+      const int32_t ir = min(max(recs[min(sb + slot, n_rec - 1)].x, 0), row_max);
+      const int64_t h = q_head0 + col % G;
       const uint16_t* src = m == 0 ? q + b * qs0 + ir * qs1 + h * qs2 : dout + b * gs0 + ir * gs1 + h * gs2;
-      S.pre[u] = ok ? load16(src + piece) : u32x4{0u, 0u, 0u, 0u};
+      S.pre[u] = load16(src + piece);
+      ok_bits |= ok ? 1u << u : 0u;
     }
-    if (tid < kChunk) {
-      const int col = tid;
+    {
+      const int col = tid % kChunk;  // only threads below kChunk stash it
       const int slot = col / G;
-      if (col < cols && sb + slot < n_rec) {
-        const int4 e = recs[sb + slot];
-        const int64_t idx = (b * S_q + min(max(e.x, 0), row_max)) * Hq + q_head0 + col % G;
-        S.stat = float2{lse[idx] * kLog2e, delta[idx]};
-        S.mask = uint2{static_cast<uint32_t>(e.y), static_cast<uint32_t>(e.z)};
-      } else {
-        S.stat = float2{0.f, 0.f};
-        S.mask = uint2{0u, 0u};
-      }
+      const bool ok = tid < kChunk && col < cols && sb + slot < n_rec;
+      const int4 e = recs[min(sb + slot, n_rec - 1)];
+      const int64_t idx = (b * S_q + min(max(e.x, 0), row_max)) * Hq + q_head0 + col % G;
+      S.stat = float2{lse[idx], delta[idx]};  // raw: any arithmetic here would wait for the loads
+      S.mask = uint2{static_cast<uint32_t>(e.y), static_cast<uint32_t>(e.z)};
+      ok_bits |= ok ? 1u << kPer : 0u;
     }
+    S.ok = ok_bits;
   };
   auto stash = [&](const Stage& S, int buf) {
 #pragma unroll
@@ -524,11 +529,13 @@ __global__ void __launch_bounds__(64 * kWaves)
       const int m = pc / (kChunk * Gm::kLanesPerRow);
       const int col = (pc / Gm::kLanesPerRow) % kChunk;
       const int piece = 8 * (pc % Gm::kLanesPerRow);
-      *reinterpret_cast<u32x4*>(&slab[buf][m][col * Gm::kTrStride + piece]) = S.pre[u];
+      *reinterpret_cast<u32x4*>(&slab[buf][m][col * Gm::kTrStride + piece]) =
+          (S.ok >> u) & 1u ? S.pre[u] : u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < kChunk) {
-      stat[buf][tid] = S.stat;
-      cmask[buf][tid] = S.mask;
+      const bool ok = (S.ok >> kPer) & 1u;
+      stat[buf][tid] = ok ? S.stat : float2{0.f, 0.f};
+      cmask[buf][tid] = ok ? S.mask : uint2{0u, 0u};
     }
   };
   auto compute = [&](int cur) {
@@ -539,7 +546,7 @@ __global__ void __launch_bounds__(64 * kWaves)
     for (int r = 0; r < 4; ++r) {
       const float2 st2 = stat[cur][4 * g + r];
       const uint2 mk = cmask[cur][4 * g + r];
-      lse2[r] = st2.x;
+      lse2[r] = st2.x * kLog2e;
       dl[r] = st2.y;
       on[r] = ((kbit < 32 ? mk.x >> kbit : mk.y >> (kbit - 32)) & 1u) != 0;
     }
@@ -587,23 +594,28 @@ __global__ void __launch_bounds__(64 * kWaves)
     for (int e = tid; e < n_rec; e += kThreads) recs[e] = segs[c0 + e];
     __syncthreads();
     const int32_t n_batches = (n_rec + rows_per_batch - 1) / rows_per_batch;
+    // Fetches run unconditionally (past the last batch they read in-range
+    // rows that are never stashed): with the same loads in flight on every
+    // path, the wait before a stash covers that stage's loads only, not the
+    // other stage's, which stay in flight across the batch.
     fetch(A, 0);
     stash(A, 0);
-    if (n_batches > 1) fetch(A, rows_per_batch);
-    if (n_batches > 2) fetch(B, 2 * rows_per_batch);
+    fetch(A, rows_per_batch);
+    fetch(B, 2 * rows_per_batch);
     __syncthreads();
     // X holds batch bi + 1 (the other stage holds bi + 2); the two stages swap roles every batch.
     auto step = [&](int32_t bi, Stage& X) {
       const int cur = bi & 1;
       compute(cur);
       if (bi + 1 < n_batches) stash(X, cur ^ 1);  // the other buffer was last read before the previous barrier
-      if (bi + 3 < n_batches) fetch(X, (bi + 3) * rows_per_batch);
+      fetch(X, (bi + 3) * rows_per_batch);
       __syncthreads();
     };
     for (int32_t bi = 0; bi < n_batches; bi += 2) {  // workgroup-uniform
       step(bi, A);
       if (bi + 1 < n_batches) step(bi + 1, B);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // the fetches past the last batch land before the next chunk reuses the stages
   }
 
   if (n_parts > 1) {

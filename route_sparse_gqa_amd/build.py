@@ -27,6 +27,7 @@ SOURCES = [
     "membership_tiles.hip",
     "gather_attention.hip",
     "attention_backward.hip",
+    "dkdv.hip",
     "key_segments.hip",
     "tile_lists.hip",
     "route_select.hip",
@@ -43,11 +44,19 @@ COMMON_FLAGS = [
     "-Wall",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in ordinary VGPRs: the online-softmax rescale then needs
-    # no AGPR round trips and the attention kernel fits two waves per SIMD
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
 ]
+
+# MFMA accumulators in ordinary VGPRs: the online-softmax rescale then needs no
+# AGPR round trips and the attention kernel fits two waves per SIMD.  dkdv.hip
+# keeps them in AGPRs: its dK/dV sums only accumulate, and the freed VGPRs let
+# the compiler read the staged operands ahead of the matrix instructions.
+VGPR_FORM_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_FORM_SOURCES = {"dkdv.hip"}
+
+
+def flags_for(src: str) -> list:
+    return COMMON_FLAGS + ([] if os.path.basename(src) in AGPR_FORM_SOURCES else VGPR_FORM_FLAGS)
 
 
 def hipcc() -> str:
@@ -59,7 +68,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags_for(src), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

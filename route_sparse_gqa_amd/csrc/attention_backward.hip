@@ -13,7 +13,8 @@
 // p is recomputed from the forward's log-sum-exp: p_j = exp(s_j - lse).
 //
 // Two kernels, both deterministic (each sum is taken in a fixed order; no
-// floating-point atomics), which is the part the pages leave unsupported:
+// floating-point atomics), which is the part the pages leave unsupported (the
+// second lives in dkdv.hip, built with its MFMA accumulators in AGPRs):
 //  * dq_kernel: one wavefront per (b, i, hk) unit, mapped like the forward
 //    (one KV head per XCD).  It gathers the unit's routed K and V rows in
 //    16-key chunks through the wave's LDS slabs, recomputes S^T = K Q^T and
@@ -38,26 +39,16 @@
 
 #include <algorithm>
 
+#include "backward_geometry.h"
 #include "device_common.h"
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
 
-constexpr int kWaves = 4;   // work units per workgroup
-constexpr int kChunk = 16;  // keys per dq iteration; keys per dkdv tile; MFMA rows per dkdv batch
-constexpr int kRecChunk = 1024;  // segment records staged in LDS at a time by dkdv
-
-template <int D>
-struct Geo {
-  static constexpr int kSteps = D / 32;                 // 32-dim k-steps of the score products
-  static constexpr int kDimTiles = D / 16;              // 16-dim output tiles
-  static constexpr int kLanesPerRow = D / 8;            // 16-byte pieces per row
-  static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
-  static constexpr int kLoads = kChunk / kRowsPerLoad;  // load instructions per 16 rows
-  static constexpr int kTrStride = D + 16;              // slabs read transposed: 2D + 32 bytes per row
-  static constexpr int kRowStride = D + 8;              // slabs read by rows only: 2D + 16 bytes per row
-};
+using bwd::Geo;
+using bwd::kChunk;
+using bwd::kWaves;
 
 // ---------------------------------------------------------------------------
 // dq (and delta)
@@ -407,313 +398,6 @@ __global__ void __launch_bounds__(64 * kWaves) dq_combine_kernel(const DqArgs a)
   dq_combine_unit<D>(a, static_cast<int64_t>(blockIdx.x) * kWaves + wave, threadIdx.x & 63);
 }
 
-// ---------------------------------------------------------------------------
-// dk, dv
-// ---------------------------------------------------------------------------
-
-template <int D>
-__global__ void __launch_bounds__(64 * kWaves)
-    dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                const uint16_t* __restrict__ dout, int64_t qs0, int64_t qs1, int64_t qs2, int64_t ks0, int64_t ks1,
-                int64_t ks2, int64_t vs0, int64_t vs1, int64_t vs2, int64_t gs0, int64_t gs1, int64_t gs2,
-                const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ seg_start,
-                const int4* __restrict__ segs, const int32_t* __restrict__ part_start,
-                const int32_t* __restrict__ slot_start, const int32_t* __restrict__ plan, int64_t S_q, int64_t S_kv,
-                int64_t Hq, int64_t Hkv, int G, int rows_per_batch, int64_t n_kt, int64_t n_tiles, float scale_log2e,
-                float scale, float* __restrict__ partial, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-  using Gm = Geo<D>;
-  constexpr int kThreads = 64 * kWaves;
-  constexpr int kPieces = 2 * kChunk * Gm::kLanesPerRow;  // 16-byte pieces of Q and dO per batch
-  constexpr int kPer = kPieces / kThreads;                  // per thread
-  static_assert(kPer * kThreads == kPieces, "staging must split evenly over the workgroup");
-  // Double-buffered staging of one batch: Q and dO of its 16 (row, head)
-  // columns, and per column (lse2, delta) and the 64-bit key mask.
-  __shared__ __attribute__((aligned(16))) uint16_t slab[2][2][kChunk * Gm::kTrStride];
-  __shared__ float2 stat[2][kChunk];
-  __shared__ uint2 cmask[2][kChunk];
-  __shared__ int4 recs[kRecChunk];  // segment records of the part (a chunk at a time)
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t x = blockIdx.x;
-  const int64_t hk = x % Hkv;  // one KV head per XCD
-  // Work item of this workgroup: part f of the split (parts numbered tile by tile).
-  const int32_t f = static_cast<int32_t>(x / Hkv);
-  if (f >= plan[1]) return;  // uniform over the workgroup
-  int64_t lo = 0, hi = n_tiles;  // the tile u with part_start[u] <= f < part_start[u + 1]
-  while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) / 2;
-    if (part_start[mid] <= f) lo = mid; else hi = mid;
-  }
-  const int64_t unit = lo;  // b * n_kt + 64-key tile
-  const int32_t part = f - part_start[unit];
-  const int32_t n_parts = part_start[unit + 1] - part_start[unit];
-  const int32_t part_len = plan[0];
-  const int64_t b = unit / n_kt;
-  const int kbit = 16 * wave + (lane & 15);         // this lane's key within the 64-key tile
-  const int64_t key0 = (unit % n_kt) * 64 + 16 * wave;  // this wave's first key
-  const int c = lane & 15;  // key (N side); col / dim row within a 16-tile
-  const int g = lane >> 4;
-
-  // K and V of the wave's 16 keys as B operands: lane (c, g) holds key c, dims 32s + 8g .. +7.
-  bf16x8 kf[Gm::kSteps], vf[Gm::kSteps];
-  {
-    const int64_t key = min(key0 + c, S_kv - 1);
-    const uint16_t* kp = k + b * ks0 + key * ks1 + hk * ks2 + 8 * g;
-    const uint16_t* vp = v + b * vs0 + key * vs1 + hk * vs2 + 8 * g;
-#pragma unroll
-    for (int s = 0; s < Gm::kSteps; ++s) {
-      kf[s] = __builtin_bit_cast(bf16x8, load16(kp + 32 * s));
-      vf[s] = __builtin_bit_cast(bf16x8, load16(vp + 32 * s));
-    }
-  }
-  f32x4 acc_k[Gm::kDimTiles], acc_v[Gm::kDimTiles];
-#pragma unroll
-  for (int t = 0; t < Gm::kDimTiles; ++t) acc_k[t] = acc_v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int cols = rows_per_batch * G;  // MFMA rows in use: (row slot, head) = (col / G, col % G)
-  const int32_t s_begin = seg_start[unit] + part * part_len;
-  const int32_t s_end = min(seg_start[unit + 1], s_begin + part_len);
-  const int64_t q_head0 = hk * G;
-  const int32_t row_max = static_cast<int32_t>(S_q - 1);
-
-  // The part's segment records are staged in LDS (kRecChunk at a time), so a
-  // batch's loads take their addresses from LDS and never wait on another
-  // global load.  Batches then flow through two register stages (loads of
-  // batches i + 1 and i + 2 in flight while batch i is computed) into a
-  // double-buffered LDS slab.
-  // Every load is issued unconditionally from an in-range address (a column
-  // past the batch reads the chunk's last record's row) and masked when the
-  // stage is written to LDS: a load under a divergent branch would make the
-  // compiler wait for it at the branch's join, i.e. at once.
-  struct Stage {
-    u32x4 pre[kPer];
-    float2 stat;
-    uint2 mask;
-    uint32_t ok;  // bit u: pre[u] is a batch column; bit kPer: stat and mask are
-  };
-  int32_t n_rec = 0;  // records staged for the current chunk (>= 1 while batches run)
-  auto fetch = [&](Stage& S, int32_t sb) {  // sb: first record of the batch, within the chunk
-    uint32_t ok_bits = 0;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int pc = tid + kThreads * u;
-      const int m = pc / (kChunk * Gm::kLanesPerRow);  // 0: Q, 1: dO
-      const int col = (pc / Gm::kLanesPerRow) % kChunk;
-      const int piece = 8 * (pc % Gm::kLanesPerRow);
-      const int slot = col / G;
-      const bool ok = col < cols && sb + slot < n_rec;
-      const int32_t ir = min(max(recs[min(sb + slot, n_rec - 1)].x, 0), row_max);
-      const int64_t h = q_head0 + col % G;
-      const uint16_t* src = m == 0 ? q + b * qs0 + ir * qs1 + h * qs2 : dout + b * gs0 + ir * gs1 + h * gs2;
-      S.pre[u] = load16(src + piece);
-      ok_bits |= ok ? 1u << u : 0u;
-    }
-    {
-      const int col = tid % kChunk;  // only threads below kChunk stash it
-      const int slot = col / G;
-      const bool ok = tid < kChunk && col < cols && sb + slot < n_rec;
-      const int4 e = recs[min(sb + slot, n_rec - 1)];
-      const int64_t idx = (b * S_q + min(max(e.x, 0), row_max)) * Hq + q_head0 + col % G;
-      S.stat = float2{lse[idx], delta[idx]};  // raw: any arithmetic here would wait for the loads
-      S.mask = uint2{static_cast<uint32_t>(e.y), static_cast<uint32_t>(e.z)};
-      ok_bits |= ok ? 1u << kPer : 0u;
-    }
-    S.ok = ok_bits;
-  };
-  auto stash = [&](const Stage& S, int buf) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int pc = tid + kThreads * u;
-      const int m = pc / (kChunk * Gm::kLanesPerRow);
-      const int col = (pc / Gm::kLanesPerRow) % kChunk;
-      const int piece = 8 * (pc % Gm::kLanesPerRow);
-      *reinterpret_cast<u32x4*>(&slab[buf][m][col * Gm::kTrStride + piece]) =
-          (S.ok >> u) & 1u ? S.pre[u] : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < kChunk) {
-      const bool ok = (S.ok >> kPer) & 1u;
-      stat[buf][tid] = ok ? S.stat : float2{0.f, 0.f};
-      cmask[buf][tid] = ok ? S.mask : uint2{0u, 0u};
-    }
-  };
-  auto compute = [&](int cur) {
-    // Per-column statistics for this lane's columns 4g .. 4g+3 and key c.
-    float lse2[4], dl[4];
-    bool on[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float2 st2 = stat[cur][4 * g + r];
-      const uint2 mk = cmask[cur][4 * g + r];
-      lse2[r] = st2.x * kLog2e;
-      dl[r] = st2.y;
-      on[r] = ((kbit < 32 ? mk.x >> kbit : mk.y >> (kbit - 32)) & 1u) != 0;
-    }
-    // Waves whose 16 keys no row of the batch routes skip the products.
-    if (__ballot(on[0] || on[1] || on[2] || on[3])) {
-      const uint16_t* my_q = slab[cur][0];
-      const uint16_t* my_g = slab[cur][1];
-      // S[col 4g + r][key c] = Q K^T and dP = dO V^T; A operands are slab rows
-      // (col c, dims 32s + 8g .. +7).
-      f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* qa = my_q + c * Gm::kTrStride + 8 * g;
-      const uint16_t* ga = my_g + c * Gm::kTrStride + 8 * g;
-#pragma unroll
-      for (int s = 0; s < Gm::kSteps; ++s) {
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(qa + 32 * s)), kf[s], st, 0, 0,
-                                                     0);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(ga + 32 * s)), vf[s], dp, 0, 0,
-                                                     0);
-      }
-      bf16x4 pb, dsb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = on[r] ? exp2f(st[r] * scale_log2e - lse2[r]) : 0.f;
-        pb[r] = static_cast<__bf16>(p);
-        dsb[r] = static_cast<__bf16>(p * (dp[r] - dl[r]));
-      }
-      const i16x4 pi = __builtin_bit_cast(i16x4, pb);
-      const i16x4 di = __builtin_bit_cast(i16x4, dsb);
-      // dV^T += dO^T P and dK^T += Q^T dS: the transposed reads give lane (c, g)
-      // columns 4g .. 4g+3 of dim 16t + c, matching its four P / dS values.
-      const uint16_t* qtr = my_q + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
-      const uint16_t* gtr = my_g + (lane >> 2) * Gm::kTrStride + 4 * (lane & 3);
-#pragma unroll
-      for (int t = 0; t < Gm::kDimTiles; ++t) {
-        acc_v[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(gtr + 16 * t), pi, acc_v[t], 0, 0, 0);
-        acc_k[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr(qtr + 16 * t), di, acc_k[t], 0, 0, 0);
-      }
-    }
-  };
-
-  Stage A, B;
-  for (int32_t c0 = s_begin; c0 < s_end; c0 += kRecChunk) {
-    n_rec = min(s_end - c0, static_cast<int32_t>(kRecChunk));
-    __syncthreads();  // the previous chunk's records and slabs are no longer read
-    for (int e = tid; e < n_rec; e += kThreads) recs[e] = segs[c0 + e];
-    __syncthreads();
-    const int32_t n_batches = (n_rec + rows_per_batch - 1) / rows_per_batch;
-    // Fetches run unconditionally (past the last batch they read in-range
-    // rows that are never stashed): with the same loads in flight on every
-    // path, the wait before a stash covers that stage's loads only, not the
-    // other stage's, which stay in flight across the batch.
-    fetch(A, 0);
-    stash(A, 0);
-    fetch(A, rows_per_batch);
-    fetch(B, 2 * rows_per_batch);
-    __syncthreads();
-    // X holds batch bi + 1 (the other stage holds bi + 2); the two stages swap roles every batch.
-    auto step = [&](int32_t bi, Stage& X) {
-      const int cur = bi & 1;
-      compute(cur);
-      if (bi + 1 < n_batches) stash(X, cur ^ 1);  // the other buffer was last read before the previous barrier
-      fetch(X, (bi + 3) * rows_per_batch);
-      __syncthreads();
-    };
-    for (int32_t bi = 0; bi < n_batches; bi += 2) {  // workgroup-uniform
-      step(bi, A);
-      if (bi + 1 < n_batches) step(bi + 1, B);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // the fetches past the last batch land before the next chunk reuses the stages
-  }
-
-  if (n_parts > 1) {
-    // One part of a split tile: fp32 partial sums in the lane-native layout
-    // [slot][hk][wave][dk tiles, dv tiles][lane][4], reduced in part order later.
-    float* dst = partial + (((static_cast<int64_t>(slot_start[unit]) + part) * Hkv + hk) * kWaves + wave) *
-                               (2 * Gm::kDimTiles * 256);
-#pragma unroll
-    for (int t = 0; t < Gm::kDimTiles; ++t) {
-      *reinterpret_cast<f32x4*>(dst + (t * 64 + lane) * 4) = acc_k[t];
-      *reinterpret_cast<f32x4*>(dst + ((Gm::kDimTiles + t) * 64 + lane) * 4) = acc_v[t];
-    }
-    return;
-  }
-  // Lane (c, g) holds dims 16t + 4g .. +3 of key key0 + c.
-  if (key0 + c < S_kv) {
-    const int64_t off = ((b * S_kv + key0 + c) * Hkv + hk) * D + 4 * g;
-#pragma unroll
-    for (int t = 0; t < Gm::kDimTiles; ++t) {
-      bf16x4 wk, wv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        wk[r] = static_cast<__bf16>(acc_k[t][r] * scale);
-        wv[r] = static_cast<__bf16>(acc_v[t][r]);
-      }
-      *reinterpret_cast<u32x2*>(dk + off + 16 * t) = __builtin_bit_cast(u32x2, wk);
-      *reinterpret_cast<u32x2*>(dv + off + 16 * t) = __builtin_bit_cast(u32x2, wv);
-    }
-  }
-}
-
-// Split tiles: sum the parts' partial sums in part order (a fixed order, so
-// the result is deterministic) and write dk and dv.  One workgroup per
-// (b, 64-key tile, hk, key group w of dkdv_kernel's wave w); its four waves
-// each sum a quarter of the group's dk and dv slices, two parts' loads in
-// flight at a time.  Tiles that were not split were written by dkdv_kernel.
-template <int D>
-__global__ void __launch_bounds__(64 * kWaves)
-    dkdv_reduce_kernel(const int32_t* __restrict__ part_start, const int32_t* __restrict__ slot_start,
-                       const float* __restrict__ partial, int64_t S_kv, int64_t Hkv, int64_t n_kt, int64_t n_tiles,
-                       float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
-  using Gm = Geo<D>;
-  constexpr int kSlices = 2 * Gm::kDimTiles;  // dk tiles, then dv tiles, per key group
-  constexpr int kMine = kSlices / kWaves;     // slices per wave: this wave sums slices wave + kWaves * j
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  int64_t x = blockIdx.x;
-  const int64_t hk = x % Hkv;
-  x /= Hkv;
-  const int w = static_cast<int>(x % kWaves);  // key group: keys 16w .. 16w+15 of the tile
-  const int64_t unit = x / kWaves;
-  if (unit >= n_tiles) return;
-  const int32_t n_parts = part_start[unit + 1] - part_start[unit];
-  if (n_parts <= 1) return;
-  const int64_t b = unit / n_kt;
-  const int64_t key0 = (unit % n_kt) * 64 + 16 * w;
-  const int c = lane & 15;
-  const int g = lane >> 4;
-  auto part_ptr = [&](int32_t p) {
-    return partial + (((static_cast<int64_t>(slot_start[unit]) + p) * Hkv + hk) * kWaves + w) * (kSlices * 256) +
-           lane * 4;
-  };
-  f32x4 acc[kMine];
-#pragma unroll
-  for (int j = 0; j < kMine; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int32_t p = 0;
-  for (; p + 1 < n_parts; p += 2) {  // parts p and p + 1 loaded together, added in order
-    const float* s0 = part_ptr(p);
-    const float* s1 = part_ptr(p + 1);
-    f32x4 a0[kMine], a1[kMine];
-#pragma unroll
-    for (int j = 0; j < kMine; ++j) {
-      a0[j] = *reinterpret_cast<const f32x4*>(s0 + (wave + kWaves * j) * 256);
-      a1[j] = *reinterpret_cast<const f32x4*>(s1 + (wave + kWaves * j) * 256);
-    }
-#pragma unroll
-    for (int j = 0; j < kMine; ++j) acc[j] = (acc[j] + a0[j]) + a1[j];
-  }
-  if (p < n_parts) {
-    const float* s0 = part_ptr(p);
-#pragma unroll
-    for (int j = 0; j < kMine; ++j) acc[j] += *reinterpret_cast<const f32x4*>(s0 + (wave + kWaves * j) * 256);
-  }
-  if (key0 + c < S_kv) {
-    const int64_t off = ((b * S_kv + key0 + c) * Hkv + hk) * D + 4 * g;
-#pragma unroll
-    for (int j = 0; j < kMine; ++j) {
-      const int slice = wave + kWaves * j;
-      const bool is_k = slice < Gm::kDimTiles;
-      const int t = is_k ? slice : slice - Gm::kDimTiles;
-      bf16x4 o;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = static_cast<__bf16>(is_k ? acc[j][r] * scale : acc[j][r]);
-      *reinterpret_cast<u32x2*>((is_k ? dk : dv) + off + 16 * t) = __builtin_bit_cast(u32x2, o);
-    }
-  }
-}
-
 bool narrow_offsets(const BwdArgs& a) {
   const int64_t lim = (int64_t{1} << 32) - 1;
   if (a.ks[1] < 0 || a.vs[1] < 0) return false;
@@ -784,25 +468,6 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
 }
 
 template <int D>
-hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t stream) {
-  const int64_t n_kt = (a.S_kv + 63) / 64;
-  const int64_t n_tiles = a.B * n_kt;
-  // Parts never exceed n_tiles + max_parts; workgroups past the planned count exit.
-  const int64_t blocks = (n_tiles + a.max_parts) * a.Hkv;
-  const int G = static_cast<int>(a.Hq / a.Hkv);
-  hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0, stream, a.q, a.k,
-                     a.v, a.dout, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0], a.vs[1], a.vs[2],
-                     a.gs[0], a.gs[1], a.gs[2], a.lse, a.delta, a.seg_start, a.segs, a.part_start, a.slot_start,
-                     a.plan, a.S_q, a.S_kv, a.Hq, a.Hkv, G, kChunk / G, n_kt, n_tiles, a.scale * kLog2e, a.scale,
-                     a.partial, a.dk, a.dv);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3(static_cast<uint32_t>(n_tiles * kWaves * a.Hkv)), dim3(64 * kWaves), 0,
-                     stream, a.part_start, a.slot_start, a.partial, a.S_kv, a.Hkv, n_kt, n_tiles, a.scale, a.dk, a.dv);
-  return hipGetLastError();
-}
-
-template <int D>
 hipError_t launch_dq_any(const BwdArgs& a, hipStream_t stream) {
   return narrow_offsets(a) ? launch_dq_d<D, true>(a, stream) : launch_dq_d<D, false>(a, stream);
 }
@@ -814,15 +479,6 @@ hipError_t launch_attention_dq(const BwdArgs& a, hipStream_t stream) {
     case 64: return launch_dq_any<64>(a, stream);
     case 128: return launch_dq_any<128>(a, stream);
     case 256: return launch_dq_any<256>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_attention_dkdv(const BwdArgs& a, hipStream_t stream) {
-  switch (a.D) {
-    case 64: return launch_dkdv_d<64>(a, stream);
-    case 128: return launch_dkdv_d<128>(a, stream);
-    case 256: return launch_dkdv_d<256>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

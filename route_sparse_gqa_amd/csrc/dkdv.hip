@@ -39,7 +39,7 @@ using bwd::kChunk;
 using bwd::kWaves;
 constexpr int kRecChunk = 1024;  // segment records staged in LDS at a time
 
-template <int D>
+template <int D, bool kNarrow>
 __global__ void __launch_bounds__(64 * kWaves)
     dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                 const uint16_t* __restrict__ dout, int64_t qs0, int64_t qs1, int64_t qs2, int64_t ks0, int64_t ks1,
@@ -111,32 +111,38 @@ __global__ void __launch_bounds__(64 * kWaves)
   // global load.  Batches then flow through two register stages (loads of
   // batches i + 1 and i + 2 in flight while batch i is computed) into a
   // double-buffered LDS slab.
-  // Every load is issued unconditionally from an in-range address (a column
-  // past the batch reads the chunk's last record's row) and masked when the
-  // stage is written to LDS: a load under a divergent branch would make the
-  // compiler wait for it at the branch's join, i.e. at once.
+  // Every load is issued unconditionally from an in-range address (a load
+  // under a divergent branch would make the compiler wait for it at the
+  // branch's join, i.e. at once).  A column past the batch stages the
+  // chunk's last record's row (finite data) with a cleared key mask, so its
+  // P and dS are exactly zero and it adds nothing.
   struct Stage {
     u32x4 pre[kPer];
     float2 stat;
     uint2 mask;
-    uint32_t ok;  // bit u: pre[u] is a batch column; bit kPer: stat and mask are
+    uint32_t ok;  // stat and mask belong to a batch column
   };
+  // Batch-invariant bases of this thread's staged pieces: Q or dO of head
+  // q_head0 + col % G at the piece's dims; each batch adds its row's offset.
+  const char* src_base[kPer];
+  int64_t src_stride[kPer];  // row stride in bytes
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int pc = tid + kThreads * u;
+    const int m = pc / (kChunk * Gm::kLanesPerRow);  // 0: Q, 1: dO
+    const int col = (pc / Gm::kLanesPerRow) % kChunk;
+    const int piece = 8 * (pc % Gm::kLanesPerRow);
+    const int64_t h = q_head0 + col % G;
+    src_base[u] = reinterpret_cast<const char*>(m == 0 ? q + b * qs0 + h * qs2 : dout + b * gs0 + h * gs2) + 2 * piece;
+    src_stride[u] = 2 * (m == 0 ? qs1 : gs1);
+  }
   int32_t n_rec = 0;  // records staged for the current chunk (>= 1 while batches run)
   auto fetch = [&](Stage& S, int32_t sb) {  // sb: first record of the batch, within the chunk
-    uint32_t ok_bits = 0;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int pc = tid + kThreads * u;
-      const int m = pc / (kChunk * Gm::kLanesPerRow);  // 0: Q, 1: dO
-      const int col = (pc / Gm::kLanesPerRow) % kChunk;
-      const int piece = 8 * (pc % Gm::kLanesPerRow);
-      const int slot = col / G;
-      const bool ok = col < cols && sb + slot < n_rec;
-      const int32_t ir = min(max(recs[min(sb + slot, n_rec - 1)].x, 0), row_max);
-      const int64_t h = q_head0 + col % G;
-      const uint16_t* src = m == 0 ? q + b * qs0 + ir * qs1 + h * qs2 : dout + b * gs0 + ir * gs1 + h * gs2;
-      S.pre[u] = load16(src + piece);
-      ok_bits |= ok ? 1u << u : 0u;
+      const int col = ((tid + kThreads * u) / Gm::kLanesPerRow) % kChunk;
+      const int32_t ir = min(max(recs[min(sb + col / G, n_rec - 1)].x, 0), row_max);
+      S.pre[u] = load16(src_base[u] + RowOffset<kNarrow>::of(ir, src_stride[u]));
     }
     {
       const int col = tid % kChunk;  // only threads below kChunk stash it
@@ -146,9 +152,8 @@ __global__ void __launch_bounds__(64 * kWaves)
       const int64_t idx = (b * S_q + min(max(e.x, 0), row_max)) * Hq + q_head0 + col % G;
       S.stat = float2{lse[idx], delta[idx]};  // raw: any arithmetic here would wait for the loads
       S.mask = uint2{static_cast<uint32_t>(e.y), static_cast<uint32_t>(e.z)};
-      ok_bits |= ok ? 1u << kPer : 0u;
+      S.ok = ok ? 1u : 0u;
     }
-    S.ok = ok_bits;
   };
   auto stash = [&](const Stage& S, int buf) {
 #pragma unroll
@@ -157,11 +162,10 @@ __global__ void __launch_bounds__(64 * kWaves)
       const int m = pc / (kChunk * Gm::kLanesPerRow);
       const int col = (pc / Gm::kLanesPerRow) % kChunk;
       const int piece = 8 * (pc % Gm::kLanesPerRow);
-      *reinterpret_cast<u32x4*>(&slab[buf][m][col * Gm::kTrStride + piece]) =
-          (S.ok >> u) & 1u ? S.pre[u] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&slab[buf][m][col * Gm::kTrStride + piece]) = S.pre[u];
     }
     if (tid < kChunk) {
-      const bool ok = (S.ok >> kPer) & 1u;
+      const bool ok = S.ok != 0u;
       stat[buf][tid] = ok ? S.stat : float2{0.f, 0.f};
       cmask[buf][tid] = ok ? S.mask : uint2{0u, 0u};
     }
@@ -197,7 +201,8 @@ __global__ void __launch_bounds__(64 * kWaves)
       bf16x4 pb, dsb;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = on[r] ? exp2f(st[r] * scale_log2e - lse2[r]) : 0.f;
+        // hardware exp2 (v_exp_f32): p is rounded to bf16 right after
+        const float p = on[r] ? __builtin_amdgcn_exp2f(st[r] * scale_log2e - lse2[r]) : 0.f;
         pb[r] = static_cast<__bf16>(p);
         dsb[r] = static_cast<__bf16>(p * (dp[r] - dl[r]));
       }
@@ -342,6 +347,14 @@ __global__ void __launch_bounds__(64 * kWaves)
   }
 }
 
+// True when every Q and dO row lies within 4 GiB of its (batch, head) base,
+// so the staged rows' offsets can be formed in 32 bits.
+bool narrow_rows(const BwdArgs& a) {
+  const int64_t lim = (int64_t{1} << 32) - 1;
+  if (a.qs[1] < 0 || a.gs[1] < 0) return false;
+  return (a.S_q - 1) * a.qs[1] * 2 <= lim && (a.S_q - 1) * a.gs[1] * 2 <= lim;
+}
+
 template <int D>
 hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t stream) {
   const int64_t n_kt = (a.S_kv + 63) / 64;
@@ -349,8 +362,9 @@ hipError_t launch_dkdv_d(const BwdArgs& a, hipStream_t stream) {
   // Parts never exceed n_tiles + max_parts; workgroups past the planned count exit.
   const int64_t blocks = (n_tiles + a.max_parts) * a.Hkv;
   const int G = static_cast<int>(a.Hq / a.Hkv);
-  hipLaunchKernelGGL((dkdv_kernel<D>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0, stream, a.q, a.k,
-                     a.v, a.dout, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0], a.vs[1], a.vs[2],
+  auto kernel = narrow_rows(a) ? dkdv_kernel<D, true> : dkdv_kernel<D, false>;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0, stream, a.q, a.k, a.v,
+                     a.dout, a.qs[0], a.qs[1], a.qs[2], a.ks[0], a.ks[1], a.ks[2], a.vs[0], a.vs[1], a.vs[2],
                      a.gs[0], a.gs[1], a.gs[2], a.lse, a.delta, a.seg_start, a.segs, a.part_start, a.slot_start,
                      a.plan, a.S_q, a.S_kv, a.Hq, a.Hkv, G, kChunk / G, n_kt, n_tiles, a.scale * kLog2e, a.scale,
                      a.partial, a.dk, a.dv);

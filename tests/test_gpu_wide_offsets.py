@@ -16,7 +16,9 @@ reach the wide path are exercised through the C ABI:
 The result must meet the BF16 tolerance against the fp64 oracle on the
 unreversed, contiguous tensors, and be bitwise equal to the result of the
 same call on contiguous copies (the narrow path), since only the addressing
-differs.  The backward (dq, dk, dv) is checked the same way.
+differs.  The backward (dq, dk, dv) is checked the same way, with K and V
+stored those ways and, separately, with Q and dO stored those ways (the
+dk/dv kernel forms its staged query rows' offsets by the same rule).
 """
 
 from __future__ import annotations
@@ -118,6 +120,11 @@ def test_forward_wide_offsets(case, how):
     check_forward(gpu_bf16_bits(wide), ref, ocnt, v, f"wide forward {how} {case}")
 
 
+def _addr(x):
+    """(pointer, strides) of a tensor or of a KVLayout (any [B, S, H, D] bf16 array stored one of three ways)."""
+    return (x.ptr, x.strides) if isinstance(x, KVLayout) else (x.data_ptr(), tuple(x.stride()))
+
+
 def _backward(q, kl: KVLayout, vl: KVLayout, out, dout, lse, lst, cnt, shape, scale):
     B, S_q, S_kv, Hq, Hkv, D, K = shape
     dq = torch.empty((B, S_q, Hq, D), dtype=torch.bfloat16, device=device())
@@ -125,9 +132,10 @@ def _backward(q, kl: KVLayout, vl: KVLayout, out, dout, lse, lst, cnt, shape, sc
     dv = torch.empty_like(dk)
     ws_bytes = qsa.qsa_backward_workspace_size(B, S_q, S_kv, Hq, Hkv, D, K)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device())
+    (q_ptr, q_st), (g_ptr, g_st) = _addr(q), _addr(dout)
     st = qsa.lib().qsa_backward(
-        _p(q.data_ptr()), _strides(q.stride()), _p(kl.ptr), _strides(kl.strides), _p(vl.ptr), _strides(vl.strides),
-        _p(out.data_ptr()), _p(dout.data_ptr()), _strides(dout.stride()), _p(lse.data_ptr()), _p(lst.data_ptr()),
+        _p(q_ptr), _strides(q_st), _p(kl.ptr), _strides(kl.strides), _p(vl.ptr), _strides(vl.strides),
+        _p(out.data_ptr()), _p(g_ptr), _strides(g_st), _p(lse.data_ptr()), _p(lst.data_ptr()),
         _p(cnt.data_ptr()), B, S_q, S_kv, Hq, Hkv, D, K, ctypes.c_float(scale), _p(dq.data_ptr()),
         _p(dk.data_ptr()), _p(dv.data_ptr()), _p(ws.data_ptr()), ctypes.c_size_t(ws_bytes), None)
     assert st == 0, qsa.qsa_status_string(st)
@@ -157,6 +165,38 @@ def test_backward_wide_offsets(how):
     from test_gpu_backward import check_grad
 
     dq_ref, dk_ref, dv_ref = oracle.backward(q, k, v, gpu_bf16_bits(dout), r, scale)
+    floor = 1e-3 * float(np.abs(dv_ref).max())
+    check_grad(gpu_bf16_bits(wide[0]), dq_ref, f"dq {how}", floor)
+    check_grad(gpu_bf16_bits(wide[1]), dk_ref, f"dk {how}", floor)
+    check_grad(gpu_bf16_bits(wide[2]), dv_ref, f"dv {how}")
+
+
+@pytest.mark.parametrize("how", ["reversed", "huge"])
+def test_backward_wide_query_rows(how):
+    """Q and dO stored reversed or past 4 GiB: the dk/dv kernel's staged rows take 64-bit offsets (and dq's
+    query reads their 64-bit base); results bitwise equal to contiguous Q and dO, and within tolerance."""
+    case = (1, 300, 200, 16, 2, 256, 60)
+    B, S_q, S_kv, Hq, Hkv, D, K = case
+    print(f"wide-offset backward query rows {how} {case}", flush=True)
+    q, k, v, r = random_small_case(123, B, S_q, S_kv, Hq, Hkv, D, K)
+    scale = 1.0 / math.sqrt(D)
+    lst, cnt, _, _ = qsa.qsa_preprocess(torch.from_numpy(r).to(device()), S_kv)
+    qg = bf16_to_gpu(q)
+    kc, vc = KVLayout(k, "contiguous"), KVLayout(v, "contiguous")
+    lse = torch.empty((B, S_q, Hq), dtype=torch.float32, device=device())
+    out = _forward(qg, kc, vc, lst, cnt, case, scale, lse)
+    dout_bits = random_dout(9, (B, S_q, Hq, D))
+    dout = bf16_to_gpu(dout_bits)
+    ql, gl = KVLayout(q, how), KVLayout(dout_bits, how)
+    assert _uses_wide_offsets(S_q, Hq * D, ql.strides[1]) and _uses_wide_offsets(S_q, Hq * D, gl.strides[1])
+    narrow = _backward(qg, kc, vc, out, dout, lse, lst, cnt, case, scale)
+    wide = _backward(ql, kc, vc, out, gl, lse, lst, cnt, case, scale)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), wide, narrow):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name}: wide and narrow query rows disagree"
+    from test_gpu_backward import check_grad
+
+    dq_ref, dk_ref, dv_ref = oracle.backward(q, k, v, dout_bits, r, scale)
     floor = 1e-3 * float(np.abs(dv_ref).max())
     check_grad(gpu_bf16_bits(wide[0]), dq_ref, f"dq {how}", floor)
     check_grad(gpu_bf16_bits(wide[1]), dk_ref, f"dk {how}", floor)

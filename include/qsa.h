@@ -258,8 +258,8 @@ int qsa_forward_noalloc(const void *q, const int64_t q_strides[4], const void *k
  *   Other arguments as in qsa_forward.
  *
  * Gathered K/V rows are addressed as (ID) x (token stride) from each
- * (batch, head) base: in 32 bits when the token stride is non-negative and
- * (S_kv - 1) * stride * 2 + 2 * D < 2^32 bytes for both K and V, in 64 bits
+ * (batch, head) base: in 32 bits when K and V share a non-negative token
+ * stride and (S_kv - 1) * stride * 2 + 2 * D < 2^32 bytes, in 64 bits
  * otherwise (flex_qsa page, `_membership_flat_offset`: offsets past 2^31).
  */
 int qsa_forward_preprocessed(const void *q, const int64_t q_strides[4], const void *k,

@@ -306,11 +306,21 @@ __global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
   const int32_t id_max = static_cast<int32_t>(a.S_kv - 1);
   auto clamp_id = [&](int32_t xid) { return min(max(xid, 0), id_max); };
   auto load_id = [&](int base) { return lst[min(base + c, n - 1)]; };
-  auto load_rows = [&](const char* base, int64_t stride_b, int32_t id, u32x4* r) {
+  // K and V rows of a chunk; on the 32-bit path K and V share their row
+  // stride, so one offset serves both.
+  auto load_kv = [&](int32_t id, u32x4* kr, u32x4* vr) {
+    int32_t idr[Gm::kLoads];
 #pragma unroll
     for (int u = 0; u < Gm::kLoads; ++u) {
-      const int32_t idr = __shfl(id, u * Gm::kRowsPerLoad + lane / Gm::kLanesPerRow);
-      r[u] = load16(base + RowOffset<kNarrow>::of(idr, stride_b));
+      idr[u] = __shfl(id, u * Gm::kRowsPerLoad + lane / Gm::kLanesPerRow);
+      kr[u] = load16(kb + RowOffset<kNarrow>::of(idr[u], ks1b));
+    }
+#pragma unroll
+    for (int u = 0; u < Gm::kLoads; ++u) {
+      if constexpr (kNarrow)
+        vr[u] = load16(vb + RowOffset<true>::of(idr[u], ks1b));
+      else
+        vr[u] = load16(vb + RowOffset<false>::of(idr[u], vs1b));
     }
   };
 
@@ -318,8 +328,7 @@ __global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
   int32_t raw_next = load_id(kChunk);
   {
     const int32_t id0 = clamp_id(load_id(0));
-    load_rows(kb, ks1b, id0, kr);
-    load_rows(vb, vs1b, id0, vr);
+    load_kv(id0, kr, vr);
   }
   int32_t id_next = clamp_id(raw_next);
 
@@ -351,8 +360,7 @@ __global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
 
     if (more) {
       raw_next = load_id(base + 2 * kChunk);
-      load_rows(kb, ks1b, id_next, kr);
-      load_rows(vb, vs1b, id_next, vr);
+      load_kv(id_next, kr, vr);
     }
 
     // dS^T = P^T (dP^T - delta), P^T = exp2(S^T scale log2e - lse2); keys past n
@@ -361,7 +369,7 @@ __global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool on = head_ok && base + 4 * g + r < n;
-      const float pr = on ? exp2f(st[r] * a.scale_log2e - lse2) : 0.f;
+      const float pr = on ? __builtin_amdgcn_exp2f(st[r] * a.scale_log2e - lse2) : 0.f;  // hardware exp2
       dsb[r] = static_cast<__bf16>(pr * (dpt[r] - dl));
     }
     const i16x4 db = __builtin_bit_cast(i16x4, dsb);
@@ -398,9 +406,11 @@ __global__ void __launch_bounds__(64 * kWaves) dq_combine_kernel(const DqArgs a)
   dq_combine_unit<D>(a, static_cast<int64_t>(blockIdx.x) * kWaves + wave, threadIdx.x & 63);
 }
 
+// True when K and V share a non-negative row stride and every row fits 32-bit
+// byte offsets from its (batch, head) base.
 bool narrow_offsets(const BwdArgs& a) {
   const int64_t lim = (int64_t{1} << 32) - 1;
-  if (a.ks[1] < 0 || a.vs[1] < 0) return false;
+  if (a.ks[1] < 0 || a.vs[1] != a.ks[1]) return false;  // one offset serves K and V
   return (a.S_kv - 1) * a.ks[1] * 2 + 2 * a.D <= lim && (a.S_kv - 1) * a.vs[1] * 2 + 2 * a.D <= lim;
 }
 

@@ -319,23 +319,24 @@ __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const Ker
   auto clamp_id = [&](int32_t x) { return min(max(x, 0), id_max); };
   // Raw route ID of key base + c (tails repeat the last route; clamped later).
   auto load_id = [&](int base) { return lst[min(base + c, n - 1)]; };
-  // K rows of the chunk in 16-byte pieces, two full rows per load
-  // instruction (the pattern the address unit handles best); they reach the
-  // A operand of S^T = K Q^T through this wave's K slab.  Row r's ID lives in
-  // lane r.
-  auto load_k = [&](int32_t id, u32x4* kr) {
+  // K and V rows of the chunk in 16-byte pieces, two full rows per load
+  // instruction (the pattern the address unit handles best); K reaches the A
+  // operand of S^T = K Q^T through this wave's K slab, V the PV product
+  // through the V slab.  Row r's ID lives in lane r.  The 32-bit path is
+  // taken only when K and V share their row stride, so one offset serves both.
+  auto load_kv = [&](int32_t id, u32x4* kr, u32x4* vr) {
+    int32_t idr[Geo::kLoads];
 #pragma unroll
     for (int u = 0; u < Geo::kLoads; ++u) {
-      const int32_t idr = __shfl(id, u * Geo::kRowsPerLoad + lane / Geo::kLanesPerRow);
-      kr[u] = load16(kb + RowOffset<kNarrow>::of(idr, ks1b));
+      idr[u] = __shfl(id, u * Geo::kRowsPerLoad + lane / Geo::kLanesPerRow);
+      kr[u] = load16(kb + RowOffset<kNarrow>::of(idr[u], ks1b));
     }
-  };
-  // V rows of the chunk in 16-byte pieces; row r's ID lives in lane r.
-  auto load_v = [&](int32_t id, u32x4* vr) {
 #pragma unroll
     for (int u = 0; u < Geo::kLoads; ++u) {
-      const int32_t idr = __shfl(id, u * Geo::kRowsPerLoad + lane / Geo::kLanesPerRow);
-      vr[u] = load16(vb + RowOffset<kNarrow>::of(idr, vs1b));
+      if constexpr (kNarrow)
+        vr[u] = load16(vb + RowOffset<true>::of(idr[u], ks1b));
+      else
+        vr[u] = load16(vb + RowOffset<false>::of(idr[u], vs1b));
     }
   };
 
@@ -344,8 +345,7 @@ __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const Ker
   int32_t raw_next = load_id(kChunk);  // issued first: used after the rows below
   {
     const int32_t id0 = clamp_id(load_id(0));
-    load_k(id0, kr);
-    load_v(id0, vr);
+    load_kv(id0, kr, vr);
   }
   int32_t id_next = clamp_id(raw_next);
 
@@ -376,8 +376,7 @@ __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const Ker
     // Prefetch: IDs two chunks ahead first, then the next chunk's K and V rows.
     if (more) {
       raw_next = load_id(base + 2 * kChunk);
-      load_k(id_next, kr);
-      load_v(id_next, vr);
+      load_kv(id_next, kr, vr);
     }
 
     // Online softmax (log2 domain) against a lazily raised reference max.
@@ -398,7 +397,7 @@ __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const Ker
     bf16x4 pf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pf[r] = static_cast<__bf16>(exp2f(x[r] - m_run));
+      pf[r] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[r] - m_run));  // hardware exp2, rounded to bf16
       l_run += static_cast<float>(pf[r]);
     }
     const i16x4 pb = __builtin_bit_cast(i16x4, pf);
@@ -570,10 +569,11 @@ hipError_t launch(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& 
   return hipSuccess;
 }
 
-// True when (S_kv - 1) * row stride + one row fits in 32 bits for both K and V.
+// True when K and V share a non-negative row stride and (S_kv - 1) * stride +
+// one row fits in 32 bits (then one 32-bit offset addresses both rows).
 bool narrow_offsets(const AttnArgs& a) {
   const int64_t lim = (int64_t{1} << 32) - 1;
-  if (a.ks[1] < 0 || a.vs[1] < 0) return false;
+  if (a.ks[1] < 0 || a.vs[1] != a.ks[1]) return false;  // one offset serves K and V
   return (a.S_kv - 1) * a.ks[1] * 2 + 2 * a.D <= lim && (a.S_kv - 1) * a.vs[1] * 2 + 2 * a.D <= lim;
 }
 

@@ -181,8 +181,8 @@ __global__ void __launch_bounds__(64 * kWaves) delta_kernel(const DqArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) dl += bf16_lo(gw[e]) * bf16_lo(ow[e]) + bf16_hi(gw[e]) * bf16_hi(ow[e]);
   }
-  dl += __shfl_xor(dl, 16);
-  dl += __shfl_xor(dl, 32);
+  dl = pair_sum16(dl);
+  dl = pair_sum32(dl);
   if (head_ok && g == 0) a.delta[row * a.Hq + hq] = dl;
 }
 
@@ -285,8 +285,8 @@ __global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
     }
   }
   if constexpr (!kSplit) {
-    dl += __shfl_xor(dl, 16);
-    dl += __shfl_xor(dl, 32);
+    dl = pair_sum16(dl);
+    dl = pair_sum32(dl);
     if (head_ok && g == 0) a.delta[row * Hq + hq] = dl;
   } else {
     dl = head_ok ? a.delta[row * Hq + hq] : 0.f;

@@ -69,6 +69,26 @@ __device__ __forceinline__ void or_slot_run(uint32_t* bits, const int32_t* slots
   if (cur_b != 0u) atomicOr(&bits[cur_w], cur_b);
 }
 
+// Pairwise max / sum of each lane with the lane 16 apart (within its 32-lane
+// half) and with the lane 32 apart, in registers (gfx950 permlane swaps of two
+// copies leave the pair in the two results) instead of through LDS.
+__device__ __forceinline__ float pair_max16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Byte offset of a gathered row: 32-bit when every row of the tensor lies
 // within 4 GiB of its (batch, head) base, else 64-bit.
 template <bool kNarrow>

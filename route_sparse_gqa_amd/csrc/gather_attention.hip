@@ -384,8 +384,8 @@ __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const Ker
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = base + 4 * g + r < n ? st[r] * a.scale_log2e : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));      // finite: the chunk holds at least one key
+    mx = pair_max16(mx);
+    mx = pair_max32(mx);                     // finite: the chunk holds at least one key
     if (__ballot(mx > m_run + kMaxSlack)) {  // wave-uniform; always taken on the first chunk
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - m_new);
@@ -412,8 +412,8 @@ __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const Ker
   }
 
   // Normalise and store: lane holds O[head c][dims 16t + 4g .. +3].
-  float l_tot = l_run + __shfl_xor(l_run, 16);  // butterfly over the four lane groups of head c
-  l_tot += __shfl_xor(l_tot, 32);
+  float l_tot = pair_sum16(l_run);  // butterfly over the four lane groups of head c
+  l_tot = pair_sum32(l_tot);
   const float inv = 1.0f / l_tot;
   // Natural-log log-sum-exp of the scaled scores: the sum is taken against
   // the reference max m_run (log2 domain), from the same bf16-rounded

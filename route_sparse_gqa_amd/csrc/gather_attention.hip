@@ -16,9 +16,10 @@
 //    cross-lane xors.  Routed K and V rows are both gathered two full rows
 //    per 16-byte-per-lane load instruction (fewest cache lines per
 //    instruction for the address unit) and staged in this wave's LDS slabs;
-//    the K slab's 2D + 16 byte stride makes the A-operand reads (lane
-//    (c, g) = (lane % 16, lane / 16) reads dims 32s + 8g .. +7 of key c)
-//    conflict-free.
+//    both slabs have a 2D + 32 byte row stride, with which the bank-conflict
+//    counter reads zero for the row stores, the A-operand reads (lane
+//    (c, g) = (lane % 16, lane / 16) reads dims 32s + 8g .. +7 of key c) and
+//    the transposing V reads.
 //  * PV is computed transposed too, O^T = V^T P^T with
 //    v_mfma_f32_16x16x16_bf16: the four probabilities of a lane are exactly
 //    its B operand (no shuffle) and the online-softmax rescale is
@@ -72,7 +73,7 @@ struct Geometry {
   static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
   static constexpr int kLoads = kChunk / kRowsPerLoad;  // V load instructions per chunk
   static constexpr int kStride = D + 16;                // V slab row stride in bf16 (2D + 32 bytes)
-  static constexpr int kKStride = D + 8;                // K slab row stride in bf16 (2D + 16 bytes)
+  static constexpr int kKStride = D + 16;               // K slab row stride in bf16 (2D + 32 bytes)
 };
 
 struct KernelArgs {
@@ -365,7 +366,7 @@ __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const Ker
     wave_lds_sync();  // K and V rows visible to every lane of this wave
 
     // Scores: lane holds S^T[key 4g + r][head c]; the A operand is key c,
-    // dims 32s + 8g .. +7 (row stride 2D + 16 bytes: conflict-free).
+    // dims 32s + 8g .. +7.
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
     const uint16_t* ka = my_kslab + c * Geo::kKStride + 8 * g;
 #pragma unroll

@@ -73,13 +73,13 @@ struct DqArgs {
   // key-range split (as the forward's): range starts, this pass's rows and fp32 partial sums
   const int32_t* offs;
   int P;
-  int64_t row0, pass_rows, rowgroups;
+  int64_t row0, pass_rows;
   float* part;  // [pass_rows][Hkv][P][G][D]
   // the pass whose partial sums are added up (by dq_combine_kernel, or by the
   // combine workgroups interleaved into the next pass's split launch)
   int64_t comb_row0, comb_pass_rows;
   const float* comb_part;
-  int64_t comb_blocks, comb_stride;  // split launch: workgroup comb_stride * k - 1 adds units 4(k-1) ..
+  int64_t comb_blocks, comb_stride;  // split launch: workgroup comb_stride * k - 1 adds unit k - 1
 };
 
 // Adds the fp32 partial dq of one (row, KV head) unit's ranges in ascending
@@ -192,26 +192,27 @@ __global__ void __launch_bounds__(64 * kWaves) delta_kernel(const DqArgs a) {
 // has routes in no other range writes dq, otherwise an fp32 partial sum that
 // dq_combine_unit adds in ascending range order, in the next pass's launch or
 // on its own after the last pass).
+// One wavefront per workgroup, as the forward's attention kernel: a unit's
+// slot and LDS are released as soon as the unit ends.
 template <int D, bool kNarrow, bool kSplit>
-__global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
+__global__ void __launch_bounds__(64) dq_kernel(const DqArgs a) {
   using Gm = Geo<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t kslab[kWaves][kChunk * Gm::kTrStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vslab[kWaves][kChunk * Gm::kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t kslab[kChunk * Gm::kTrStride];
+  __shared__ __attribute__((aligned(16))) uint16_t vslab[kChunk * Gm::kRowStride];
 
   const int64_t S_q = a.S_q, Hq = a.Hq, Hkv = a.Hkv;
   const int G = a.G;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   int64_t x = blockIdx.x;
   int64_t hk, row, local = 0;
   int p = 0;
   if constexpr (kSplit) {
-    // Every comb_stride-th workgroup adds up four units of the previous pass
+    // Every comb_stride-th workgroup adds up one unit of the previous pass
     // instead, spread evenly over the launch; the others keep their order.
     if (a.comb_blocks > 0) {
       const int64_t k1 = (x + 1) / a.comb_stride;
       if (k1 * a.comb_stride == x + 1 && k1 <= a.comb_blocks) {
-        dq_combine_unit<D>(a, (k1 - 1) * kWaves + wave, lane);
+        dq_combine_unit<D>(a, k1 - 1, lane);
         return;
       }
       x -= min(x / a.comb_stride, a.comb_blocks);
@@ -220,14 +221,12 @@ __global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
   if constexpr (!kSplit) {
     hk = x % Hkv;  // one KV head per XCD, as in the forward
     // Rows from the last to the first, as in the forward: with causal routes the longest start first.
-    row = a.n_rows - 1 - ((x / Hkv) * kWaves + wave);
-    if (row < 0) return;  // the last workgroup's surplus waves; no workgroup barriers in this kernel
+    row = a.n_rows - 1 - x / Hkv;
   } else {
-    const int64_t phase = x / a.rowgroups;  // (range p, KV head hk), rows last to first
+    const int64_t phase = x / a.pass_rows;  // (range p, KV head hk), rows last to first
     p = static_cast<int>(phase / Hkv);
     hk = phase - static_cast<int64_t>(p) * Hkv;
-    local = a.pass_rows - 1 - ((x - phase * a.rowgroups) * kWaves + wave);
-    if (local < 0) return;
+    local = a.pass_rows - 1 - (x - phase * a.pass_rows);
     row = a.row0 + local;
   }
   const int64_t b = row / S_q;
@@ -301,8 +300,8 @@ __global__ void __launch_bounds__(64 * kWaves) dq_kernel(const DqArgs a) {
   const int64_t ks1b = 2 * a.ks1, vs1b = 2 * a.vs1;
   const char* kb = reinterpret_cast<const char*>(a.k + b * a.ks0 + hk * a.ks2) + 16 * (lane % Gm::kLanesPerRow);
   const char* vb = reinterpret_cast<const char*>(a.v + b * a.vs0 + hk * a.vs2) + 16 * (lane % Gm::kLanesPerRow);
-  uint16_t* my_k = kslab[wave];
-  uint16_t* my_v = vslab[wave];
+  uint16_t* my_k = kslab;
+  uint16_t* my_v = vslab;
   const int32_t id_max = static_cast<int32_t>(a.S_kv - 1);
   auto clamp_id = [&](int32_t xid) { return min(max(xid, 0), id_max); };
   auto load_id = [&](int base) { return lst[min(base + c, n - 1)]; };
@@ -434,8 +433,7 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
   k.dq = a.dq;
   k.delta = a.delta;
   if (!a.split.use) {
-    const int64_t blocks = (rows + kWaves - 1) / kWaves * a.Hkv;
-    hipLaunchKernelGGL((dq_kernel<D, kNarrow, false>), dim3(static_cast<uint32_t>(blocks)), dim3(64 * kWaves), 0,
+    hipLaunchKernelGGL((dq_kernel<D, kNarrow, false>), dim3(static_cast<uint32_t>(rows * a.Hkv)), dim3(64), 0,
                        stream, k);
     return hipGetLastError();
   }
@@ -456,22 +454,21 @@ hipError_t launch_dq_d(const BwdArgs& a, hipStream_t stream) {
       k.comb_pass_rows = k.pass_rows;
       k.comb_part = k.part;
     }
-    const int64_t comb_blocks = i > 0 ? (k.comb_pass_rows * a.Hkv + kWaves - 1) / kWaves : 0;
+    const int64_t comb_units = i > 0 ? k.comb_pass_rows * a.Hkv : 0;
     if (i == n_pass) {
-      hipLaunchKernelGGL((dq_combine_kernel<D>), dim3(static_cast<uint32_t>(comb_blocks)), dim3(64 * kWaves), 0,
-                         stream, k);
+      hipLaunchKernelGGL((dq_combine_kernel<D>), dim3(static_cast<uint32_t>((comb_units + kWaves - 1) / kWaves)),
+                         dim3(64 * kWaves), 0, stream, k);
       return hipGetLastError();
     }
     const int64_t r_end = rows - i * a.dq_pass_rows;
     k.row0 = std::max<int64_t>(r_end - a.dq_pass_rows, 0);
     k.pass_rows = r_end - k.row0;
-    k.rowgroups = (k.pass_rows + kWaves - 1) / kWaves;
     k.part = a.dq_part[i & 1];
-    const int64_t split_blocks = k.rowgroups * a.split.P * a.Hkv;
-    k.comb_blocks = comb_blocks;
-    k.comb_stride = comb_blocks > 0 ? (split_blocks + comb_blocks) / comb_blocks : 0;
-    hipLaunchKernelGGL((dq_kernel<D, kNarrow, true>), dim3(static_cast<uint32_t>(split_blocks + comb_blocks)),
-                       dim3(64 * kWaves), 0, stream, k);
+    const int64_t split_blocks = k.pass_rows * a.split.P * a.Hkv;
+    k.comb_blocks = comb_units;
+    k.comb_stride = comb_units > 0 ? (split_blocks + comb_units) / comb_units : 0;
+    hipLaunchKernelGGL((dq_kernel<D, kNarrow, true>), dim3(static_cast<uint32_t>(split_blocks + comb_units)),
+                       dim3(64), 0, stream, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

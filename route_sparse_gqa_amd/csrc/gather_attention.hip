@@ -6,9 +6,9 @@
 // qsa page, `_gathered_qsa_gqa_attention_chunk` (grouped layout
 // [B, Q, Hkv, G, D]: query head h reads KV head h / G).
 //
-// Design (one wavefront per (b, i, hk) work unit, four rows of one KV head
-// per workgroup, mapped so that each XCD serves one KV head, rows taken from
-// the last to the first):
+// Design (one wavefront per (b, i, hk) work unit and per workgroup, mapped
+// so that each XCD serves one KV head, rows taken from the last to the
+// first):
 //  * The G query heads of the unit are the N = 16 columns of the MFMA (zero
 //    padded when G < 16).  Scores are computed transposed, S^T = K Q^T with
 //    v_mfma_f32_16x16x32_bf16, 16 routed keys as the M rows, so each lane
@@ -61,7 +61,7 @@
 namespace qsa {
 namespace {
 
-constexpr int kWaves = 4;   // work units per workgroup
+constexpr int kWaves = 4;   // wavefronts per workgroup of the range-start and combine kernels
 constexpr int kChunk = 16;  // routes per inner iteration (M of S^T, K of PV)
 constexpr float kMaxSlack = 8.0f;  // log2 headroom before the reference max is raised
 
@@ -92,7 +92,7 @@ struct KernelArgs {
   // key-range split
   const int32_t* offs;  // [B * S_q][P + 1] range starts within each row's list
   int P;
-  int64_t row0, pass_rows, rowgroups;  // rows [row0, row0 + pass_rows) of this pass, ceil(pass_rows / 4)
+  int64_t row0, pass_rows;             // rows [row0, row0 + pass_rows) of this pass
   uint16_t* part_o;                    // [pass_rows][Hkv][P][G][D] bf16
   float* part_lse;                     // [pass_rows][Hkv][P][G] fp32, log2 domain
   // the pass whose partials are merged (by the combine kernel, or by the
@@ -100,7 +100,7 @@ struct KernelArgs {
   int64_t comb_row0, comb_pass_rows;
   const uint16_t* comb_part_o;
   const float* comb_part_lse;
-  int64_t comb_blocks, comb_stride;  // split launch: workgroup comb_stride * k - 1 merges units 4(k-1) ..
+  int64_t comb_blocks, comb_stride;  // split launch: workgroup comb_stride * k - 1 merges unit k - 1
 };
 
 // Merges the partial results of one (row, KV head) unit of a split pass
@@ -215,50 +215,52 @@ __device__ __forceinline__ void combine_unit(const KernelArgs& a, int64_t unit, 
   combine_unit<D, 1>(a, unit, lane);
 }
 
+// One wavefront per workgroup: a unit's workgroup slot and LDS are released
+// as soon as its unit ends, and the CU starts the next unit at once.  (Four
+// units per workgroup held the slots of all four until the longest ended;
+// within one key range the units of neighbouring rows differ widely in
+// length.)
 template <int D, bool kNarrow, bool kSplit>
-__global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const KernelArgs a) {
+__global__ void __launch_bounds__(64) gather_attention_kernel(const KernelArgs a) {
   using Geo = Geometry<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t slab[kWaves][kChunk * Geo::kStride];
-  __shared__ __attribute__((aligned(16))) uint16_t kslab[kWaves][kChunk * Geo::kKStride];
+  __shared__ __attribute__((aligned(16))) uint16_t slab[kChunk * Geo::kStride];
+  __shared__ __attribute__((aligned(16))) uint16_t kslab[kChunk * Geo::kKStride];
 
   const int64_t S_q = a.S_q, Hq = a.Hq, Hkv = a.Hkv;
   const int G = a.G;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));  // wave-uniform
   int64_t x = blockIdx.x;
   int64_t hk, row, local = 0;
   int p = 0;
   if constexpr (kSplit) {
-    // Every comb_stride-th workgroup merges four units of the previous pass
+    // Every comb_stride-th workgroup merges one unit of the previous pass
     // instead, spread evenly over the launch; the others keep their order.
     if (a.comb_blocks > 0) {
       const int64_t k1 = (x + 1) / a.comb_stride;
       if (k1 * a.comb_stride == x + 1 && k1 <= a.comb_blocks) {
-        combine_unit<D>(a, (k1 - 1) * kWaves + wave, lane);
+        combine_unit<D>(a, k1 - 1, lane);
         return;
       }
       x -= min(x / a.comb_stride, a.comb_blocks);
     }
   }
   if constexpr (!kSplit) {
-    // Workgroup x -> (KV head x % Hkv, four neighbouring rows): workgroups are
-    // dealt round-robin to the 8 XCDs, so when Hkv divides 8 each XCD serves a
-    // single KV head (half the K/V working set per L2 at Hkv = 2), while rows
-    // still spread evenly over the XCDs.  Rows are taken from the last to the
-    // first: with causal routes later rows route more keys, so the longest
-    // rows start first and the short ones fill the end of the launch.
+    // Workgroup x -> (KV head x % Hkv, row): workgroups are dealt round-robin
+    // to the 8 XCDs, so when Hkv divides 8 each XCD serves a single KV head
+    // (half the K/V working set per L2 at Hkv = 2), while rows still spread
+    // evenly over the XCDs.  Rows are taken from the last to the first: with
+    // causal routes later rows route more keys, so the longest rows start
+    // first and the short ones fill the end of the launch.
     hk = x % Hkv;
-    row = a.n_units / Hkv - 1 - ((x / Hkv) * kWaves + wave);  // b * S_q + i
-    if (row < 0) return;  // the last workgroup's surplus waves; no workgroup barriers in this kernel
+    row = a.n_units / Hkv - 1 - x / Hkv;  // b * S_q + i
   } else {
-    // Workgroup x -> phase x / rowgroups = (range p, KV head hk), then four
-    // rows of the pass, last rows first.  Consecutive workgroups go to all
-    // XCDs in turn, so the XCDs sweep the phases together.
-    const int64_t phase = x / a.rowgroups;
+    // Workgroup x -> phase x / pass_rows = (range p, KV head hk), then a row
+    // of the pass, last rows first.  Consecutive workgroups go to all XCDs in
+    // turn, so the XCDs sweep the phases together.
+    const int64_t phase = x / a.pass_rows;
     p = static_cast<int>(phase / Hkv);
     hk = phase - static_cast<int64_t>(p) * Hkv;
-    local = a.pass_rows - 1 - ((x - phase * a.rowgroups) * kWaves + wave);
-    if (local < 0) return;
+    local = a.pass_rows - 1 - (x - phase * a.pass_rows);
     row = a.row0 + local;
   }
   const int64_t b = row / S_q;
@@ -314,8 +316,8 @@ __global__ void __launch_bounds__(64 * kWaves) gather_attention_kernel(const Ker
   const int64_t ks1b = 2 * a.ks1, vs1b = 2 * a.vs1;  // row strides in bytes
   const char* kb = reinterpret_cast<const char*>(a.k + b * a.ks0 + hk * a.ks2) + 16 * (lane % Geo::kLanesPerRow);
   const char* vb = reinterpret_cast<const char*>(a.v + b * a.vs0 + hk * a.vs2) + 16 * (lane % Geo::kLanesPerRow);
-  uint16_t* my_slab = slab[wave];
-  uint16_t* my_kslab = kslab[wave];
+  uint16_t* my_slab = slab;
+  uint16_t* my_kslab = kslab;
   const int32_t id_max = static_cast<int32_t>(a.S_kv - 1);
   auto clamp_id = [&](int32_t x) { return min(max(x, 0), id_max); };
   // Raw route ID of key base + c (tails repeat the last route; clamped later).
@@ -526,9 +528,8 @@ hipError_t launch(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& 
   KernelArgs k = kernel_args(a);
   const int64_t rows = a.B * a.S_q;
   if (!plan.use) {
-    const int64_t blocks = (rows + kWaves - 1) / kWaves * a.Hkv;
-    hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow, false>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(64 * kWaves), 0, stream, k);
+    hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow, false>), dim3(static_cast<uint32_t>(rows * a.Hkv)),
+                       dim3(64), 0, stream, k);
     return hipGetLastError();
   }
   if (hipError_t e = launch_range_offsets(a.route_list, a.route_count, rows, a.K, a.S_kv, plan, w.offs, stream);
@@ -548,23 +549,22 @@ hipError_t launch(const AttnArgs& a, const SplitPlan& plan, const SplitBuffers& 
       k.comb_part_o = k.part_o;
       k.comb_part_lse = k.part_lse;
     }
-    const int64_t comb_blocks = i > 0 ? (k.comb_pass_rows * a.Hkv + kWaves - 1) / kWaves : 0;
+    const int64_t comb_units = i > 0 ? k.comb_pass_rows * a.Hkv : 0;
     if (i == n_pass) {
-      hipLaunchKernelGGL((range_combine_kernel<D>), dim3(static_cast<uint32_t>(comb_blocks)), dim3(64 * kWaves), 0,
-                         stream, k);
+      hipLaunchKernelGGL((range_combine_kernel<D>), dim3(static_cast<uint32_t>((comb_units + kWaves - 1) / kWaves)),
+                         dim3(64 * kWaves), 0, stream, k);
       return hipGetLastError();
     }
     const int64_t r_end = rows - i * w.pass_rows;
     k.row0 = std::max<int64_t>(r_end - w.pass_rows, 0);
     k.pass_rows = r_end - k.row0;
-    k.rowgroups = (k.pass_rows + kWaves - 1) / kWaves;
     k.part_o = w.part_o[i & 1];
     k.part_lse = w.part_lse[i & 1];
-    const int64_t gather_blocks = k.rowgroups * plan.P * a.Hkv;
-    k.comb_blocks = comb_blocks;
-    k.comb_stride = comb_blocks > 0 ? (gather_blocks + comb_blocks) / comb_blocks : 0;
+    const int64_t gather_blocks = k.pass_rows * plan.P * a.Hkv;
+    k.comb_blocks = comb_units;
+    k.comb_stride = comb_units > 0 ? (gather_blocks + comb_units) / comb_units : 0;
     hipLaunchKernelGGL((gather_attention_kernel<D, kNarrow, true>),
-                       dim3(static_cast<uint32_t>(gather_blocks + comb_blocks)), dim3(64 * kWaves), 0, stream, k);
+                       dim3(static_cast<uint32_t>(gather_blocks + comb_units)), dim3(64), 0, stream, k);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   return hipSuccess;

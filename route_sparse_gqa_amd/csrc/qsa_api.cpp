@@ -150,8 +150,8 @@ bool attention_plan(int64_t B, int64_t S_q, int64_t S_kv, int64_t Hq, int64_t Hk
 // partials need one buffer; else two buffers of a pass), or 0 when fewer than min(rows, kMinPassRows) fit.
 int64_t split_pass_rows(const qsa::SplitPlan& plan, int64_t rows, int64_t Hkv, size_t bytes) {
   if (bytes < static_cast<size_t>(plan.offs_bytes)) return 0;
-  // split launch: ceil(pass / 4) * P * Hkv workgroups, plus ceil(previous pass * Hkv / 4) merging the previous pass
-  const int64_t grid_rows = kMaxGrid / ((plan.P + 1) * Hkv) * 4;
+  // split launch: pass * P * Hkv one-wavefront workgroups, plus previous pass * Hkv merging the previous pass
+  const int64_t grid_rows = qsa::kMaxWaveBlocks / ((plan.P + 1) * Hkv);
   auto fits = [&](int64_t pass) {
     return static_cast<size_t>(qsa::split_workspace_bytes(plan, pass, rows)) <= bytes;
   };
@@ -290,7 +290,7 @@ int check_attention(const void* q, const int64_t q_strides[4], const void* k, co
   if (int st = check_bf16_tensor(v, v_strides)) return st;
   if (!aligned(out, 16)) return QSA_ERR_LAYOUT;
   int64_t units = 0, out_elems = 0;
-  if (!mul_ok(s->rows, Hkv, &units) || (s->rows + 3) / 4 * Hkv > kMaxGrid) return QSA_ERR_LIMIT;
+  if (!mul_ok(s->rows, Hkv, &units) || units > qsa::kMaxWaveBlocks) return QSA_ERR_LIMIT;  // one workgroup per unit
   int64_t row_elems = 0;
   if (!mul_ok(Hq, D, &row_elems) || !mul_ok(s->rows, row_elems, &out_elems) || out_elems > (INT64_MAX >> 2))
     return QSA_ERR_LIMIT;
@@ -545,10 +545,12 @@ QSA_EXPORT int qsa_backward(const void* q, const int64_t q_strides[4], const voi
   if (!bwd_layout(B, S_q, S_kv, Hq, Hkv, D, K, &l)) return QSA_ERR_LIMIT;
   int64_t kv_elems = 0;
   if (!mul_ok(B * S_kv, Hkv * D, &kv_elems) || kv_elems > (INT64_MAX >> 2)) return QSA_ERR_LIMIT;
-  // grids: dk/dv and its reduction, dq (and delta and its combine) per (row, KV head) group of four, the
-  // split dq per (range, KV head, four rows of a pass), the segment counts
+  // grids: dk/dv and its reduction, dq per (row, KV head) in one-wavefront workgroups (delta and the
+  // combine per four of them), the split dq per (range, KV head, row of a pass) plus the previous pass's
+  // (row, KV head) units, the segment counts
   if ((l.n_kt * B + l.max_parts) * Hkv > kMaxGrid || l.n_kt * B * 4 * Hkv > kMaxGrid ||
-      (s.rows + 3) / 4 * Hkv > kMaxGrid || (l.split.use && (l.dq_pass_rows + 3) / 4 * l.split.P * Hkv > kMaxGrid) ||
+      s.rows * Hkv > qsa::kMaxWaveBlocks ||
+      (l.split.use && l.dq_pass_rows * (l.split.P + 1) * Hkv > qsa::kMaxWaveBlocks) ||
       (B * ((S_q + qsa::kSegChunkRows - 1) / qsa::kSegChunkRows) * l.n_kt + 255) / 256 > kMaxGrid)
     return QSA_ERR_LIMIT;
   if (workspace == nullptr || workspace_bytes < l.total || !aligned(workspace, kWorkspaceAlign))

@@ -9,9 +9,11 @@ namespace qsa {
 
 // One launch holds fewer than 2^32 work-items per grid dimension
 // (gridDim.x * blockDim.x); kMaxBlocks is that limit in 256-thread
-// workgroups, the size of most launches here.
+// workgroups, the size of most launches here, kMaxWaveBlocks in
+// one-wavefront workgroups (the attention kernel's).
 constexpr int64_t kMaxLaunchItems = (int64_t{1} << 32) - 1;
 constexpr int64_t kMaxBlocks = kMaxLaunchItems / 256;
+constexpr int64_t kMaxWaveBlocks = kMaxLaunchItems / 64;
 
 // Work-items per query row of the route normalisation launch that K and
 // kv_length select (the host checks B * S_q times it against kMaxLaunchItems).

@@ -154,7 +154,7 @@ def test_launches_beyond_one_grid_are_refused():
     assert L.qsa_preprocess(fake[0], 1, 1, 1 << 22, 8193, sk, 1 << 20, fake[1], fake[2], None, None, None) == -11
     assert _call_forward(S_q=1 << 24) == -11
     assert _call_forward(S_q=1 << 22, K=8193, S_kv=1 << 20) == -11
-    assert _call_forward(S_q=1 << 22, Hq=16, Hkv=16) == -11          # ceil(rows / 4) * Hkv = 2^24 workgroups
+    assert _call_forward(S_q=1 << 22, Hq=16, Hkv=16) == -11          # rows * Hkv = 2^26 wavefronts = 2^32 work-items
     assert _call_backward(S_q=1 << 22, Hq=16, Hkv=16) == -11
     # a top-k row that sees more than 16384 blocks takes a 1024-thread workgroup: at most 2^22 - 1 rows
     assert _call_select(S_q=1 << 22, S_global=1 << 22, c=64, budget=64) == -11

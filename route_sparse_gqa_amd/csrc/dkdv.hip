@@ -244,10 +244,17 @@ __global__ void __launch_bounds__(64 * kWaves)
       fetch(X, (bi + 3) * rows_per_batch);
       __syncthreads();
     };
-    for (int32_t bi = 0; bi < n_batches; bi += 2) {  // workgroup-uniform
+    // Pairs of batches, then the odd last one: every path back to the loop
+    // head then has A's loads issued before B's, which lets the compiler's
+    // wait before a stash cover that stage's loads only.  (A loop that could
+    // also come round after step A alone made it assume either order and
+    // wait for the other stage's first load too.)
+    int32_t bi = 0;
+    for (; bi + 1 < n_batches; bi += 2) {  // workgroup-uniform
       step(bi, A);
-      if (bi + 1 < n_batches) step(bi + 1, B);
+      step(bi + 1, B);
     }
+    if (bi < n_batches) step(bi, A);
     __builtin_amdgcn_s_waitcnt(0);  // the fetches past the last batch land before the next chunk reuses the stages
   }
 

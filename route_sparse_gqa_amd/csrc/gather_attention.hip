@@ -12,8 +12,9 @@
 //  * The G query heads of the unit are the N = 16 columns of the MFMA (zero
 //    padded when G < 16).  Scores are computed transposed, S^T = K Q^T with
 //    v_mfma_f32_16x16x32_bf16, 16 routed keys as the M rows, so each lane
-//    ends up owning one head and four keys; row max/sum reductions are two
-//    cross-lane xors.  Routed K and V rows are both gathered two full rows
+//    ends up owning one head and four keys; a head's max and sum over its
+//    four lane groups are two gfx950 lane swaps (permlane16 and permlane32).
+//    Routed K and V rows are both gathered two full rows
 //    per 16-byte-per-lane load instruction (fewest cache lines per
 //    instruction for the address unit) and staged in this wave's LDS slabs;
 //    both slabs have a 2D + 32 byte row stride, with which the bank-conflict

@@ -66,7 +66,11 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t x, int src) {
 
 // One wavefront per query row.  At the last list entry of each tile run it
 // marks the (row, tile) bit (kFill false) or writes the segment at its rank
-// (kFill true).
+// (kFill true).  The list is read 64 entries at a time, the next chunk's
+// entries (and the entry after it, which decides whether lane 63 ends a
+// run) in flight while the current chunk is processed; the entry after each
+// lane's own comes from its neighbour lane.  The rank's loads (tile start,
+// chunk prefix and the words of the row's chunk) are issued together.
 template <bool kFill>
 __global__ void __launch_bounds__(64 * kWaves)
     row_segments_kernel(const int32_t* __restrict__ route_list, const int32_t* __restrict__ route_count,
@@ -86,40 +90,61 @@ __global__ void __launch_bounds__(64 * kWaves)
   uint32_t* words = bits + b * W * n_kt;  // word (w', t) at words[w' * n_kt + t]
   int32_t carry_tile = -1;                // tile of the run still open at the end of the previous chunk
   uint64_t carry_mask = 0;
+  int32_t raw = n > 0 ? lst[min(lane, n - 1)] : 0;  // this lane's entry of the current chunk
+  int32_t raw_after = n > 0 ? lst[min(64, n - 1)] : 0;  // the entry after the current chunk
   for (int base = 0; base < n; base += 64) {
     const int j = base + lane;
     const bool valid = j < n;
-    const int32_t id = valid ? min(max(lst[j], 0), id_max) : 0;
+    const int32_t id = valid ? min(max(raw, 0), id_max) : 0;
     const int32_t tile = valid ? id / kKeyTile : -2 - lane;  // lanes past the list never join a run
-    const int32_t next = j + 1 < n ? min(max(lst[j + 1], 0), id_max) / kKeyTile : -1;
+    const int32_t after = min(max(raw_after, 0), id_max) / kKeyTile;
+    // the next chunk's entries, in flight while this chunk is processed (read
+    // unconditionally from in-range positions, values past the list unused:
+    // a load under a branch would be waited for where the branch joins)
+    const int nb = base + 64;
+    const int32_t raw_n = lst[min(nb + lane, n - 1)];
+    const int32_t raw_after_n = lst[min(nb + 64, n - 1)];
+    int32_t next = __shfl_down(tile, 1);  // the tile of entry j + 1 (lane 63: the entry after the chunk)
+    if (lane == 63) next = after;
+    if (j + 1 >= n) next = -1;
     const bool last = valid && next != tile;
-    if (!kFill) {
+    if constexpr (!kFill) {
       if (last) atomicOr(&words[w * n_kt + tile], bit);
-      continue;
-    }
-    // Keys of each run: inclusive OR over the lanes of the same tile (a run
-    // is contiguous in an ascending list, so equal tiles d lanes apart bound
-    // a run), plus the part of the run carried from the previous chunk.
-    uint64_t m = valid ? uint64_t{1} << (id % kKeyTile) : 0;
+    } else {
+      // Keys of each run: inclusive OR over the lanes of the same tile (a run
+      // is contiguous in an ascending list, so equal tiles d lanes apart bound
+      // a run), plus the part of the run carried from the previous chunk.
+      uint64_t m = valid ? uint64_t{1} << (id % kKeyTile) : 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint64_t y = shfl_up64(m, d);
-      const int32_t ty = __shfl_up(tile, d);
-      if (lane >= d && ty == tile) m |= y;
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t y = shfl_up64(m, d);
+        const int32_t ty = __shfl_up(tile, d);
+        if (lane >= d && ty == tile) m |= y;
+      }
+      if (tile == carry_tile) m |= carry_mask;
+      carry_tile = __shfl(tile, 63);
+      carry_mask = shfl64(m, 63);
+      if (last) {
+        // Rank among the rows touching this tile: rows of earlier chunks, then
+        // earlier words of this chunk, then earlier rows of this word.
+        const int64_t c = w / kChunkWords;
+        const int64_t w0 = c * kChunkWords;
+        const int32_t start = tile_start[b * n_kt + tile];
+        const int32_t prefix = chunk_prefix[(b * C + c) * n_kt + tile];
+        uint32_t wd[kChunkWords];
+#pragma unroll
+        for (int k = 0; k < kChunkWords; ++k) wd[k] = w0 + k <= w ? words[(w0 + k) * n_kt + tile] : 0u;
+        int64_t pos = static_cast<int64_t>(start) + prefix;
+#pragma unroll
+        for (int k = 0; k < kChunkWords; ++k)
+          pos += __popc(w0 + k < w ? wd[k] : (w0 + k == w ? wd[k] & (bit - 1u) : 0u));
+        if (pos < capacity)
+          segs[pos] = int4{static_cast<int32_t>(i), static_cast<int32_t>(static_cast<uint32_t>(m)),
+                           static_cast<int32_t>(static_cast<uint32_t>(m >> 32)), 0};
+      }
     }
-    if (tile == carry_tile) m |= carry_mask;
-    carry_tile = __shfl(tile, 63);
-    carry_mask = shfl64(m, 63);
-    if (!last) continue;
-    // Rank among the rows touching this tile: rows of earlier chunks, then
-    // earlier words of this chunk, then earlier rows of this word.
-    const int64_t c = w / kChunkWords;
-    int64_t pos = static_cast<int64_t>(tile_start[b * n_kt + tile]) + chunk_prefix[(b * C + c) * n_kt + tile];
-    for (int64_t w2 = c * kChunkWords; w2 < w; ++w2) pos += __popc(words[w2 * n_kt + tile]);
-    pos += __popc(words[w * n_kt + tile] & (bit - 1u));
-    if (pos < capacity)
-      segs[pos] = int4{static_cast<int32_t>(i), static_cast<int32_t>(static_cast<uint32_t>(m)),
-                       static_cast<int32_t>(static_cast<uint32_t>(m >> 32)), 0};
+    raw = raw_n;
+    raw_after = raw_after_n;
   }
 }
 

@@ -171,12 +171,20 @@ __global__ void __launch_bounds__(256)
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= B * n_kt) return;
   const int64_t b = idx / n_kt, t = idx % n_kt;
+  int32_t* col = chunk_prefix + b * C * n_kt + t;  // chunk c at col[c * n_kt]
+  constexpr int kBatch = 16;  // counts loaded together (from clamped in-range chunks), then scanned in order
   int32_t run = 0;
-  for (int64_t c = 0; c < C; ++c) {
-    int32_t* p = chunk_prefix + (b * C + c) * n_kt + t;
-    const int32_t v = *p;
-    *p = run;
-    run += v;
+  for (int64_t c0 = 0; c0 < C; c0 += kBatch) {
+    int32_t v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) v[k] = col[min(c0 + k, C - 1) * n_kt];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (c0 + k < C) {
+        col[(c0 + k) * n_kt] = run;
+        run += v[k];
+      }
+    }
   }
   totals[idx] = run;
 }

@@ -343,6 +343,11 @@ __global__ void __launch_bounds__(64) dq_kernel(const DqArgs a) {
       *reinterpret_cast<u32x4*>(my_k + r * Gm::kTrStride + col) = kr[u];
       *reinterpret_cast<u32x4*>(my_v + r * Gm::kRowStride + col) = vr[u];
     }
+    // Prefetch as soon as the rows are staged: IDs two chunks ahead, then the next chunk's rows.
+    if (more) {
+      raw_next = load_id(base + 2 * kChunk);
+      load_kv(id_next, kr, vr);
+    }
     wave_lds_sync();
 
     // S^T[key 4g + r][head c] and dP^T[key 4g + r][head c]; A operands are
@@ -355,11 +360,6 @@ __global__ void __launch_bounds__(64) dq_kernel(const DqArgs a) {
       st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(ka + 32 * s)), qf[s], st, 0, 0, 0);
       dpt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, load16(va + 32 * s)), gf[s], dpt, 0, 0,
                                                     0);
-    }
-
-    if (more) {
-      raw_next = load_id(base + 2 * kChunk);
-      load_kv(id_next, kr, vr);
     }
 
     // dS^T = P^T (dP^T - delta), P^T = exp2(S^T scale log2e - lse2); keys past n

@@ -366,6 +366,12 @@ __global__ void __launch_bounds__(64) gather_attention_kernel(const KernelArgs a
       *reinterpret_cast<u32x4*>(my_kslab + r * Geo::kKStride + col) = kr[u];
       *reinterpret_cast<u32x4*>(my_slab + r * Geo::kStride + col) = vr[u];
     }
+    // Prefetch, as soon as the rows are staged (the registers are free again):
+    // IDs two chunks ahead first, then the next chunk's K and V rows.
+    if (more) {
+      raw_next = load_id(base + 2 * kChunk);
+      load_kv(id_next, kr, vr);
+    }
     wave_lds_sync();  // K and V rows visible to every lane of this wave
 
     // Scores: lane holds S^T[key 4g + r][head c]; the A operand is key c,
@@ -377,11 +383,6 @@ __global__ void __launch_bounds__(64) gather_attention_kernel(const KernelArgs a
       st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ka + 32 * s)),
                                                   qf[s], st, 0, 0, 0);
 
-    // Prefetch: IDs two chunks ahead first, then the next chunk's K and V rows.
-    if (more) {
-      raw_next = load_id(base + 2 * kChunk);
-      load_kv(id_next, kr, vr);
-    }
 
     // Online softmax (log2 domain) against a lazily raised reference max.
     float x[4];

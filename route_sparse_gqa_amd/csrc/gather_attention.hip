@@ -301,10 +301,19 @@ __global__ void __launch_bounds__(64) gather_attention_kernel(const KernelArgs a
   bf16x8 qf[Geo::kSteps];
   {
     const uint16_t* qp = a.q + b * a.qs0 + i * a.qs1 + (hk * G + (head_ok ? c : 0)) * a.qs2 + 8 * g;
+    // Unsplit, each query row is read once: streamed past the caches, which
+    // keeps them for K and V (the split rereads a row once per range, and the
+    // Infinity Cache serves those rereads).
 #pragma unroll
-    for (int s = 0; s < Geo::kSteps; ++s)
-      qf[s] = head_ok ? __builtin_bit_cast(bf16x8, load16(reinterpret_cast<const char*>(qp + 32 * s)))
-                      : bf16x8{};
+    for (int s = 0; s < Geo::kSteps; ++s) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(qp + 32 * s);
+      if (!head_ok)
+        qf[s] = bf16x8{};
+      else if constexpr (kSplit)
+        qf[s] = __builtin_bit_cast(bf16x8, load16(src));
+      else
+        qf[s] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(src));
+    }
   }
 
   f32x4 acc[Geo::kDimTiles];

@@ -311,7 +311,7 @@ __global__ void __launch_bounds__(64) dq_kernel(const DqArgs a) {
     int32_t idr[Gm::kLoads];
 #pragma unroll
     for (int u = 0; u < Gm::kLoads; ++u) {
-      idr[u] = __shfl(id, u * Gm::kRowsPerLoad + lane / Gm::kLanesPerRow);
+      idr[u] = chunk_row_id<Gm::kRowsPerLoad>(id, u, lane);
       kr[u] = load16(kb + RowOffset<kNarrow>::of(idr[u], ks1b));
     }
 #pragma unroll

@@ -29,6 +29,23 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));  // generic -> LDS address-space cast
 }
 
+// Route ID of the rows of gather load u of a chunk, for this lane: with R
+// rows per load instruction, lane L loads row u * R + L / (64 / R), whose ID
+// sits in lane (u * R + L / (64 / R)) of `id` (row r's ID in lane r).  The R
+// IDs are read into scalar registers (v_readlane: no LDS round trip, which
+// would queue behind the chunk's slab writes) and selected by the lane's row.
+template <int R>
+__device__ __forceinline__ int32_t chunk_row_id(int32_t id, int u, int lane) {
+  const int rsel = lane / (64 / R);
+  int32_t v = __builtin_amdgcn_readlane(id, u * R);
+#pragma unroll
+  for (int q = 1; q < R; ++q) {
+    const int32_t s_id = __builtin_amdgcn_readlane(id, u * R + q);
+    v = rsel == q ? s_id : v;
+  }
+  return v;
+}
+
 // Orders this wavefront's LDS writes before its later LDS reads (and the
 // reverse); wavefront scope only, so no workgroup barrier is involved.
 __device__ __forceinline__ void wave_lds_sync() {

@@ -341,7 +341,7 @@ __global__ void __launch_bounds__(64) gather_attention_kernel(const KernelArgs a
     int32_t idr[Geo::kLoads];
 #pragma unroll
     for (int u = 0; u < Geo::kLoads; ++u) {
-      idr[u] = __shfl(id, u * Geo::kRowsPerLoad + lane / Geo::kLanesPerRow);
+      idr[u] = chunk_row_id<Geo::kRowsPerLoad>(id, u, lane);
       kr[u] = load16(kb + RowOffset<kNarrow>::of(idr[u], ks1b));
     }
 #pragma unroll

@@ -137,24 +137,40 @@ __global__ void __launch_bounds__(64 * kWaves)
     src_stride[u] = 2 * (m == 0 ? qs1 : gs1);
   }
   int32_t n_rec = 0;  // records staged for the current chunk (>= 1 while batches run)
-  auto fetch = [&](Stage& S, int32_t sb) {  // sb: first record of the batch, within the chunk
+  // A fetch in two halves: `plan` reads the batch's records from LDS and forms
+  // the addresses, `issue` starts the global loads.  The step plans the fetch
+  // before its compute and stash, so those LDS reads do not queue behind the
+  // stash's slab writes ahead of the loads.
+  struct Plan {
+    const char* src[kPer];
+    int64_t idx;
+    uint2 mask;
+    uint32_t ok;
+  };
+  auto plan_fetch = [&](int32_t sb) {  // sb: first record of the batch, within the chunk
+    Plan P;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int col = ((tid + kThreads * u) / Gm::kLanesPerRow) % kChunk;
       const int32_t ir = min(max(recs[min(sb + col / G, n_rec - 1)].x, 0), row_max);
-      S.pre[u] = load16(src_base[u] + RowOffset<kNarrow>::of(ir, src_stride[u]));
+      P.src[u] = src_base[u] + RowOffset<kNarrow>::of(ir, src_stride[u]);
     }
-    {
-      const int col = tid % kChunk;  // only threads below kChunk stash it
-      const int slot = col / G;
-      const bool ok = tid < kChunk && col < cols && sb + slot < n_rec;
-      const int4 e = recs[min(sb + slot, n_rec - 1)];
-      const int64_t idx = (b * S_q + min(max(e.x, 0), row_max)) * Hq + q_head0 + col % G;
-      S.stat = float2{lse[idx], delta[idx]};  // raw: any arithmetic here would wait for the loads
-      S.mask = uint2{static_cast<uint32_t>(e.y), static_cast<uint32_t>(e.z)};
-      S.ok = ok ? 1u : 0u;
-    }
+    const int col = tid % kChunk;  // only threads below kChunk stash it
+    const int slot = col / G;
+    const int4 e = recs[min(sb + slot, n_rec - 1)];
+    P.idx = (b * S_q + min(max(e.x, 0), row_max)) * Hq + q_head0 + col % G;
+    P.mask = uint2{static_cast<uint32_t>(e.y), static_cast<uint32_t>(e.z)};
+    P.ok = tid < kChunk && col < cols && sb + slot < n_rec ? 1u : 0u;
+    return P;
   };
+  auto issue = [&](Stage& S, const Plan& P) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) S.pre[u] = load16(P.src[u]);
+    S.stat = float2{lse[P.idx], delta[P.idx]};  // raw: any arithmetic here would wait for the loads
+    S.mask = P.mask;
+    S.ok = P.ok;
+  };
+  auto fetch = [&](Stage& S, int32_t sb) { issue(S, plan_fetch(sb)); };
   auto stash = [&](const Stage& S, int buf) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -238,10 +254,11 @@ __global__ void __launch_bounds__(64 * kWaves)
     __syncthreads();
     // X holds batch bi + 1 (the other stage holds bi + 2); the two stages swap roles every batch.
     auto step = [&](int32_t bi, Stage& X) {
+      const Plan next = plan_fetch((bi + 3) * rows_per_batch);
       const int cur = bi & 1;
       compute(cur);
       if (bi + 1 < n_batches) stash(X, cur ^ 1);  // the other buffer was last read before the previous barrier
-      fetch(X, (bi + 3) * rows_per_batch);
+      issue(X, next);
       __syncthreads();
     };
     // Pairs of batches, then the odd last one: every path back to the loop

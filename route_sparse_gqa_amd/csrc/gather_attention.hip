@@ -366,13 +366,28 @@ __global__ void __launch_bounds__(64) gather_attention_kernel(const KernelArgs a
   for (int base = 0; base < n; base += kChunk) {
     const bool more = base + kChunk < n;  // wave-uniform
 
-    // Stage this chunk's K and V rows in LDS (row-major, padded strides).
+    // Stage this chunk's K rows in LDS, read the score operands right behind
+    // them, then stage the V rows (row-major, padded strides): the operand
+    // reads do not queue behind the V writes.
     wave_lds_sync();  // previous chunk's reads of both slabs are complete
 #pragma unroll
     for (int u = 0; u < Geo::kLoads; ++u) {
       const int r = u * Geo::kRowsPerLoad + lane / Geo::kLanesPerRow;
       const int col = 8 * (lane % Geo::kLanesPerRow);
       *reinterpret_cast<u32x4*>(my_kslab + r * Geo::kKStride + col) = kr[u];
+    }
+    wave_lds_sync();  // K rows visible to every lane of this wave
+    // Scores: lane holds S^T[key 4g + r][head c]; the A operand is key c,
+    // dims 32s + 8g .. +7.
+    const uint16_t* ka = my_kslab + c * Geo::kKStride + 8 * g;
+    bf16x8 kf[Geo::kSteps];
+#pragma unroll
+    for (int s = 0; s < Geo::kSteps; ++s) kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ka + 32 * s));
+    __builtin_amdgcn_sched_barrier(0);  // the operand reads stay ahead of the V writes
+#pragma unroll
+    for (int u = 0; u < Geo::kLoads; ++u) {
+      const int r = u * Geo::kRowsPerLoad + lane / Geo::kLanesPerRow;
+      const int col = 8 * (lane % Geo::kLanesPerRow);
       *reinterpret_cast<u32x4*>(my_slab + r * Geo::kStride + col) = vr[u];
     }
     // Prefetch, as soon as the rows are staged (the registers are free again):
@@ -381,17 +396,9 @@ __global__ void __launch_bounds__(64) gather_attention_kernel(const KernelArgs a
       raw_next = load_id(base + 2 * kChunk);
       load_kv(id_next, kr, vr);
     }
-    wave_lds_sync();  // K and V rows visible to every lane of this wave
-
-    // Scores: lane holds S^T[key 4g + r][head c]; the A operand is key c,
-    // dims 32s + 8g .. +7.
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* ka = my_kslab + c * Geo::kKStride + 8 * g;
 #pragma unroll
-    for (int s = 0; s < Geo::kSteps; ++s)
-      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ka + 32 * s)),
-                                                  qf[s], st, 0, 0, 0);
-
+    for (int s = 0; s < Geo::kSteps; ++s) st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], st, 0, 0, 0);
 
     // Online softmax (log2 domain) against a lazily raised reference max.
     float x[4];
@@ -415,6 +422,7 @@ __global__ void __launch_bounds__(64) gather_attention_kernel(const KernelArgs a
       l_run += static_cast<float>(pf[r]);
     }
     const i16x4 pb = __builtin_bit_cast(i16x4, pf);
+    wave_lds_sync();  // V rows visible to every lane of this wave
 
     // O^T += V^T P^T: one transposed LDS read gives lane (c, g) keys 4g..4g+3
     // of dim 16t + c, matching its four probabilities.

@@ -30,7 +30,12 @@
 //  * Software pipeline: while chunk c is computed, the K and V rows of chunk
 //    c + 1 (in registers) and the route IDs of chunk c + 2 are in flight.
 //    The IDs are issued before the rows and used one iteration later, so the
-//    in-order load counter never makes the rows wait for them.
+//    in-order load counter never makes the rows wait for them.  Within a
+//    chunk the LDS sees, in order: the K rows' writes, the score operands'
+//    reads, the V rows' writes (LDS operations of a wave run in order, so
+//    the operand reads wait only for the K writes), and the next chunk's
+//    loads are issued right after, with their row IDs taken by lane reads
+//    rather than LDS permutes.
 //  * Online softmax in fp32 with exp2 and the scale folded into log2(e).  The
 //    reference max is raised only when a chunk exceeds it by more than 2^8,
 //    so the accumulator rescale is skipped once the max has settled.

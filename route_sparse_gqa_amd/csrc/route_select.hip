@@ -14,8 +14,9 @@
 // Design:
 //  * select_scores_kernel -- a workgroup owns 16/HG query rows of one batch
 //    (HG = head groups of 16) and a segment of up to 4096 blocks, walked in
-//    LDS chunks of 32 KB of block keys (row stride 2D + 16 bytes, so operand
-//    reads are conflict-free).  The next chunk is prefetched into registers
+//    LDS chunks of 32 KB of block keys (row stride 2D + 32 bytes, with which
+//    the bank-conflict counter reads zero for the operand reads and row
+//    stores).  The next chunk is prefetched into registers
 //    while the current one is used; the rows' queries are loaded once and
 //    stay in registers as the A operand.  Per 16 blocks a wave runs
 //    v_mfma_f32_16x16x32_bf16 with the 16 index heads of a row on M and the
@@ -54,7 +55,7 @@ constexpr int kBins = 2048;           // histogram bins of one radix pass (11 bi
 template <int D, int kChunkKB>
 struct SelGeo {
   static constexpr int kSteps = D / 32;                  // K-slices of one 16x16x32 product
-  static constexpr int kStride = D + 8;                  // LDS row stride (bf16): 2D + 16 bytes
+  static constexpr int kStride = D + 16;                 // LDS row stride (bf16): 2D + 32 bytes
   static constexpr int kPieces = D / 8;                  // 16-byte pieces of one key row
   static constexpr int kChunk = kChunkKB * 512 / D;      // blocks per LDS chunk (kChunkKB KB of keys)
   static constexpr int kPerThread = kChunk * kPieces / kScoreThreads;  // 16-byte pieces per thread: 8 or 4

@@ -24,7 +24,9 @@
 //    the relu and three adds give a partial sum, and three gfx950 lane swaps
 //    (two across the wave's halves, one across 16-lane rows; registers only)
 //    complete the sums of four rows and leave row g's sum in lane group g,
-//    which stores it.  The
+//    which holds a chunk's sums in registers and stores them once the next
+//    chunk is staged (vector loads and stores share one wait counter, so a
+//    store issued before the staging would be waited for there).  The
 //    segments of one row tile run on one XCD; the tiles that see the most
 //    blocks are dispatched first.  fp32 scores go to a [rows, ld] workspace,
 //    only for rows that see more than kb blocks, only for visible blocks.
@@ -162,10 +164,14 @@ __global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per
 
   for (int ch = 0; ch < n_chunks; ++ch) {
     const int64_t j0 = seg0 + static_cast<int64_t>(ch) * Geo::kChunk;
-    const bool more = ch + 1 < n_chunks;
-    if (more) fetch(j0 + Geo::kChunk);  // in flight while this chunk is scored
+    fetch(j0 + Geo::kChunk);  // in flight while this chunk is scored (past the segment: zeros, no loads)
     const int n_sub = static_cast<int>((min(static_cast<int64_t>(Geo::kChunk), seg_end - j0) + 15) / 16);
-    for (int sc = 0; sc < n_sub; ++sc) {
+    constexpr int kSub = Geo::kChunk / 16;
+    float held[kSub];
+#pragma unroll
+    for (int sc = 0; sc < kSub; ++sc) {
+      held[sc] = 0.f;
+      if (sc >= n_sub) continue;
       bf16x8 kf[Geo::kSteps];
       const uint16_t* kp = kslab + (16 * sc + m) * Geo::kStride + 8 * g;
 #pragma unroll
@@ -193,13 +199,17 @@ __global__ void __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per
       const float ys = __uint_as_float(p13[0]) + __uint_as_float(p13[1]);
       const u32x2 z = __builtin_amdgcn_permlane16_swap(__float_as_uint(xs), __float_as_uint(ys), false, false);
       const float total = __uint_as_float(z[0]) + __uint_as_float(z[1]);  // >= +0.0: sums of relu terms
-      const int64_t j = j0 + 16 * sc + m;
-      if (my_store && j < my_nv) my_out[j] = total;
+      held[sc] = total;
     }
-    if (more) {
-      __syncthreads();  // every wave is done with this chunk's keys
-      stage();
-      __syncthreads();
+    __syncthreads();  // every wave is done with this chunk's keys
+    stage();
+    __syncthreads();
+    // The chunk's scores are stored only now, so that the wait before the staging above covers
+    // the next chunk's loads and none of these stores.
+#pragma unroll
+    for (int sc = 0; sc < kSub; ++sc) {
+      const int64_t j = j0 + 16 * sc + m;
+      if (my_store && j < my_nv) my_out[j] = held[sc];
     }
   }
 }

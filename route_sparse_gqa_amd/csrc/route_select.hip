@@ -35,7 +35,9 @@
 //    length fits its E, slots past the row hold 0); three LDS-histogram
 //    passes over the nonzero float bit patterns (non-negative floats order
 //    like their bits; 11, 11 and 10 bits) find the kb-th largest value tau
-//    and how many of the values equal to tau to keep.  Ballots build bitmaps
+//    and how many of the values equal to tau to keep; when a pass needs its
+//    boundary bin whole, the search stops there and every key at or above
+//    the bin's lower bound is kept (no tie to split).  Ballots build bitmaps
 //    of the values above tau and of those equal to it; a block prefix over
 //    the words keeps the lowest-index ties and places every kept block at its
 //    rank, in ascending block order.  The row is then written coalesced.
@@ -285,7 +287,8 @@ __global__ void __launch_bounds__(NT)
     // takes from the row's own (lower indices, and the row has more than kb values).
     uint32_t prefix = 0, hi_mask = 0;
     int remaining = static_cast<int>(kb);
-    bool settled = false;  // workgroup-uniform: tau found to be 0
+    bool settled = false;  // workgroup-uniform: tau found to be 0, or the boundary bin is kept whole
+    bool whole = false;    // workgroup-uniform: every key >= tau is kept and no tie is split
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
       if (settled) continue;
@@ -326,6 +329,13 @@ __global__ void __launch_bounds__(NT)
       prefix |= static_cast<uint32_t>(found[0]) << sh;
       hi_mask |= dmask << sh;
       remaining = found[1];
+      // The boundary bin is needed whole: every key >= prefix (its lower bits zero) is kept, exactly
+      // kb of them, and the lower digits need no pass.  prefix 0 is left to the general path (zero
+      // keys are not in the histograms).
+      if (p < 2 && prefix != 0u && static_cast<int>(hist[found[0]]) == remaining) {
+        whole = true;
+        settled = true;
+      }
       __syncthreads();  // found and hist are rewritten by the next pass
     }
     const uint32_t tau = prefix;  // the kb-th largest value; keep `remaining` of the values equal to it
@@ -335,8 +345,8 @@ __global__ void __launch_bounds__(NT)
     // `remaining` of them) first.
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const uint64_t bg = __ballot(key[e] > tau);
-      const uint64_t be = __ballot(key[e] == tau);
+      const uint64_t bg = __ballot(whole ? key[e] >= tau : key[e] > tau);
+      const uint64_t be = __ballot(!whole && key[e] == tau);
       if (lane == 0) {
         gt_words[e * kWaves + wave] = bg;  // word e * kWaves + wave covers blocks 64 * word .. +63
         eq_words[e * kWaves + wave] = be;

@@ -197,6 +197,33 @@ def test_select_many_batch_rows_one_topk_launch():
     np.testing.assert_array_equal(got[:, 240:260], oracle.select_token_ids(iq, ck, lens, budget, c, rows=(240, 260)))
 
 
+def test_select_radix_digits_and_boundary_bins():
+    """Scores hi + lo with hi in {0, 2^10, 2^20, 2^21} and lo an integer below 256: clusters whose
+    members differ only in the 2nd (2^10 + lo) or the 3rd (2^20 + lo) radix digit, and many exact
+    duplicates.  The rows see 2001..2064 blocks and four budgets put the kb-th largest value between
+    clusters (row 30 then needs exactly the 2^21 cluster: the first digit's bin is taken whole) and
+    inside each cluster, so the search ends after the first, second or third digit, with the
+    boundary bin taken whole or split between equal values by the lowest-index rule.  Must equal
+    the oracle exactly."""
+    B, S_q, H, D, c, q_offset = 1, 64, 1, 64, 1, 2000
+    n_blocks = q_offset + S_q
+    rng = np.random.Generator(np.random.PCG64(2026_12))
+    hi = rng.choice(np.array([0.0, 2.0 ** 10, 2.0 ** 20, 2.0 ** 21], np.float32), size=n_blocks, p=[0.3, 0.3, 0.3, 0.1])
+    lo = rng.integers(0, 256, size=n_blocks).astype(np.float32)
+    ck = np.zeros((B, n_blocks, 1, D), np.uint16)
+    ck[0, :, 0, 0] = float32_to_bf16_bits(hi)  # powers of two and integers below 256 are exact in bf16
+    ck[0, :, 0, 1] = float32_to_bf16_bits(lo)
+    iq = np.zeros((B, S_q, H, D), np.uint16)
+    iq[..., 0:2] = float32_to_bf16_bits(np.float32(1.0))  # score of block j = hi_j + lo_j, exact in fp32
+    lens = np.array([n_blocks], np.int64)
+    top_cluster = int((hi[:q_offset + 31] == 2.0 ** 21).sum())  # blocks of the 2^21 cluster row 30 sees
+    for budget in (top_cluster, 300, 1000, 1500):
+        print(f"select radix case budget {budget}", flush=True)
+        got = run_gpu(iq, ck, lens, budget, c, q_offset, n_blocks)
+        np.testing.assert_array_equal(got, oracle.select_token_ids(iq, ck, lens, budget, c, q_offset),
+                                      err_msg=f"budget {budget}")
+
+
 # --------------------------------------------------------- continuous cases
 
 CONT_CASES = [  # B, S_q, H, D, c, budget
